@@ -1,0 +1,149 @@
+/*
+ * spec_verify.h -- C ABI of the speculative-decoding verify step on AMD MI355X (gfx950).
+ *
+ * One verify step scores the k drafted tokens of every sequence plus one bonus position in a
+ * single target forward, then accepts or rejects the drafts without changing the target's
+ * output distribution.  The pages this follows:
+ *   - llm-wiki.hwlabs.dev, "Gemma 4 MTP: 드래프터가 초안을 쓰고 타깃이 검증하는 추론 가속 구조",
+ *     section "투기적 디코딩(Speculative Decoding)의 기본 구조": the target checks the k
+ *     proposed tokens in one forward, confirms them up to the first wrong one and generates
+ *     the token there itself, which keeps the output distribution unchanged;
+ *   - butteryoon.github.io, "Gemma 4 MTP 서빙 가이드 해설", section 4 execution flow
+ *     (parallel verification against the target's own distribution, then accept/reject with
+ *     the drafts after the first rejection discarded), section 1 table (the drafter and the
+ *     target share one KV-cache pool; a 256k vocabulary), section 7 settings table (local
+ *     attention heads of dim 256, global heads of dim 512);
+ *   - news.hada.io topic 29214, "Gemma 4 가속하기 : 다중 토큰 예측 drafter로 더 빠른 추론",
+ *     section "MTP가 동작하는 방식": when the target agrees with the whole draft it accepts it
+ *     and generates one extra token in the same forward.
+ * The acceptance rule is the one of Leviathan et al. (2022), which the pages cite.
+ *
+ * Conventions for every call:
+ *   - Pointers are device pointers owned by the caller (except where noted).  The library
+ *     allocates nothing and keeps no handles; scratch memory is the caller's `workspace`,
+ *     at least as large as the matching *_workspace() query says.
+ *   - `stream` is a hipStream_t (NULL: the null stream).  Calls only enqueue work on it and
+ *     return; results are valid once the stream has reached that point.
+ *   - Return value: SPEC_OK (0) or a negative spec_status.  Host-checkable argument errors are
+ *     reported before anything is enqueued; spec_last_error() then describes the failure (a
+ *     thread-local string, valid until the next call on the same thread).
+ *   - Preconditions on device-resident data are documented per call and not checked on the
+ *     host; where a violation could make a kernel read out of bounds the kernel clamps or
+ *     masks instead (stated per call), so no input makes a kernel fault.
+ *   - All tensors are dense, row-major, with the shapes given; "b-major" means sequence
+ *     index outermost.
+ */
+#ifndef SPEC_VERIFY_H
+#define SPEC_VERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SPEC_OK = 0,
+  SPEC_EINVAL = -1,        /* a null pointer, a non-positive size, inconsistent shapes */
+  SPEC_EUNSUPPORTED = -2,  /* a shape or dtype outside what the kernels implement */
+  SPEC_EWORKSPACE = -3,    /* workspace smaller than the *_workspace() query returns */
+  SPEC_EHIP = -4           /* the HIP runtime rejected a launch; message from hipGetErrorString */
+} spec_status;
+
+typedef enum {
+  SPEC_F32 = 0,            /* IEEE binary32 */
+  SPEC_BF16 = 1            /* bfloat16 (upper 16 bits of a binary32) */
+} spec_dtype;
+
+/* Version of this interface, (major << 16) | minor. */
+int spec_version(void);
+
+/* Message describing the last failing call on this thread ("" if none). */
+const char *spec_last_error(void);
+
+/* ------------------------------------------------------------------------------------------
+ * (i) Verify attention: K1 = k + 1 causal queries per sequence over a paged KV cache, one
+ *     layer per call, grouped-query heads.
+ *
+ * The K1 verified positions are the last K1 tokens of each sequence's cache (their K/V are
+ * already written).  Query i of sequence b sits at position t = ctx_lens[b] - K1 + i and sees
+ * the key positions s with lo <= s <= t, lo = 0 for a global layer (window == 0) and
+ * lo = max(0, t - window + 1) for a sliding-window layer.  Query head h reads KV head
+ * h / (Hq / Hkv).  out = softmax(scale * q k^T) v over the visible keys, accumulated in fp32.
+ *
+ *   q           [B, K1, Hq, D]               dtype
+ *   k_pool      [num_pages, Hkv, page_size, D] dtype   key position s of sequence b is at page
+ *   v_pool      [num_pages, Hkv, page_size, D] dtype   page_table[b][s / page_size], slot
+ *                                                       s % page_size
+ *   page_table  [B, max_pages_per_seq] int32  physical page ids
+ *   ctx_lens    [B] int32                     tokens in each cache, the K1 new ones included
+ *   out         [B, K1, Hq, D] fp32
+ *   D in {64, 128, 256, 512}; page_size == 16; Hq % Hkv == 0; K1 in [1, 64].
+ *
+ * Device-data preconditions: K1 <= ctx_lens[b] <= max_pages_per_seq * page_size.  ctx_lens
+ * beyond that bound are clamped to it; a page id outside [0, num_pages) hides the keys on
+ * that page; a query with no visible key gets a zero output row.
+ * ---------------------------------------------------------------------------------------- */
+size_t spec_verify_attn_workspace(int B, int K1, int Hq, int Hkv, int D, int page_size,
+                                  int max_pages_per_seq, int window);
+
+int spec_verify_attn(const void *q, const void *k_pool, const void *v_pool,
+                     const int32_t *page_table, const int32_t *ctx_lens, float *out,
+                     int B, int K1, int Hq, int Hkv, int D, int page_size, int num_pages,
+                     int max_pages_per_seq, int window, float scale, spec_dtype dtype,
+                     void *workspace, size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------------------------------
+ * (ii) lm-head: logits = hidden W^T over the R = B * K1 verify rows, then the target's row
+ *      distributions p = softmax(logits / T) (temperature per row; T <= 0 gives the one-hot
+ *      vector at the first maximal logit, i.e. greedy).
+ *
+ *   hidden       [R, H]  dtype  (rows b-major: row b*K1 + i is query position i of sequence b)
+ *   weight       [V, H]  dtype  vocab x hidden table, row-major
+ *   temperature  [R] fp32 (device)
+ *   logits       [R, V] fp32, or NULL when the raw logits are not wanted
+ *   probs        [R, V] fp32  p, rows summing to 1
+ *   H % 8 == 0 (16-byte rows for bf16).  Accumulation is fp32 (MFMA).
+ * ---------------------------------------------------------------------------------------- */
+size_t spec_lm_head_workspace(int R, int H, int V);
+
+int spec_lm_head(const void *hidden, const void *weight, const float *temperature,
+                 float *logits, float *probs, int R, int H, int V, spec_dtype dtype,
+                 void *workspace, size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------------------------------
+ * (iii) Accept / reject (Leviathan et al.), with the correction or bonus token.
+ *
+ * For each sequence b and i < k: draft i is accepted iff u[b][i] * q[b][i][d] < p[b][i][d]
+ * with d = draft[b][i], evaluated exactly (fp64 product of fp32 values); acceptance stops at
+ * the first rejection, n = number accepted.  Then one token y is drawn with u[b][k]:
+ * n < k: from max(0, p[b][n] - q[b][n]) (correction); n == k: from p[b][k] (bonus).  The draw
+ * is an inverse CDF over integer weights floor(x * 2^38) (order-independent sums; if every
+ * correction weight is 0 the weights of p[b][n] are used): with W the weight total and
+ * m = floor(u[b][k] * 2^24), y is the smallest index whose running weight sum exceeds
+ * floor(m * W / 2^24).
+ *
+ *   draft       [B, k]     int32
+ *   q           [B, k, V]  fp32  drafter distributions (may be NULL when k == 0)
+ *   p           [B, K1, V] fp32  target distributions, K1 = k + 1
+ *   uniforms    [B, K1]    fp32  in [0, 1): k acceptance tests, then the one draw
+ *   n_accepted  [B] int32  (out) 0..k
+ *   tokens      [B, K1] int32 (out) d_0 .. d_{n-1}, y, then -1 padding
+ *   k in [0, 63].
+ *
+ * Device-data preconditions: p and q rows are distributions (non-negative, summing to 1).  A
+ * draft id outside [0, V) is rejected without being read.  A p row whose weights are all 0
+ * draws index 0.
+ * ---------------------------------------------------------------------------------------- */
+size_t spec_accept_workspace(int B, int k, int V);
+
+int spec_accept(const int32_t *draft, const float *q, const float *p, const float *uniforms,
+                int32_t *n_accepted, int32_t *tokens, int B, int k, int V,
+                void *workspace, size_t workspace_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPEC_VERIFY_H */

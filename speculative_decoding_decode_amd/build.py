@@ -1,0 +1,76 @@
+"""Compile the HIP sources into libspecverify.so (gfx950), in-tree.
+
+    python -m speculative_decoding_decode_amd.build
+
+Each csrc/*.hip file is compiled to an object under _build/ in parallel, then linked into a
+shared library next to this file.  Packed-fp32 instructions are disabled for all device code.
+"""
+from __future__ import annotations
+
+import concurrent.futures as cf
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+BUILD = os.path.join(ROOT, "_build")
+LIB_NAME = "libspecverify.so"
+LIB_PATH = os.path.join(PKG, LIB_NAME)
+ARCH = "gfx950"
+
+COMMON = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
+          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-Wno-unused-command-line-argument", "-I" + INCLUDE, "-I" + CSRC]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (ROCm is required to build the HIP library)")
+
+
+def sources():
+    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
+
+
+def _run(cmd):
+    p = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    # the host pass does not know the packed-fp32 target feature and says so; that is harmless
+    lines = [l for l in p.stdout.splitlines() if "packed-fp32-ops" not in l]
+    return p.returncode, "\n".join(lines)
+
+
+def build(verbose: bool = False, jobs: int | None = None) -> str:
+    cc = hipcc()
+    os.makedirs(BUILD, exist_ok=True)
+    objs, cmds = [], []
+    for src in sources():
+        obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+        objs.append(obj)
+        cmds.append([cc, *COMMON, "-c", src, "-o", obj])
+    jobs = jobs or min(len(cmds), os.cpu_count() or 4, 16)
+    with cf.ThreadPoolExecutor(jobs) as ex:
+        results = list(ex.map(_run, cmds))
+    for cmd, (rc, out) in zip(cmds, results):
+        if verbose or rc != 0:
+            print(" ".join(cmd))
+            if out:
+                print(out)
+        if rc != 0:
+            raise RuntimeError(f"compilation failed: {cmd[-3]}")
+    tmp = LIB_PATH + ".tmp"
+    rc, out = _run([cc, "--offload-arch=" + ARCH, "-shared", "-fPIC", *objs, "-o", tmp])
+    if rc != 0:
+        print(out)
+        raise RuntimeError("link failed")
+    os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,397 @@
+// lm-head of the verify step: logits = hidden W^T for the R = B*K1 verify rows, and the
+// target's row distributions p = softmax(logits / T).
+//
+// The pages single out this contraction: with a 256k vocabulary the final logit projection is
+// a major cost (butteryoon "Gemma 4 MTP 서빙 가이드 해설", section 1; damoang's text of the
+// MTP announcement, drafter internals section), and decoding is bound by streaming weights
+// from memory (same guide, introduction).  At R = 3..96 rows the kernel is a stream over the
+// V x H table: every table element is read once from HBM and used R times.
+//
+// Design (gfx950):
+//  * one workgroup = 4 waves = 256 vocab rows ("block"); each wave owns 4 MFMA tiles of
+//    16 vocab rows and NT tiles of 16 hidden-state rows;
+//  * the table streams straight from HBM into registers as 16-byte fragments that are the A
+//    operand of v_mfma_f32_16x16x32_bf16 (fp32 tables: four v_mfma_f32_16x16x4_f32); loads are
+//    issued one batch of kDepth K-steps ahead of the MFMAs that consume them;
+//  * the hidden rows (the B operand) are staged once per chunk of the hidden dimension in LDS,
+//    so the only global traffic inside the loop is the table;
+//  * the epilogue turns the 256 x R logits of the block into per-block softmax statistics
+//    (max, sum of exp, first argmax) and writes exp(logit - block max) into p; a second small
+//    kernel merges the statistics of all blocks and rescales p in place (or writes the greedy
+//    one-hot rows).
+#include <math.h>
+
+#include "common.hpp"
+
+namespace {
+
+using spec::kWave;
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / kWave;          // 4
+constexpr int kMT = 4;                            // 16-row vocab tiles per wave
+constexpr int kBlockRows = kWaves * kMT * 16;     // 256 vocab rows per workgroup
+constexpr int kDepth = 4;                         // K-steps per load batch
+constexpr int kXBudget = 40 * 1024;               // LDS bytes for a staged hidden-row chunk
+constexpr int kFinChunk = 4096;                   // vocab entries per finalize workgroup
+constexpr float kLog2e = 1.4426950408889634f;
+
+template <typename T> struct Mma;
+template <> struct Mma<uint16_t> {  // bf16 table: one 16x16x32 MFMA per 16-byte fragment
+  static constexpr int kEPL = 8;             // elements per lane per fragment
+  static constexpr int kStep = 4 * kEPL;     // hidden elements per K-step (4 lane groups)
+  __device__ static __forceinline__ f32x4_t run(uint4 a, uint4 b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+  }
+};
+template <> struct Mma<float> {  // fp32 table: four 16x16x4 MFMAs, one per fragment element
+  static constexpr int kEPL = 4;
+  static constexpr int kStep = 4 * kEPL;
+  __device__ static __forceinline__ f32x4_t run(uint4 a, uint4 b, f32x4_t c) {
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.x), __uint_as_float(b.x), c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.y), __uint_as_float(b.y), c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.z), __uint_as_float(b.z), c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.w), __uint_as_float(b.w), c, 0, 0, 0);
+    return c;
+  }
+};
+
+__device__ __forceinline__ bool better(float m, int a, float om, int oa) {
+  return om > m || (om == m && oa < a);
+}
+
+// Contraction + per-block statistics.  Grid: (ceil(V / 256), ceil(R / (16 NT))).
+// MFMA operand roles: A = 16 vocab rows x K of the table, B = K x 16 hidden rows, so the
+// accumulator lane l holds logits of vocab rows 4*(l/16) + e (e = 0..3) for hidden row l % 16.
+template <typename T, int NT>
+__global__ __launch_bounds__(kThreads) void lm_head_kernel(
+    const T *__restrict__ X, const T *__restrict__ W, const float *__restrict__ temp,
+    float *__restrict__ logits, float *__restrict__ probs, float2 *__restrict__ stats,
+    int *__restrict__ amax, int R, int H, int V, int kcs) {
+  using M = Mma<T>;
+  extern __shared__ __align__(16) unsigned char smem[];
+  T *xs = reinterpret_cast<T *>(smem);
+  __shared__ float red_m[kWaves][NT * 16];
+  __shared__ float red_s[kWaves][NT * 16];
+  __shared__ int red_i[kWaves][NT * 16];
+
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int lr = lane & 15, lq = lane >> 4;
+  const int blk = blockIdx.x;
+  const int r0 = blockIdx.y * NT * 16;
+  const int nrows = min(NT * 16, R - r0);
+  const int vrow0 = blk * kBlockRows + wave * kMT * 16;
+  const int xstride = kcs * M::kStep + M::kEPL;   // LDS row stride (elements), 16-byte pad
+
+  const T *wrow[kMT];
+#pragma unroll
+  for (int t = 0; t < kMT; ++t) {
+    const int v = min(vrow0 + t * 16 + lr, V - 1);    // tail rows are read but discarded
+    wrow[t] = W + (size_t)v * H + lq * M::kEPL;
+  }
+
+  f32x4_t acc[kMT][NT];
+#pragma unroll
+  for (int t = 0; t < kMT; ++t)
+#pragma unroll
+    for (int n = 0; n < NT; ++n) acc[t][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const int nks = (H + M::kStep - 1) / M::kStep;
+  for (int c0 = 0; c0 < nks; c0 += kcs) {
+    const int cn = min(kcs, nks - c0);
+    const int cn_pad = (cn + kDepth - 1) / kDepth * kDepth;
+    __syncthreads();
+    {  // stage hidden rows [r0, r0 + nrows) x K-steps [c0, c0 + cn_pad) into LDS
+      const int groups = cn_pad * M::kStep / M::kEPL;
+      for (int e = threadIdx.x; e < nrows * groups; e += kThreads) {
+        const int r = e / groups, g = e - r * groups;
+        const int k = c0 * M::kStep + g * M::kEPL;
+        uint4 val = {0u, 0u, 0u, 0u};
+        if (k < H) val = *reinterpret_cast<const uint4 *>(X + (size_t)(r0 + r) * H + k);
+        *reinterpret_cast<uint4 *>(xs + r * xstride + g * M::kEPL) = val;
+      }
+    }
+    __syncthreads();
+
+    uint4 a0[kDepth][kMT], a1[kDepth][kMT];
+    auto load = [&](uint4(&a)[kDepth][kMT], int batch) {
+#pragma unroll
+      for (int d = 0; d < kDepth; ++d) {
+        const int ks = c0 + batch * kDepth + d;
+        const bool ok = ks < nks && ks * M::kStep + lq * M::kEPL < H;
+#pragma unroll
+        for (int t = 0; t < kMT; ++t)
+          a[d][t] = ok ? *reinterpret_cast<const uint4 *>(wrow[t] + (size_t)ks * M::kStep)
+                       : uint4{0u, 0u, 0u, 0u};
+      }
+    };
+    auto compute = [&](const uint4(&a)[kDepth][kMT], int batch) {
+#pragma unroll
+      for (int d = 0; d < kDepth; ++d) {
+        const int kl = (batch * kDepth + d) * M::kStep + lq * M::kEPL;
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+          const int r = n * 16 + lr;
+          uint4 b = {0u, 0u, 0u, 0u};
+          if (r < nrows) b = *reinterpret_cast<const uint4 *>(xs + r * xstride + kl);
+#pragma unroll
+          for (int t = 0; t < kMT; ++t) acc[t][n] = M::run(a[d][t], b, acc[t][n]);
+        }
+      }
+    };
+    const int nb = cn_pad / kDepth;
+    load(a0, 0);
+    for (int bi = 0; bi < nb; bi += 2) {
+      if (bi + 1 < nb) load(a1, bi + 1);
+      compute(a0, bi);
+      if (bi + 1 < nb) {
+        if (bi + 2 < nb) load(a0, bi + 2);
+        compute(a1, bi + 1);
+      }
+    }
+  }
+
+  // ---- epilogue: block max and first argmax per hidden row
+#pragma unroll
+  for (int n = 0; n < NT; ++n) {
+    float mx = -INFINITY;
+    int ax = 0x7fffffff;
+#pragma unroll
+    for (int t = 0; t < kMT; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int v = vrow0 + t * 16 + lq * 4 + e;
+        const float z = acc[t][n][e];
+        if (v < V && z > mx) { mx = z; ax = v; }
+      }
+#pragma unroll
+    for (int off = 16; off < kWave; off <<= 1) {
+      const float om = __shfl_xor(mx, off);
+      const int oa = __shfl_xor(ax, off);
+      if (better(mx, ax, om, oa)) { mx = om; ax = oa; }
+    }
+    if (lq == 0) { red_m[wave][n * 16 + lr] = mx; red_i[wave][n * 16 + lr] = ax; }
+  }
+  __syncthreads();
+
+  float bmax[NT], cexp[NT];
+  bool live[NT];
+#pragma unroll
+  for (int n = 0; n < NT; ++n) {
+    const int c = n * 16 + lr;
+    float m = red_m[0][c];
+    for (int w = 1; w < kWaves; ++w) m = fmaxf(m, red_m[w][c]);
+    bmax[n] = m;
+    const int r = r0 + c;
+    live[n] = r < R;
+    const float tr = live[n] ? temp[r] : 1.f;
+    cexp[n] = tr > 0.f ? kLog2e / tr : 0.f;   // 0: greedy row, p is written by the finalize
+    float s = 0.f;
+#pragma unroll
+    for (int t = 0; t < kMT; ++t) {
+      const int v0 = vrow0 + t * 16 + lq * 4;
+      if (live[n] && logits != nullptr) {
+        float *dst = logits + (size_t)r * V + v0;
+        if (v0 + 3 < V && (V & 3) == 0) {
+          *reinterpret_cast<float4 *>(dst) =
+              make_float4(acc[t][n][0], acc[t][n][1], acc[t][n][2], acc[t][n][3]);
+        } else {
+          for (int e = 0; e < 4; ++e)
+            if (v0 + e < V) dst[e] = acc[t][n][e];
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float ex = (v0 + e < V) ? exp2f((acc[t][n][e] - m) * cexp[n]) : 0.f;
+        acc[t][n][e] = ex;
+        s += ex;
+      }
+    }
+#pragma unroll
+    for (int off = 16; off < kWave; off <<= 1) s += __shfl_xor(s, off);
+    if (lq == 0) red_s[wave][c] = s;
+  }
+  __syncthreads();
+
+  if (wave == 0 && lq == 0) {
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      const int c = n * 16 + lr, r = r0 + c;
+      if (r >= R) continue;
+      float m = red_m[0][c];
+      int a = red_i[0][c];
+      for (int w = 1; w < kWaves; ++w)
+        if (better(m, a, red_m[w][c], red_i[w][c])) { m = red_m[w][c]; a = red_i[w][c]; }
+      const float s = ((red_s[0][c] + red_s[1][c]) + red_s[2][c]) + red_s[3][c];
+      stats[(size_t)blk * R + r] = make_float2(m, s);
+      amax[(size_t)blk * R + r] = a;
+    }
+  }
+#pragma unroll
+  for (int n = 0; n < NT; ++n) {
+    const int r = r0 + n * 16 + lr;
+    if (!live[n] || cexp[n] == 0.f) continue;
+#pragma unroll
+    for (int t = 0; t < kMT; ++t) {
+      const int v0 = vrow0 + t * 16 + lq * 4;
+      float *dst = probs + (size_t)r * V + v0;
+      if (v0 + 3 < V && (V & 3) == 0) {
+        *reinterpret_cast<float4 *>(dst) =
+            make_float4(acc[t][n][0], acc[t][n][1], acc[t][n][2], acc[t][n][3]);
+      } else {
+        for (int e = 0; e < 4; ++e)
+          if (v0 + e < V) dst[e] = acc[t][n][e];
+      }
+    }
+  }
+}
+
+// Merge the block statistics of row blockIdx.y and normalise its chunk of p in place.
+// Grid: (ceil(V / kFinChunk), R).
+__global__ __launch_bounds__(kThreads) void lm_head_finalize(
+    float *__restrict__ probs, const float2 *__restrict__ stats, const int *__restrict__ amax,
+    const float *__restrict__ temp, int R, int V, int nblk) {
+  __shared__ float sm[kThreads];
+  __shared__ int si[kThreads];
+  const int r = blockIdx.y, tid = threadIdx.x;
+  const float tr = temp[r];
+  const bool greedy = !(tr > 0.f);
+  const float c = greedy ? 0.f : kLog2e / tr;
+
+  float m = -INFINITY;
+  int a = 0x7fffffff;
+  for (int b = tid; b < nblk; b += kThreads) {
+    const float2 st = stats[(size_t)b * R + r];
+    const int ia = amax[(size_t)b * R + r];
+    if (better(m, a, st.x, ia)) { m = st.x; a = ia; }
+  }
+  sm[tid] = m;
+  si[tid] = a;
+  __syncthreads();
+  for (int s = kThreads / 2; s > 0; s >>= 1) {
+    if (tid < s && better(sm[tid], si[tid], sm[tid + s], si[tid + s])) {
+      sm[tid] = sm[tid + s];
+      si[tid] = si[tid + s];
+    }
+    __syncthreads();
+  }
+  const float gmax = sm[0];
+  const int garg = si[0];
+  __syncthreads();
+
+  const int v0 = blockIdx.x * kFinChunk;
+  const int v1 = min(V, v0 + kFinChunk);
+  float *row = probs + (size_t)r * V;
+  if (greedy) {
+    for (int v = v0 + tid; v < v1; v += kThreads) row[v] = (v == garg) ? 1.f : 0.f;
+    return;
+  }
+  float s = 0.f;
+  for (int b = tid; b < nblk; b += kThreads) {
+    const float2 st = stats[(size_t)b * R + r];
+    s += st.y * exp2f((st.x - gmax) * c);
+  }
+  sm[tid] = s;
+  __syncthreads();
+  for (int h = kThreads / 2; h > 0; h >>= 1) {
+    if (tid < h) sm[tid] += sm[tid + h];
+    __syncthreads();
+  }
+  const float inv = 1.f / sm[0];
+  if ((V & 3) == 0) {
+    for (int v = v0 + tid * 4; v < v1; v += kThreads * 4) {
+      const float f = exp2f((stats[(size_t)(v / kBlockRows) * R + r].x - gmax) * c) * inv;
+      float4 x = *reinterpret_cast<float4 *>(row + v);
+      x.x *= f; x.y *= f; x.z *= f; x.w *= f;
+      *reinterpret_cast<float4 *>(row + v) = x;
+    }
+  } else {
+    for (int v = v0 + tid; v < v1; v += kThreads) {
+      const float f = exp2f((stats[(size_t)(v / kBlockRows) * R + r].x - gmax) * c) * inv;
+      row[v] *= f;
+    }
+  }
+}
+
+template <typename T, int NT>
+int launch_nt(const void *X, const void *W, const float *temp, float *logits, float *probs,
+              float2 *stats, int *amax, int R, int H, int V, hipStream_t st) {
+  using M = Mma<T>;
+  const int nks = (H + M::kStep - 1) / M::kStep;
+  const int rows = min(NT * 16, R);
+  const int esz = (int)sizeof(T);
+  int kcs = (kXBudget / (rows * esz) - M::kEPL) / M::kStep;
+  kcs = max(kDepth, kcs / kDepth * kDepth);
+  kcs = min(kcs, (nks + kDepth - 1) / kDepth * kDepth);
+  const size_t lds = (size_t)rows * (kcs * M::kStep + M::kEPL) * esz;
+  const int nblk = spec::ceil_div(V, kBlockRows);
+  dim3 grid(nblk, spec::ceil_div(R, NT * 16));
+  hipLaunchKernelGGL((lm_head_kernel<T, NT>), grid, dim3(kThreads), lds, st,
+                     static_cast<const T *>(X), static_cast<const T *>(W), temp, logits, probs,
+                     stats, amax, R, H, V, kcs);
+  return spec::launched("lm_head_kernel");
+}
+
+template <typename T>
+int launch(int NT, const void *X, const void *W, const float *temp, float *logits, float *probs,
+           float2 *stats, int *amax, int R, int H, int V, hipStream_t st) {
+  switch (NT) {
+    case 1: return launch_nt<T, 1>(X, W, temp, logits, probs, stats, amax, R, H, V, st);
+    case 2: return launch_nt<T, 2>(X, W, temp, logits, probs, stats, amax, R, H, V, st);
+    case 3: return launch_nt<T, 3>(X, W, temp, logits, probs, stats, amax, R, H, V, st);
+    case 4: return launch_nt<T, 4>(X, W, temp, logits, probs, stats, amax, R, H, V, st);
+    case 5: return launch_nt<T, 5>(X, W, temp, logits, probs, stats, amax, R, H, V, st);
+    case 6: return launch_nt<T, 6>(X, W, temp, logits, probs, stats, amax, R, H, V, st);
+    case 7: return launch_nt<T, 7>(X, W, temp, logits, probs, stats, amax, R, H, V, st);
+    default: return launch_nt<T, 8>(X, W, temp, logits, probs, stats, amax, R, H, V, st);
+  }
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace
+
+extern "C" size_t spec_lm_head_workspace(int R, int H, int V) {
+  if (R <= 0 || H <= 0 || V <= 0) {
+    spec::fail(SPEC_EINVAL, "spec_lm_head_workspace: R=%d H=%d V=%d must be positive", R, H, V);
+    return 0;
+  }
+  const size_t nblk = (size_t)spec::ceil_div(V, kBlockRows);
+  return spec::align_up(nblk * R * sizeof(float2), 256) + spec::align_up(nblk * R * sizeof(int), 256);
+}
+
+extern "C" int spec_lm_head(const void *hidden, const void *weight, const float *temperature,
+                            float *logits, float *probs, int R, int H, int V, spec_dtype dtype,
+                            void *workspace, size_t workspace_bytes, void *stream) {
+  spec::clear_error();
+  SPEC_REQUIRE(hidden && weight && temperature && probs, SPEC_EINVAL,
+               "spec_lm_head: hidden, weight, temperature and probs must be non-null");
+  SPEC_REQUIRE(R > 0 && H > 0 && V > 0, SPEC_EINVAL,
+               "spec_lm_head: R=%d H=%d V=%d must be positive", R, H, V);
+  SPEC_REQUIRE(dtype == SPEC_F32 || dtype == SPEC_BF16, SPEC_EUNSUPPORTED,
+               "spec_lm_head: unsupported dtype %d", (int)dtype);
+  SPEC_REQUIRE(H % 8 == 0, SPEC_EUNSUPPORTED, "spec_lm_head: H=%d must be a multiple of 8", H);
+  SPEC_REQUIRE(aligned16(hidden) && aligned16(weight) && aligned16(probs) &&
+                   (logits == nullptr || aligned16(logits)),
+               SPEC_EINVAL, "spec_lm_head: hidden, weight, probs and logits need 16-byte alignment");
+  const size_t need = spec_lm_head_workspace(R, H, V);
+  SPEC_REQUIRE(workspace != nullptr && workspace_bytes >= need, SPEC_EWORKSPACE,
+               "spec_lm_head: workspace of %zu bytes needed, %zu given", need, workspace_bytes);
+  const size_t nblk = (size_t)spec::ceil_div(V, kBlockRows);
+  float2 *stats = static_cast<float2 *>(workspace);
+  int *amax = reinterpret_cast<int *>(static_cast<char *>(workspace) +
+                                      spec::align_up(nblk * R * sizeof(float2), 256));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int NT = min(8, spec::ceil_div(R, 16));
+  int rc = dtype == SPEC_BF16
+               ? launch<uint16_t>(NT, hidden, weight, temperature, logits, probs, stats, amax, R, H, V, st)
+               : launch<float>(NT, hidden, weight, temperature, logits, probs, stats, amax, R, H, V, st);
+  if (rc != SPEC_OK) return rc;
+  dim3 grid(spec::ceil_div(V, kFinChunk), R);
+  hipLaunchKernelGGL(lm_head_finalize, grid, dim3(kThreads), 0, st, probs, stats, amax,
+                     temperature, R, V, (int)nblk);
+  return spec::launched("lm_head_finalize");
+}

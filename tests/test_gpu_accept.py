@@ -1,0 +1,83 @@
+"""GPU parity of spec_accept: accept counts and emitted tokens bit-exact against the oracle,
+given identical fp32 p / q and uniforms."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from workloads import WORKLOADS, gen
+from cases import accept_inputs, gpu_accept, say, dev
+
+pytestmark = pytest.mark.gpu
+
+
+def compare(draft, q, p, u, label):
+    say(f"[accept] {label}: B={p.shape[0]} k={p.shape[1] - 1} V={p.shape[2]}")
+    n, tok = gpu_accept(draft, q, p, u, dev())
+    n_ref, tok_ref = oracle.verify_accept(draft, q, p, u)
+    assert np.array_equal(n, n_ref), (n, n_ref)
+    assert np.array_equal(tok, tok_ref)
+    say(f"    mean accepted {n.mean():.3f}, tokens/step {(n + 1).mean():.3f}")
+    return n
+
+
+@pytest.mark.parametrize("name,batch,vocab", [
+    ("tiny_fp32_b1_k2", 256, None),
+    ("b1_k2_sliding256_8k", 48, None),
+    ("b1_k4_global512_32k", 12, None),
+    ("b8_ragged_k5_hybrid", 8, None),
+    ("b32_k2_mixed_16k", 32, None),
+    ("b8_ragged_k5_hybrid", 40, 1000),
+])
+def test_workload_recipes(name, batch, vocab):
+    w = WORKLOADS[name]
+    draft, q, p, u = accept_inputs(w, step=1, batch=batch, vocab=vocab)
+    compare(draft, q, p, u, name)
+
+
+def test_greedy_tiny():
+    w = WORKLOADS["tiny_fp32_b1_k2"]
+    draft, q, p, u = accept_inputs(w, step=2, batch=128, temps=np.zeros(128))
+    n = compare(draft, q, p, u, "greedy")
+    # greedy: accepted prefix = drafts matching the target's argmax
+    for b in range(128):
+        j = 0
+        while j < 2 and draft[b, j] == int(np.argmax(p[b, j])):
+            j += 1
+        assert n[b] == j
+
+
+def test_edge_cases():
+    rng = np.random.default_rng(5)
+    B, k, V = 6, 3, 777
+    p = rng.dirichlet(np.ones(V), size=(B, k + 1)).astype(np.float32)
+    q = rng.dirichlet(np.ones(V), size=(B, k)).astype(np.float32)
+    draft = rng.integers(0, V, size=(B, k)).astype(np.int32)
+    u = rng.random((B, k + 1), dtype=np.float32)
+    draft[0, 0] = -5                      # out of range: rejected
+    draft[1, 1] = V + 3
+    q[2] = p[2, :k]                       # q == p: every draft accepted, bonus draw
+    draft[2] = np.argmax(p[2, :k], axis=1)
+    # residual empty after flooring: q just above p everywhere, u near 1 rejects draft 0
+    q[3, 0] = np.nextafter(p[3, 0], np.float32(1))
+    u[3, 0] = np.float32(1 - 2 ** -24)
+    u[4] = 0.0                            # smallest uniforms
+    u[5] = np.float32(1 - 2 ** -24)       # largest uniforms
+    n = compare(draft, q, p, u, "edge cases")
+    assert n[0] == 0 and n[1] == 1 and n[2] == k and n[3] == 0
+
+
+def test_k_zero_plain_sampling():
+    rng = np.random.default_rng(6)
+    B, V = 64, 3000
+    p = rng.dirichlet(np.ones(V) * 0.3, size=(B, 1)).astype(np.float32)
+    u = rng.random((B, 1), dtype=np.float32)
+    compare(np.zeros((B, 0), np.int32), np.zeros((B, 0, V), np.float32), p, u, "k=0")
+
+
+def test_deterministic_repeat():
+    w = WORKLOADS["b32_k2_mixed_16k"]
+    draft, q, p, u = accept_inputs(w, step=3, vocab=50000)
+    a = gpu_accept(draft, q, p, u, dev())
+    b = gpu_accept(draft, q, p, u, dev())
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])

@@ -1,0 +1,98 @@
+"""GPU parity of spec_verify_attn (split-K paged GQA verify attention) against the fp64
+oracle: all workload layers at full size (sampled sequences for the largest batch), plus
+ragged and degenerate cases."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import speculative_decoding_decode_amd as sv
+from workloads import WORKLOADS, gen
+from workloads.configs import Layer, Workload
+from cases import TOL, attn_inputs, oracle_attn, say, dev
+
+pytestmark = pytest.mark.gpu
+
+
+def check(inp, dtype, label, rows=None):
+    B, K1, Hq, D = inp["q"].shape
+    say(f"[attn] {label}: B={B} K1={K1} Hq={Hq} Hkv={inp['k_pool'].shape[1]} D={D} "
+        f"window={inp['window']} ctx={inp['ctx_lens'].cpu().tolist()[:8]}")
+    out = sv.verify_attn(**inp)
+    torch.cuda.synchronize()
+    ref = oracle_attn(inp, rows=rows)
+    got = out.cpu().numpy().astype(np.float64)
+    if rows is not None:
+        sel = tuple(np.array(rows).T)
+        got, ref = got[sel], ref[sel]
+    err = np.abs(got - ref).max()
+    say(f"    max |err| = {err:.3e}")
+    assert np.isfinite(got).all()
+    assert err <= TOL[dtype]
+    return out
+
+
+def test_tiny_fp32_workload():
+    w = WORKLOADS["tiny_fp32_b1_k2"]
+    check(attn_inputs(w, 0, dev()), "f32", "tiny fp32")
+
+
+@pytest.mark.parametrize("name", ["b1_k2_sliding256_8k", "b1_k4_global512_32k"])
+def test_batch1_workloads(name):
+    w = WORKLOADS[name]
+    check(attn_inputs(w, 0, dev()), "bf16", name)
+
+
+@pytest.mark.parametrize("layer", [0, 3])
+def test_ragged_hybrid_workload(layer):
+    w = WORKLOADS["b8_ragged_k5_hybrid"]
+    check(attn_inputs(w, layer, dev()), "bf16", f"b8 ragged layer {layer}")
+
+
+@pytest.mark.parametrize("layer", [0, 1])
+def test_batch32_workload_sampled(layer):
+    w = WORKLOADS["b32_k2_mixed_16k"]
+    inp = attn_inputs(w, layer, dev())
+    rows = [(b, i) for b in (0, 5, 13, 31) for i in range(w.k1)]
+    check(inp, "bf16", f"b32 layer {layer}", rows=rows)
+
+
+def small_workload(dtype, hq, hkv, d, window, k, batch=3):
+    kind = "sliding" if window else "global"
+    return Workload(name="ragged", batch=batch, k=k, layers=(Layer(kind, hq, hkv, d, window),),
+                    ctx="fixed:16", hidden=8, vocab=8, dtype=dtype, logit_recipe="gauss",
+                    noise_key="sigma:1", temperatures=(1.0,), seed=11)
+
+
+@pytest.mark.parametrize("dtype,hq,hkv,d,window,k", [
+    ("bf16", 6, 3, 128, 37, 3), ("f32", 4, 1, 256, 0, 1), ("f32", 8, 2, 512, 100, 5),
+    ("bf16", 12, 1, 64, 0, 4), ("bf16", 4, 4, 256, 1, 2), ("f32", 16, 2, 64, 0, 9)])
+def test_ragged_small(dtype, hq, hkv, d, window, k):
+    w = small_workload(dtype, hq, hkv, d, window, k)
+    ctx = np.array([k + 1, 333, 170], dtype=np.int32)         # minimal, ragged, page-ragged
+    table, P = gen.page_tables(w, ctx, max_pages=30)
+    table[1, 7] = P + 50                                       # a page id outside the pool
+    inp = attn_inputs(w, 0, dev(), ctx=ctx, table=table, num_pages=P)
+    check(inp, dtype, f"ragged small {dtype} hq{hq}/hkv{hkv} d{d} w{window} k{k}")
+
+
+def test_context_clamped_to_table():
+    w = small_workload("bf16", 8, 2, 256, 0, 2, batch=2)
+    ctx = np.array([64, 64], dtype=np.int32)
+    table, P = gen.page_tables(w, ctx, max_pages=4)
+    inp = attn_inputs(w, 0, dev(), ctx=ctx, table=table, num_pages=P)
+    ref_out = sv.verify_attn(**inp).clone()
+    inp["ctx_lens"] = torch.tensor([64, 10_000], dtype=torch.int32, device=dev())
+    out = sv.verify_attn(**inp)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref_out)
+
+
+def test_deterministic_repeat():
+    w = WORKLOADS["b1_k2_sliding256_8k"]
+    inp = attn_inputs(w, 0, dev(), step=4)
+    a = sv.verify_attn(**inp).clone()
+    b = sv.verify_attn(**inp)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)

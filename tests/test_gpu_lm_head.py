@@ -1,0 +1,89 @@
+"""GPU parity of spec_lm_head (MFMA contraction + row softmax) against the fp64 oracle."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import speculative_decoding_decode_amd as sv
+from workloads import WORKLOADS, gen
+from cases import TOL, P_TOL, say, dev
+
+pytestmark = pytest.mark.gpu
+
+
+def run_and_compare(x, w, temps, dtype, rows=None, label=""):
+    d = dev()
+    say(f"[lm_head] {label}: R={x.shape[0]} H={x.shape[1]} V={w.shape[0]} {dtype}")
+    t = torch.as_tensor(np.asarray(temps, np.float32), device=d)
+    logits, p = sv.lm_head(x.to(d), w.to(d), t, want_logits=True)
+    _, p2 = sv.lm_head(x.to(d), w.to(d), t)            # logits not stored: same p
+    torch.cuda.synchronize()
+    assert torch.equal(p, p2)
+    rows = list(range(x.shape[0])) if rows is None else rows
+    z_ref = oracle.logits(x.cpu(), w.cpu(), rows=rows)
+    p_ref = oracle.probabilities(z_ref, np.asarray(temps)[rows])
+    z = logits.cpu().numpy()[rows].astype(np.float64)
+    pg = p.cpu().numpy()[rows].astype(np.float64)
+    ez, ep = np.abs(z - z_ref).max(), np.abs(pg - p_ref).max()
+    say(f"    max |logit err| = {ez:.3e}   max |p err| = {ep:.3e}")
+    assert ez <= TOL[dtype]
+    assert ep <= P_TOL
+    np.testing.assert_allclose(pg.sum(axis=1), 1.0, atol=1e-5)
+    for i, r in enumerate(rows):
+        if not temps[r] > 0:   # greedy: one-hot at an index whose oracle logit is maximal
+            j = int(np.argmax(pg[i]))
+            assert pg[i, j] == 1.0 and pg[i].sum() == 1.0
+            assert z_ref[i, j] >= z_ref[i].max() - TOL[dtype]
+
+
+def test_tiny_fp32_workload():
+    w = WORKLOADS["tiny_fp32_b1_k2"]
+    x = gen.hidden_states(w)
+    W = gen.lm_head_table(w)
+    run_and_compare(x, W, [1.0, 0.0, 0.5], "f32", label="tiny fp32")
+
+
+@pytest.mark.parametrize("R,H,V,dtype", [(19, 264, 5003, "bf16"), (5, 8, 17, "f32"),
+                                          (130, 64, 1000, "bf16"), (1, 512, 4100, "f32"),
+                                          (33, 2568, 2048, "bf16")])
+def test_ragged_shapes(R, H, V, dtype):
+    torch.manual_seed(R * 7 + V)
+    td = torch.float32 if dtype == "f32" else torch.bfloat16
+    x = torch.randn(R, H).to(td)
+    W = (torch.randn(V, H) / math.sqrt(H)).to(td)
+    temps = [(0.0, 0.7, 1.0, 2.0)[r % 4] for r in range(R)]
+    run_and_compare(x, W, temps, dtype, label="ragged")
+
+
+def test_greedy_ties_take_first_index():
+    d = dev()
+    x = torch.ones(2, 16, dtype=torch.float32)
+    W = torch.zeros(600, 16, dtype=torch.float32)
+    W[[7, 300, 599]] = 1.0                         # three equal maxima across blocks
+    t = torch.zeros(2, device=d)
+    _, p = sv.lm_head(x.to(d), W.to(d), t)
+    pc = p.cpu()
+    assert pc[:, 7].tolist() == [1.0, 1.0] and float(pc.sum()) == 2.0
+
+
+@pytest.mark.parametrize("name", ["b1_k2_sliding256_8k", "b1_k4_global512_32k"])
+def test_full_size_batch1(name):
+    w = WORKLOADS[name]
+    d = dev()
+    x = gen.hidden_states(w, d)
+    W = gen.lm_head_table(w, d)
+    temps = gen.row_temperatures(w)
+    run_and_compare(x, W, temps, "bf16", label=name)
+
+
+@pytest.mark.parametrize("name", ["b8_ragged_k5_hybrid", "b32_k2_mixed_16k"])
+def test_full_size_batched_sampled_rows(name):
+    w = WORKLOADS[name]
+    d = dev()
+    x = gen.hidden_states(w, d)
+    W = gen.lm_head_table(w, d)
+    temps = gen.row_temperatures(w)
+    rows = sorted(set([0, 1, w.rows // 2, w.rows - 1, 17 % w.rows, 40 % w.rows]))
+    run_and_compare(x, W, temps, "bf16", rows=rows, label=name)
