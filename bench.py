@@ -1,0 +1,327 @@
+"""Benchmark of the verify step on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+
+Workload: batch 1, k = 2 drafts (3 verified positions), one sliding-window attention layer
+(8 query / 2 KV heads, head dim 256, window 1024) over a paged 8192-token cache (16-token
+pages, randomly permuted), lm-head 2560 x 262144 bf16, temperature 1; drafter / target noise
+tuned for about 47% acceptance at the first position.  One step = spec_verify_attn ->
+spec_lm_head -> spec_accept on inputs resident in HBM; 64 input sets (queries, cache regions,
+hidden states, drafter distributions and drafts) rotate over the steps, and every step has
+its own uniforms, so KV and drafter rows are not cache-resident from the previous step.
+
+Drafter stand-in: the drafter shares the target's vocab table (the serving guide's section 1
+table: the input embedding table is shared), so its distribution q is the lm-head call applied
+to the target hidden state plus N(0, sigma^2) noise; drafts are drawn from q by the accept call
+with k = 0.  Both are prepared before timing.
+
+Prints one JSON line: verified tokens/s (accepted drafts + the correction/bonus token per
+step), the step's HBM GB/s for the algorithmic bytes (KV read + lm-head table), a roofline
+object for the dominant kernel (the lm-head contraction, timed with HIP events the library
+records around it) and the fp64 oracle's CPU rate on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+WORKLOAD = "b1_k2_sliding256_8k"
+NSETS = 64
+SAMPLE_EVERY = 16     # steps whose contraction kernel is bracketed by HIP events
+HBM_PEAK_GBS = 8000.0
+METRIC = "verified tokens/sec and verify-step HBM GB/s (% peak), batch 1, k=2, 8K ctx"
+
+
+class HipEvents:
+    """hipEvent_t handles through the process's HIP runtime (the one torch loaded)."""
+
+    def __init__(self, n: int):
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.ev = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            if self.hip.hipEventCreate(ctypes.byref(e)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            self.ev.append(e)
+
+    def record(self, i, stream):
+        if self.hip.hipEventRecord(self.ev[i], stream) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def ms(self, a, b) -> float:
+        out = ctypes.c_float()
+        if self.hip.hipEventElapsedTime(ctypes.byref(out), self.ev[a], self.ev[b]) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(out.value)
+
+    def close(self):
+        for e in self.ev:
+            self.hip.hipEventDestroy(e)
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(w, ctx_lens):
+    """KV bytes every verify step must read plus the lm-head table: the roofline numerator."""
+    L = w.layers[0]
+    esz = 2 if w.dtype == "bf16" else 4
+    kv = 0
+    for c in ctx_lens:
+        lo = max(0, int(c) - w.k1 - L.window + 1) if L.window else 0
+        kv += (int(c) - lo) * L.hkv * L.head_dim * esz * 2
+    table = w.vocab * w.hidden * esz
+    return kv, table
+
+
+def prepare(w, device, torch, sv, gen, noise_sigma):
+    """Device-resident inputs for NSETS verify steps."""
+    B, k, K1 = w.batch, w.k, w.k1
+    L = w.layers[0]
+    ctx1 = gen.context_lengths(w)                            # [B] for one step
+    # one shared page pool holding the caches of all sets (NSETS * B sequences)
+    wpool = w.__class__(**{**w.__dict__, "batch": NSETS * B})
+    ctx_all = np.tile(ctx1, NSETS).astype(np.int32)
+    table_all, P = gen.page_tables(wpool, ctx_all)
+    kpool, vpool = gen.kv_pools(wpool, 0, P, device)
+    tables = torch.from_numpy(table_all).to(device)
+    ctx_dev = torch.from_numpy(ctx_all).to(device)
+    W = gen.lm_head_table(w, device)
+    temps = torch.from_numpy(gen.row_temperatures(w)).to(device)
+    sigma = noise_sigma(w)
+    sets = []
+    for s in range(NSETS):
+        q = gen.queries(w, 0, device, step=s)
+        x = gen.hidden_states(w, device, step=s)
+        noise = gen.drafter_hidden_noise(w, device, step=s)
+        xd = (x.float() + sigma * noise).to(x.dtype).view(B, K1, -1)[:, :k].reshape(B * k, -1)
+        xd = xd.contiguous()
+        # drafter distributions through the shared table, then drafts drawn from them
+        tq = temps.view(B, K1)[:, :k].reshape(-1).contiguous()
+        _, qd = sv.lm_head(xd, W, tq)
+        ud = torch.from_numpy(gen.rng(w, gen.STREAM_DRAFT, s).random((B * k, 1), dtype=np.float32)).to(device)
+        _, tok = sv.accept(None, None, qd.view(B * k, 1, -1), ud)
+        draft = tok[:, 0].reshape(B, k).contiguous()
+        sets.append(dict(q=q, x=x, qd=qd.view(B, k, -1), draft=draft,
+                         table=tables[s * B:(s + 1) * B], ctx=ctx_dev[s * B:(s + 1) * B]))
+    torch.cuda.synchronize(device)
+    return dict(kpool=kpool, vpool=vpool, W=W, temps=temps, sets=sets, P=P, ctx=ctx1,
+                max_pages=table_all.shape[1], scale=1.0 / math.sqrt(L.head_dim))
+
+
+def cpu_baseline(w, gen, seconds_target=12.0, max_steps=400):
+    """The fp64 oracle (untuned) on a bounded sample of the same workload."""
+    import oracle
+    from oracle.step import verify_step
+    from workloads import noise_sigma
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas_threads = 1
+    L = w.layers[0]
+    ctx = gen.context_lengths(w)
+    table, P = gen.page_tables(w, ctx)
+    kp, vp = gen.kv_pools(w, 0, P, "cpu")
+    W = gen.lm_head_table(w, "cpu")
+    W64 = W.double().numpy()                       # static weights: converted once, untimed
+    temps = gen.row_temperatures(w)
+    sigma = noise_sigma(w)
+    tokens_out, t_total, steps = 0, 0.0, 0
+    while steps < max_steps and (steps < 2 or t_total < seconds_target):
+        q = gen.queries(w, 0, "cpu", step=steps)
+        x = gen.hidden_states(w, "cpu", step=steps)
+        u = gen.uniforms(w, step=steps)
+        # drafter stand-in (untimed): the shared table applied to a perturbed hidden state
+        xd = (x.float() + sigma * gen.drafter_hidden_noise(w, "cpu", step=steps)).to(x.dtype)
+        rows = [b * w.k1 + i for b in range(w.batch) for i in range(w.k)]
+        zq = oracle.logits(xd, W64, rows=rows)
+        qd = oracle.probabilities(zq, temps[rows]).astype(np.float32).reshape(w.batch, w.k, -1)
+        draft = gen.draw_drafts(w, qd, gen.temperatures(w), step=steps)
+        layer = dict(q=q, k_pool=kp, v_pool=vp, page_table=table, ctx_lens=ctx,
+                     window=L.window, scale=1 / math.sqrt(L.head_dim))
+        t0 = time.perf_counter()
+        _, _, _, n, _ = verify_step([layer], x, W64, temps, draft, qd, u)
+        t_total += time.perf_counter() - t0
+        tokens_out += int(np.sum(n + 1))
+        steps += 1
+    return {"value": tokens_out / t_total, "unit": "verified tokens/s", "cores": int(blas_threads),
+            "kind": "oracle",
+            "sample": f"{steps} verify steps of the same workload (fp64 numpy oracle: attention, "
+                      f"lm-head, softmax, accept; table converted to fp64 once, untimed), "
+                      f"{t_total:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the verify step "
+              f"runs on a single MI355X).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import speculative_decoding_decode_amd as sv
+    from speculative_decoding_decode_amd import _lib
+    from speculative_decoding_decode_amd.telemetry import accept_stats
+    from workloads import WORKLOADS, gen, noise_sigma
+
+    if not torch.cuda.is_available():
+        raise RuntimeError("bench.py needs a GPU")
+    if not os.path.exists(_lib.LIB_PATH):
+        from speculative_decoding_decode_amd import build
+        build.build()
+    device = torch.device("cuda", 0)
+    torch.cuda.set_device(device)
+    w = WORKLOADS[WORKLOAD]
+    L = w.layers[0]
+    B, k, K1, V, H = w.batch, w.k, w.k1, w.vocab, w.hidden
+    R = B * K1
+
+    log(f"[bench] preparing {NSETS} input sets for {WORKLOAD}")
+    inp = prepare(w, device, torch, sv, gen, noise_sigma)
+    lib = _lib.load()
+    stream = torch.cuda.current_stream(device)
+    sptr = ctypes.c_void_p(stream.cuda_stream) if stream.cuda_stream else None
+    nsteps = args.warmup + args.steps
+    U = torch.from_numpy(np.stack([gen.uniforms(w, step=1000 + s) for s in range(nsteps)])).to(device)
+    n_out = torch.empty((nsteps, B), dtype=torch.int32, device=device)
+    tok_out = torch.empty((nsteps, B, K1), dtype=torch.int32, device=device)
+    attn_out = torch.empty((B, K1, L.hq, L.head_dim), dtype=torch.float32, device=device)
+    probs = torch.empty((R, V), dtype=torch.float32, device=device)
+    ws_attn = torch.empty(sv.verify_attn_workspace_bytes(B, K1, L.hq, L.hkv, L.head_dim,
+                                                         inp["max_pages"], L.window),
+                          dtype=torch.uint8, device=device)
+    ws_lm = torch.empty(sv.lm_head_workspace_bytes(R, H, V), dtype=torch.uint8, device=device)
+    ws_acc = torch.empty(sv.accept_workspace_bytes(B, k, V), dtype=torch.uint8, device=device)
+    dt = sv.SPEC_BF16 if w.dtype == "bf16" else sv.SPEC_F32
+
+    # argument tuples of the three C calls for every input set (pointers only)
+    calls = []
+    for s in inp["sets"]:
+        a = (s["q"].data_ptr(), inp["kpool"].data_ptr(), inp["vpool"].data_ptr(),
+             s["table"].data_ptr(), s["ctx"].data_ptr(), attn_out.data_ptr(), B, K1, L.hq, L.hkv,
+             L.head_dim, w.page_size, inp["P"], inp["max_pages"], L.window, inp["scale"], dt,
+             ws_attn.data_ptr(), ws_attn.numel(), sptr)
+        m = (s["x"].data_ptr(), inp["W"].data_ptr(), inp["temps"].data_ptr(), None,
+             probs.data_ptr(), R, H, V, dt, ws_lm.data_ptr(), ws_lm.numel(), sptr)
+        calls.append((a, m, s["draft"].data_ptr(), s["qd"].data_ptr()))
+
+    def step(i, ev=None, evi=0):
+        a, m, d_ptr, q_ptr = calls[i % NSETS]
+        rc = lib.spec_verify_attn(*a)
+        if rc:
+            _lib.check("spec_verify_attn", rc)
+        if ev is not None:
+            lib.spec_profile_lm_head(ev.ev[evi], ev.ev[evi + 1])
+        rc = lib.spec_lm_head(*m)
+        if rc:
+            _lib.check("spec_lm_head", rc)
+        rc = lib.spec_accept(d_ptr, q_ptr, probs.data_ptr(), U[i].data_ptr(),
+                             n_out[i].data_ptr(), tok_out[i].data_ptr(), B, k, V,
+                             ws_acc.data_ptr(), ws_acc.numel(), sptr)
+        if rc:
+            _lib.check("spec_accept", rc)
+
+    log(f"[bench] warmup {args.warmup} steps")
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize(device)
+
+    K = args.steps
+    nsamp = (K + SAMPLE_EVERY - 1) // SAMPLE_EVERY
+    ev_lm = HipEvents(2 * nsamp)
+    ev_tot = HipEvents(2)
+    log(f"[bench] timing {K} steps (contraction bracketed on every {SAMPLE_EVERY}th step)")
+    torch.cuda.synchronize(device)
+    t0 = time.perf_counter()
+    ev_tot.record(0, sptr)
+    for j in range(K):
+        if j % SAMPLE_EVERY == 0:
+            step(args.warmup + j, ev_lm, 2 * (j // SAMPLE_EVERY))
+        else:
+            step(args.warmup + j)
+    ev_tot.record(1, sptr)
+    torch.cuda.synchronize(device)
+    t1 = time.perf_counter()
+    wall = t1 - t0
+
+    lm_ms = np.array([ev_lm.ms(2 * i, 2 * i + 1) for i in range(nsamp)])
+    gpu_total_ms = ev_tot.ms(0, 1)
+    ev_lm.close()
+    ev_tot.close()
+    n_all = n_out[args.warmup:].cpu().numpy()
+    tok_all = tok_out[args.warmup:].cpu().numpy()
+    assert ((tok_all >= -1) & (tok_all < V)).all()
+    emitted = int(np.sum(n_all + 1))
+    stats = accept_stats(n_all, k)
+    value = emitted / wall
+    kv_bytes, table_bytes = algorithmic_bytes(w, inp["ctx"])
+    step_bytes = kv_bytes + table_bytes
+    ms_per_step = wall * 1e3 / K
+    lm_avg_ms = float(lm_ms.mean())
+    achieved = table_bytes / (lm_avg_ms * 1e-3) / 1e9
+    step_gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
+    log(f"[bench] gpu {gpu_total_ms * 1e3 / K:.1f} us/step; lm-head contraction {lm_avg_ms * 1e3:.1f} us = {achieved:.0f} GB/s; "
+        f"wall {ms_per_step * 1e3:.1f} us/step; acceptance pos {stats.per_position}")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (fp64 oracle)")
+        cpu = cpu_baseline(w, gen)
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "verified tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD, "batch": B, "k": k, "verified_positions": K1,
+                   "ctx": int(inp["ctx"][0]), "attention": f"sliding hd{L.head_dim} window "
+                   f"{L.window}, {L.hq}q/{L.hkv}kv, 16-token pages",
+                   "lm_head": f"{H} x {V} bf16", "input_sets": NSETS},
+        "step_hbm_gbs": round(step_gbs, 1),
+        "step_frac_peak": round(step_gbs / HBM_PEAK_GBS, 4),
+        "step_algorithmic_bytes": step_bytes,
+        "gpu_event_ms_per_step": round(gpu_total_ms / K, 5),
+        "tokens_per_step": round(stats.mean_accepted_length, 4),
+        "acceptance_per_position": [round(a, 4) for a in stats.per_position],
+        "roofline": {"kernel": "lm_head_kernel (vocab-table contraction)", "bound": "hbm",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "bytes_per_launch": table_bytes, "avg_launch_us": round(lm_avg_ms * 1e3, 2),
+                     "launches_timed": int(nsamp)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

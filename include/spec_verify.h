@@ -112,6 +112,13 @@ int spec_lm_head(const void *hidden, const void *weight, const float *temperatur
                  float *logits, float *probs, int R, int H, int V, spec_dtype dtype,
                  void *workspace, size_t workspace_bytes, void *stream);
 
+/* Profiling aid for (ii): arms a one-shot bracket around the contraction kernel of the next
+ * spec_lm_head call on this thread.  `start_event` / `stop_event` are hipEvent_t handles
+ * created by the caller (either may be NULL); the call records them on its stream right
+ * before and right after the contraction kernel (not around the softmax finalize), then
+ * disarms.  Returns SPEC_OK. */
+int spec_profile_lm_head(void *start_event, void *stop_event);
+
 /* ------------------------------------------------------------------------------------------
  * (iii) Accept / reject (Leviathan et al.), with the correction or bonus token.
  *

@@ -30,6 +30,7 @@ constexpr int kThreads = 256;
 constexpr int kMaxK = 63;
 constexpr float kFixedScale = 274877906944.0f;   // 2^38
 constexpr int kUniformBits = 24;
+constexpr int kMaxE = 64;                        // elements per thread per chunk (V <= 4M)
 
 __device__ __forceinline__ uint64_t fixed_weight(float x) {
   const float s = x * kFixedScale;   // exact: power-of-two scaling
@@ -80,10 +81,29 @@ __device__ void block_inclusive_scan(uint64_t *sh) {
   }
 }
 
+// Chunk c of a sequence's row: elements [c * chunk, (c + 1) * chunk), chunk = kThreads * E;
+// thread t owns the E contiguous elements starting at c * chunk + t * E (E is 4 in the common
+// case, one float4 load per row).
+template <int E>
+__device__ __forceinline__ void load_run(const float *__restrict__ row, int j0, int V, float (&x)[E]) {
+  if (E == 4 && j0 + 3 < V && (V & 3) == 0) {
+    const float4 t = *reinterpret_cast<const float4 *>(row + j0);
+    x[0] = t.x; x[1] = t.y; x[2] = t.z; x[3] = t.w;
+  } else {
+#pragma unroll
+    for (int e = 0; e < E; ++e) x[e] = j0 + e < V ? row[j0 + e] : 0.f;
+  }
+}
+
+__device__ __forceinline__ uint64_t residual(uint64_t P, uint64_t Q) { return P > Q ? P - Q : 0ull; }
+
+// Grid: (nchunks, B).  Round trips: drafts, then p/q at the drafts (n), then the chunk of the
+// row the draw uses.
+template <int E>
 __global__ __launch_bounds__(kThreads) void accept_chunks(
     const int32_t *__restrict__ draft, const float *__restrict__ q, const float *__restrict__ p,
     const float *__restrict__ u, uint64_t *__restrict__ wsum, uint64_t *__restrict__ psum,
-    int32_t *__restrict__ nbuf, int k, int V, int chunk, int nchunks) {
+    int32_t *__restrict__ nbuf, int k, int V, int nchunks) {
   __shared__ int n_sh;
   __shared__ uint64_t red[kThreads];
   const int b = blockIdx.y, c = blockIdx.x, tid = threadIdx.x;
@@ -94,68 +114,59 @@ __global__ __launch_bounds__(kThreads) void accept_chunks(
   __syncthreads();
   const int n = n_sh;
   const float *prow = p + ((size_t)b * (k + 1) + n) * V;
-  const float *qrow = n < k ? q + ((size_t)b * k + n) * V : nullptr;
-  const int lo = c * chunk, hi = min(V, lo + chunk);
-  uint64_t sw = 0, sp = 0;
-  for (int j = lo + tid; j < hi; j += kThreads) {
-    const uint64_t P = fixed_weight(prow[j]);
+  const int j0 = c * kThreads * E + tid * E;
+  float pv[E], qv[E];
+  load_run<E>(prow, j0, V, pv);
+  const bool corr = n < k;
+  if (corr) load_run<E>(q + ((size_t)b * k + n) * V, j0, V, qv);
+  uint64_t sp = 0, sw = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const uint64_t P = fixed_weight(pv[e]);
     sp += P;
-    if (qrow) {
-      const uint64_t Q = fixed_weight(qrow[j]);
-      sw += P > Q ? P - Q : 0ull;
-    }
+    if (corr) sw += residual(P, fixed_weight(qv[e]));
   }
   sp = block_sum(sp, red);
-  if (qrow) sw = block_sum(sw, red);
+  if (corr) sw = block_sum(sw, red);
   if (tid == 0) {
-    wsum[(size_t)b * nchunks + c] = qrow ? sw : sp;
+    wsum[(size_t)b * nchunks + c] = corr ? sw : sp;
     psum[(size_t)b * nchunks + c] = sp;
     if (c == 0) nbuf[b] = n;
   }
 }
 
+// Grid: (B).  Round trips: n, chunk sums, uniform and drafts together; then the chosen chunk.
+template <int E>
 __global__ __launch_bounds__(kThreads) void accept_draw(
     const int32_t *__restrict__ draft, const float *__restrict__ q, const float *__restrict__ p,
     const float *__restrict__ u, const uint64_t *__restrict__ wsum,
     const uint64_t *__restrict__ psum, const int32_t *__restrict__ nbuf,
-    int32_t *__restrict__ n_out, int32_t *__restrict__ tokens, int k, int V, int chunk,
-    int nchunks) {
+    int32_t *__restrict__ n_out, int32_t *__restrict__ tokens, int k, int V, int nchunks) {
   __shared__ uint64_t sh[kThreads];
   __shared__ int found_sh;
   __shared__ uint64_t base_sh;
   const int b = blockIdx.x, tid = threadIdx.x;
-  const int n = nbuf[b];
   const int K1 = k + 1;
+  // everything independent of n at once (nchunks <= kThreads)
+  const int n = nbuf[b];
+  const uint64_t cw = tid < nchunks ? wsum[(size_t)b * nchunks + tid] : 0ull;
+  const uint64_t cp = tid < nchunks ? psum[(size_t)b * nchunks + tid] : 0ull;
+  const float uk = u[(size_t)b * K1 + k];
+  const int dtok = tid < k ? draft[(size_t)b * k + tid] : -1;
 
-  // chunk sums; the correction weights fall back to p's when they are all zero
-  const uint64_t *cs = wsum + (size_t)b * nchunks;
-  const int per = (nchunks + kThreads - 1) / kThreads;   // chunks per thread (contiguous)
-  uint64_t mine = 0;
-  for (int e = 0; e < per; ++e) {
-    const int c = tid * per + e;
-    if (c < nchunks) mine += cs[c];
-  }
-  const uint64_t wtot = block_sum(mine, sh);
-  const bool fallback = n < k && wtot == 0ull;
-  if (fallback) {
-    cs = psum + (size_t)b * nchunks;
-    mine = 0;
-    for (int e = 0; e < per; ++e) {
-      const int c = tid * per + e;
-      if (c < nchunks) mine += cs[c];
-    }
-  }
-  const uint64_t total = fallback ? block_sum(mine, sh) : wtot;
+  const uint64_t wtot = block_sum(cw, sh);
+  const bool fallback = n < k && wtot == 0ull;   // every correction weight 0: draw from p
+  const uint64_t mine = fallback ? cp : cw;
+  const uint64_t total = fallback ? block_sum(cp, sh) : wtot;
 
   int y = 0;
   if (total > 0ull) {
-    const float uk = u[(size_t)b * K1 + k];
     const float uf = uk * 16777216.0f;   // exact scaling by 2^24
     uint64_t m = uf > 0.f ? static_cast<uint64_t>(uf) : 0ull;
     if (m > (1ull << kUniformBits) - 1) m = (1ull << kUniformBits) - 1;
     const uint64_t t = (m * total) >> kUniformBits;   // m < 2^24, total < 2^40
 
-    // 1) the chunk whose running sum first exceeds t
+    // 1) the chunk whose running sum first exceeds t (one chunk per thread)
     sh[tid] = mine;
     __syncthreads();
     block_inclusive_scan(sh);
@@ -163,35 +174,26 @@ __global__ __launch_bounds__(kThreads) void accept_draw(
     __syncthreads();
     {
       const uint64_t incl = sh[tid], excl = incl - mine;
-      if (excl <= t && t < incl) {   // exactly one thread owns t
-        uint64_t run = excl;
-        for (int e = 0; e < per; ++e) {
-          const int c = tid * per + e;
-          if (c >= nchunks) break;
-          if (t < run + cs[c]) { found_sh = c; base_sh = run; break; }
-          run += cs[c];
-        }
-      }
+      if (excl <= t && t < incl) { found_sh = tid; base_sh = excl; }
     }
     __syncthreads();
     const int cstar = found_sh;
     const uint64_t t2 = t - base_sh;
 
-    // 2) inside the chunk: running weights in index order
-    const float *prow = p + ((size_t)b * K1 + n) * V;
-    const float *qrow = (n < k && !fallback) ? q + ((size_t)b * k + n) * V : nullptr;
-    const int lo = cstar * chunk, hi = min(V, lo + chunk);
-    const int epl = (chunk + kThreads - 1) / kThreads;   // elements per thread (contiguous)
-    const int j0 = lo + tid * epl;
-    uint64_t wsum_t = 0;
-    for (int e = 0; e < epl; ++e) {
-      const int j = j0 + e;
-      if (j >= hi) break;
-      const uint64_t P = fixed_weight(prow[j]);
-      uint64_t w = P;
-      if (qrow) { const uint64_t Q = fixed_weight(qrow[j]); w = P > Q ? P - Q : 0ull; }
-      wsum_t += w;
+    // 2) inside the chunk: running weights in index order, E contiguous elements per thread
+    const bool corr = n < k && !fallback;
+    const int j0 = cstar * kThreads * E + tid * E;
+    float pv[E], qv[E];
+    load_run<E>(p + ((size_t)b * K1 + n) * V, j0, V, pv);
+    if (corr) load_run<E>(q + ((size_t)b * k + n) * V, j0, V, qv);
+    uint64_t w[E], wsum_t = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const uint64_t P = fixed_weight(pv[e]);
+      w[e] = corr ? residual(P, fixed_weight(qv[e])) : P;
+      wsum_t += w[e];
     }
+    __syncthreads();
     sh[tid] = wsum_t;
     __syncthreads();
     block_inclusive_scan(sh);
@@ -201,39 +203,32 @@ __global__ __launch_bounds__(kThreads) void accept_draw(
       const uint64_t incl = sh[tid], excl = incl - wsum_t;
       if (excl <= t2 && t2 < incl) {
         uint64_t run = excl;
-        for (int e = 0; e < epl; ++e) {
-          const int j = j0 + e;
-          if (j >= hi) break;
-          const uint64_t P = fixed_weight(prow[j]);
-          uint64_t w = P;
-          if (qrow) { const uint64_t Q = fixed_weight(qrow[j]); w = P > Q ? P - Q : 0ull; }
-          if (t2 < run + w) { found_sh = j; break; }
-          run += w;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          if (t2 < run + w[e]) { found_sh = j0 + e; break; }
+          run += w[e];
         }
       }
     }
     __syncthreads();
     y = found_sh;
   }
-  if (tid <= k) {
-    int tok = -1;
-    if (tid < n) tok = draft[(size_t)b * k + tid];
-    else if (tid == n) tok = y;
-    tokens[(size_t)b * K1 + tid] = tok;
-  }
+  if (tid <= k) tokens[(size_t)b * K1 + tid] = tid < n ? dtok : (tid == n ? y : -1);
   if (tid == 0) n_out[b] = n;
 }
 
 struct AcceptPlan {
-  int chunk, nchunks;
+  int E, chunk, nchunks;
   size_t off_w, off_p, off_n, bytes;
 };
 
 AcceptPlan plan(int B, int V) {
   AcceptPlan pl;
-  // chunk = 256 * E elements; at most 256 chunks per sequence (256 * 256 elements or fewer
-  // per thread pass); V = 262144 gives 256 chunks of 1024.
-  const int E = max(1, spec::ceil_div(V, kThreads * 256));
+  // chunk = 256 * E elements, E a power of two chosen so that a row has at most 256 chunks
+  // (one chunk sum per thread of the draw kernel); V = 262144 gives 256 chunks of 1024.
+  int E = 1;
+  while (E < kMaxE && (long)kThreads * E * kThreads < V) E *= 2;
+  pl.E = E;
   pl.chunk = kThreads * E;
   pl.nchunks = spec::ceil_div(V, pl.chunk);
   const size_t sums = (size_t)B * pl.nchunks * sizeof(uint64_t);
@@ -242,6 +237,19 @@ AcceptPlan plan(int B, int V) {
   pl.off_n = pl.off_p + spec::align_up(sums, 256);
   pl.bytes = pl.off_n + spec::align_up((size_t)B * sizeof(int32_t), 256);
   return pl;
+}
+
+template <int E>
+int launch(const AcceptPlan &pl, const int32_t *draft, const float *q, const float *p,
+           const float *uniforms, int32_t *n_accepted, int32_t *tokens, int B, int k, int V,
+           uint64_t *wsum, uint64_t *psum, int32_t *nbuf, hipStream_t st) {
+  hipLaunchKernelGGL((accept_chunks<E>), dim3(pl.nchunks, B), dim3(kThreads), 0, st, draft, q,
+                     p, uniforms, wsum, psum, nbuf, k, V, pl.nchunks);
+  int rc = spec::launched("accept_chunks");
+  if (rc != SPEC_OK) return rc;
+  hipLaunchKernelGGL((accept_draw<E>), dim3(B), dim3(kThreads), 0, st, draft, q, p, uniforms,
+                     wsum, psum, nbuf, n_accepted, tokens, k, V, pl.nchunks);
+  return spec::launched("accept_draw");
 }
 
 }  // namespace
@@ -262,6 +270,8 @@ extern "C" int spec_accept(const int32_t *draft, const float *q, const float *p,
                "spec_accept: B=%d k=%d V=%d out of range", B, k, V);
   SPEC_REQUIRE(k <= kMaxK, SPEC_EUNSUPPORTED, "spec_accept: k=%d exceeds %d (one wave per sequence)",
                k, kMaxK);
+  SPEC_REQUIRE((long)V <= (long)kMaxE * kThreads * kThreads, SPEC_EUNSUPPORTED,
+               "spec_accept: V=%d exceeds %ld", V, (long)kMaxE * kThreads * kThreads);
   SPEC_REQUIRE(p && uniforms && n_accepted && tokens && (k == 0 || (draft && q)), SPEC_EINVAL,
                "spec_accept: null pointer argument");
   const AcceptPlan pl = plan(B, V);
@@ -272,11 +282,13 @@ extern "C" int spec_accept(const int32_t *draft, const float *q, const float *p,
   uint64_t *psum = reinterpret_cast<uint64_t *>(ws + pl.off_p);
   int32_t *nbuf = reinterpret_cast<int32_t *>(ws + pl.off_n);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  hipLaunchKernelGGL(accept_chunks, dim3(pl.nchunks, B), dim3(kThreads), 0, st, draft, q, p,
-                     uniforms, wsum, psum, nbuf, k, V, pl.chunk, pl.nchunks);
-  int rc = spec::launched("accept_chunks");
-  if (rc != SPEC_OK) return rc;
-  hipLaunchKernelGGL(accept_draw, dim3(B), dim3(kThreads), 0, st, draft, q, p, uniforms, wsum,
-                     psum, nbuf, n_accepted, tokens, k, V, pl.chunk, pl.nchunks);
-  return spec::launched("accept_draw");
+  switch (pl.E) {
+    case 1: return launch<1>(pl, draft, q, p, uniforms, n_accepted, tokens, B, k, V, wsum, psum, nbuf, st);
+    case 2: return launch<2>(pl, draft, q, p, uniforms, n_accepted, tokens, B, k, V, wsum, psum, nbuf, st);
+    case 4: return launch<4>(pl, draft, q, p, uniforms, n_accepted, tokens, B, k, V, wsum, psum, nbuf, st);
+    case 8: return launch<8>(pl, draft, q, p, uniforms, n_accepted, tokens, B, k, V, wsum, psum, nbuf, st);
+    case 16: return launch<16>(pl, draft, q, p, uniforms, n_accepted, tokens, B, k, V, wsum, psum, nbuf, st);
+    case 32: return launch<32>(pl, draft, q, p, uniforms, n_accepted, tokens, B, k, V, wsum, psum, nbuf, st);
+    default: return launch<64>(pl, draft, q, p, uniforms, n_accepted, tokens, B, k, V, wsum, psum, nbuf, st);
+  }
 }

@@ -26,7 +26,8 @@ constexpr int kThreads = 256;
 constexpr int kPage = 16;
 constexpr int kRows = 32;            // query rows per workgroup
 constexpr int kTargetWGs = 4096;     // splits are sized so the grid reaches about this many
-constexpr int kMinPagesPerSplit = 2;
+constexpr int kMinPagesPerSplit = 1;
+constexpr int kMaxPagesPerSplit = 256;   // page ids of a split are staged in LDS
 constexpr int kMaxSplits = 4096;
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -50,7 +51,11 @@ __device__ __host__ inline Span seq_span(int ctx, int K1, int window, int max_pa
 template <int D, typename T>
 struct AttnShape {
   static constexpr int kEPG = 16 / (int)sizeof(T);       // elements per 16-byte group
+  static constexpr int kGPR = D / kEPG;                  // 16-byte groups per row
   static constexpr int kKStr = D + kEPG;                 // LDS row stride of K/V tiles
+  static constexpr int kTileG = kPage * kGPR;            // 16-byte groups per K (or V) page tile
+  static constexpr int kGPT = (kTileG + kThreads - 1) / kThreads;   // per thread
+  static constexpr int kQPT = (kRows * kGPR + kThreads - 1) / kThreads;
   static constexpr int kCPT = D >= 256 ? D / 256 : 1;    // output columns per thread
   static constexpr int kNCol = D / kCPT;                 // threads covering one row's columns
   static constexpr int kRG = kThreads / kNCol;           // row groups
@@ -60,6 +65,9 @@ struct AttnShape {
 };
 
 // Grid: (nsplit, Hkv * nrowchunk, B).
+// Memory round trips before the first page is in LDS: the split's page ids (issued first),
+// then the queries and the first page's K/V together; while a page is being scored the next
+// page's K/V are already in flight in registers.
 template <int D, typename T>
 __global__ __launch_bounds__(kThreads) void attn_partial(
     const T *__restrict__ q, const T *__restrict__ kpool, const T *__restrict__ vpool,
@@ -74,6 +82,7 @@ __global__ __launch_bounds__(kThreads) void attn_partial(
   float *ss = reinterpret_cast<float *>(vs + kPage * S::kKStr);    // [kRows][16]
   __shared__ float m_sh[kRows], l_sh[kRows], alpha_sh[kRows];
   __shared__ int tq_sh[kRows];
+  __shared__ int pid_sh[kMaxPagesPerSplit];
 
   const int tid = threadIdx.x;
   const int b = blockIdx.z, g = blockIdx.y % Hkv, rc = blockIdx.y / Hkv, s = blockIdx.x;
@@ -82,46 +91,75 @@ __global__ __launch_bounds__(kThreads) void attn_partial(
   const int ns = (sp.np + pps - 1) / pps;
   if (s >= ns) return;
   const int pg_begin = sp.p0 + s * pps;
-  const int pg_end = min(sp.p0 + sp.np, pg_begin + pps);
+  const int npg = min(sp.p0 + sp.np, pg_begin + pps) - pg_begin;
   const int rr0 = rc * kRows;
   const int nr = min(kRows, GK1 - rr0);
 
-  // queries of this chunk, pre-scaled by scale * log2(e)
-  constexpr int GPR = D / S::kEPG;   // 16-byte groups per row
-  for (int e = tid; e < nr * GPR; e += kThreads) {
-    const int r = e / GPR, gi = e - r * GPR;
-    const int rr = rr0 + r, i = rr / G, h = g * G + (rr - i * G);
-    const uint4 raw = *reinterpret_cast<const uint4 *>(q + (((size_t)b * K1 + i) * Hq + h) * D + gi * S::kEPG);
-    float f[S::kEPG];
-    spec::unpack16(raw, f, T{});
+  // (1) page ids of the split, then the queries (registers).  Loads are unconditional with
+  // clamped indices so the wait counts the compiler inserts stay exact.
+  const int pid_reg = table[(size_t)b * max_pages + pg_begin + min(tid, npg - 1)];
+  uint4 qraw[S::kQPT];
 #pragma unroll
-    for (int x = 0; x < S::kEPG; ++x) qs[r * D + gi * S::kEPG + x] = f[x] * qscale;
+  for (int x = 0; x < S::kQPT; ++x) {
+    const int e = min(tid + x * kThreads, nr * S::kGPR - 1);
+    const int r = e / S::kGPR, gi = e - r * S::kGPR;
+    const int rr = rr0 + r, i = rr / G, h = g * G + (rr - i * G);
+    qraw[x] = *reinterpret_cast<const uint4 *>(q + (((size_t)b * K1 + i) * Hq + h) * D + gi * S::kEPG);
   }
+  if (tid < npg) pid_sh[tid] = (pid_reg >= 0 && pid_reg < num_pages) ? pid_reg : -1;
   if (tid < kRows) {
     m_sh[tid] = -INFINITY;
     l_sh[tid] = 0.f;
     tq_sh[tid] = tid < nr ? sp.ctx - K1 + (rr0 + tid) / G : -1;
   }
+  __syncthreads();
+
+  // (2) K/V of page 0 in flight while the queries land in LDS
+  uint4 kcur[S::kGPT], vcur[S::kGPT], knxt[S::kGPT], vnxt[S::kGPT];
+  auto fetch = [&](uint4(&kr)[S::kGPT], uint4(&vr)[S::kGPT], int i) {
+    const int pid = pid_sh[i];
+    const T *kb = kpool + ((size_t)(pid < 0 ? 0 : pid) * Hkv + g) * kPage * D;
+    const T *vb = vpool + ((size_t)(pid < 0 ? 0 : pid) * Hkv + g) * kPage * D;
+#pragma unroll
+    for (int x = 0; x < S::kGPT; ++x) {
+      const int e = tid + x * kThreads;
+      const bool ok = pid >= 0 && e < S::kTileG;
+      kr[x] = ok ? *reinterpret_cast<const uint4 *>(kb + e * S::kEPG) : uint4{0u, 0u, 0u, 0u};
+      vr[x] = ok ? *reinterpret_cast<const uint4 *>(vb + e * S::kEPG) : uint4{0u, 0u, 0u, 0u};
+    }
+  };
+  fetch(kcur, vcur, 0);
+#pragma unroll
+  for (int x = 0; x < S::kQPT; ++x) {
+    const int e = tid + x * kThreads;
+    if (e < nr * S::kGPR) {
+      float f[S::kEPG];
+      spec::unpack16(qraw[x], f, T{});
+#pragma unroll
+      for (int y = 0; y < S::kEPG; ++y) qs[e * S::kEPG + y] = f[y] * qscale;   // row-major [r][D]
+    }
+  }
+
   float acc[S::kRPT][S::kCPT];
 #pragma unroll
   for (int ri = 0; ri < S::kRPT; ++ri)
 #pragma unroll
     for (int c = 0; c < S::kCPT; ++c) acc[ri][c] = 0.f;
   const int rg = tid / S::kNCol, col0 = tid - rg * S::kNCol;
-  __syncthreads();
 
-  for (int pg = pg_begin; pg < pg_end; ++pg) {
-    const int pid = table[(size_t)b * max_pages + pg];
-    if (pid < 0 || pid >= num_pages) continue;   // uniform: hides the page's keys
-    const T *kb = kpool + ((size_t)pid * Hkv + g) * kPage * D;
-    const T *vb = vpool + ((size_t)pid * Hkv + g) * kPage * D;
-    for (int e = tid; e < kPage * GPR; e += kThreads) {
-      const int row = e / GPR, gi = e - row * GPR;
-      *reinterpret_cast<uint4 *>(ks + row * S::kKStr + gi * S::kEPG) =
-          *reinterpret_cast<const uint4 *>(kb + row * D + gi * S::kEPG);
-      *reinterpret_cast<uint4 *>(vs + row * S::kKStr + gi * S::kEPG) =
-          *reinterpret_cast<const uint4 *>(vb + row * D + gi * S::kEPG);
+  for (int i = 0; i < npg; ++i) {
+#pragma unroll
+    for (int x = 0; x < S::kGPT; ++x) {
+      const int e = tid + x * kThreads;
+      if (e < S::kTileG) {
+        const int row = e / S::kGPR, gi = e - row * S::kGPR;
+        *reinterpret_cast<uint4 *>(ks + row * S::kKStr + gi * S::kEPG) = kcur[x];
+        *reinterpret_cast<uint4 *>(vs + row * S::kKStr + gi * S::kEPG) = vcur[x];
+      }
     }
+    if (i + 1 < npg) fetch(knxt, vnxt, i + 1);
+    const bool page_ok = pid_sh[i] >= 0;   // uniform
+    const int pg = pg_begin + i;
     __syncthreads();
 
     // scores and online-softmax state: 16 consecutive lanes = one query row x 16 keys
@@ -129,7 +167,7 @@ __global__ __launch_bounds__(kThreads) void attn_partial(
       const int idx = base + tid, rr = idx >> 4, j = idx & 15;
       const bool rowok = rr < nr;
       float sc = -INFINITY;
-      if (rowok) {
+      if (rowok && page_ok) {
         const int pos = pg * kPage + j, t = tq_sh[rr];
         if (pos <= t && (window == 0 || t - pos < window)) {
           const T *kr = ks + j * S::kKStr;
@@ -166,24 +204,38 @@ __global__ __launch_bounds__(kThreads) void attn_partial(
     }
     __syncthreads();
 
-    // value update: acc[row][col] = alpha * acc + sum_j p_j v_j[col]
+    // value update: acc[row][col] = alpha * acc + sum_j p_j v_j[col]; the 16 values of this
+    // thread's columns are read once and reused for every row
+    float vv[kPage][S::kCPT];
+#pragma unroll
+    for (int j = 0; j < kPage; ++j)
+#pragma unroll
+      for (int c = 0; c < S::kCPT; ++c)
+        vv[j][c] = spec::Elem<T>::to_f32(vs[j * S::kKStr + col0 + c * S::kNCol]);
 #pragma unroll
     for (int ri = 0; ri < S::kRPT; ++ri) {
       const int rr = rg + ri * S::kRG;
       if (rr < nr) {
         const float a = alpha_sh[rr];
+        const float4 *pr4 = reinterpret_cast<const float4 *>(ss + rr * kPage);
+        float pj[kPage];
 #pragma unroll
-        for (int c = 0; c < S::kCPT; ++c) acc[ri][c] *= a;
-#pragma unroll 4
-        for (int j = 0; j < kPage; ++j) {
-          const float pj = ss[rr * kPage + j];
+        for (int j4 = 0; j4 < kPage / 4; ++j4) {
+          const float4 t = pr4[j4];
+          pj[4 * j4] = t.x; pj[4 * j4 + 1] = t.y; pj[4 * j4 + 2] = t.z; pj[4 * j4 + 3] = t.w;
+        }
 #pragma unroll
-          for (int c = 0; c < S::kCPT; ++c)
-            acc[ri][c] = fmaf(pj, spec::Elem<T>::to_f32(vs[j * S::kKStr + col0 + c * S::kNCol]), acc[ri][c]);
+        for (int c = 0; c < S::kCPT; ++c) {
+          float o = acc[ri][c] * a;
+#pragma unroll
+          for (int j = 0; j < kPage; ++j) o = fmaf(pj[j], vv[j][c], o);
+          acc[ri][c] = o;
         }
       }
     }
     __syncthreads();
+#pragma unroll
+    for (int x = 0; x < S::kGPT; ++x) { kcur[x] = knxt[x]; vcur[x] = vnxt[x]; }
   }
 
   const size_t base = ((size_t)(b * Hkv + g) * nsplit + s) * GK1 + rr0;
@@ -199,7 +251,13 @@ __global__ __launch_bounds__(kThreads) void attn_partial(
   }
 }
 
-// Grid: (K1 * Hq, B).  Merges the splits of one output row with log-sum-exp weights.
+// Grid: (K1 * Hq, D / 64, B).  Merges the splits of one output row (64 columns per workgroup)
+// with log-sum-exp weights.  Thread (c, sg) sums the splits s = sg (mod 4) of column c; the
+// split loads are issued 16 at a time so a merge costs a few memory round trips.
+constexpr int kCombCols = 64;
+constexpr int kCombGroups = kThreads / kCombCols;   // 4
+constexpr int kCombBatch = 32;
+
 template <int D>
 __global__ __launch_bounds__(kThreads) void attn_combine(
     const float2 *__restrict__ part_ml, const float *__restrict__ part_acc,
@@ -208,15 +266,32 @@ __global__ __launch_bounds__(kThreads) void attn_combine(
   __shared__ float w_sh[kMaxSplits];
   __shared__ float red[kThreads];
   const int tid = threadIdx.x;
-  const int row = blockIdx.x, b = blockIdx.y;
+  const int row = blockIdx.x, b = blockIdx.z;
   const int i = row / Hq, h = row - i * Hq;
   const int G = Hq / Hkv, g = h / G, rr = i * G + (h - g * G);
   const Span sp = seq_span(ctx_lens[b], K1, window, max_pages);
   const int ns = (sp.np + pps - 1) / pps;
   const size_t base = (size_t)(b * Hkv + g) * nsplit * GK1 + rr;   // + s * GK1
 
+  // all loads of the merge at once: (max, sum) of every split and up to kCombBatch partial
+  // outputs per thread (split s = sg + kCombGroups * u of column d)
+  const int c = tid % kCombCols, sg = tid / kCombCols;
+  const int d = blockIdx.y * kCombCols + c;
+  float2 ml[kMaxSplits / kThreads];
+#pragma unroll
+  for (int x = 0; x < kMaxSplits / kThreads; ++x) {
+    const int s = tid + x * kThreads;
+    ml[x] = s < ns ? part_ml[base + (size_t)s * GK1] : make_float2(-INFINITY, 0.f);
+  }
+  float v[kCombBatch];
+#pragma unroll
+  for (int u = 0; u < kCombBatch; ++u) {
+    const int s = sg + u * kCombGroups;
+    v[u] = s < ns ? part_acc[(base + (size_t)s * GK1) * D + d] : 0.f;
+  }
   float m = -INFINITY;
-  for (int s = tid; s < ns; s += kThreads) m = fmaxf(m, part_ml[base + (size_t)s * GK1].x);
+#pragma unroll
+  for (int x = 0; x < kMaxSplits / kThreads; ++x) m = fmaxf(m, ml[x].x);
   red[tid] = m;
   __syncthreads();
   for (int h2 = kThreads / 2; h2 > 0; h2 >>= 1) {
@@ -226,11 +301,14 @@ __global__ __launch_bounds__(kThreads) void attn_combine(
   const float M = red[0];
   __syncthreads();
   float l = 0.f;
-  for (int s = tid; s < ns; s += kThreads) {
-    const float2 ml = part_ml[base + (size_t)s * GK1];
-    const float w = ml.x == -INFINITY ? 0.f : exp2f(ml.x - M);
-    w_sh[s] = w;
-    l += w * ml.y;
+#pragma unroll
+  for (int x = 0; x < kMaxSplits / kThreads; ++x) {
+    const int s = tid + x * kThreads;
+    if (s < ns) {
+      const float w = ml[x].x == -INFINITY ? 0.f : exp2f(ml[x].x - M);
+      w_sh[s] = w;
+      l += w * ml[x].y;
+    }
   }
   red[tid] = l;
   __syncthreads();
@@ -239,12 +317,32 @@ __global__ __launch_bounds__(kThreads) void attn_combine(
     __syncthreads();
   }
   const float L = red[0];
-  const float inv = L > 0.f ? 1.f / L : 0.f;
-  float *dst = out + (((size_t)b * K1 + i) * Hq + h) * D;
-  for (int d = tid; d < D; d += kThreads) {
-    float o = 0.f;
-    for (int s = 0; s < ns; ++s) o = fmaf(w_sh[s], part_acc[(base + (size_t)s * GK1) * D + d], o);
-    dst[d] = o * inv;
+  __syncthreads();
+
+  float o = 0.f;
+#pragma unroll
+  for (int u = 0; u < kCombBatch; ++u) {
+    const int s = sg + u * kCombGroups;
+    if (s < ns) o = fmaf(w_sh[s], v[u], o);
+  }
+  for (int s0 = sg + kCombGroups * kCombBatch; s0 < ns; s0 += kCombGroups * kCombBatch) {
+    float v2[kCombBatch];
+#pragma unroll
+    for (int u = 0; u < kCombBatch; ++u) {
+      const int s = s0 + u * kCombGroups;
+      v2[u] = s < ns ? part_acc[(base + (size_t)s * GK1) * D + d] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < kCombBatch; ++u) {
+      const int s = s0 + u * kCombGroups;
+      if (s < ns) o = fmaf(w_sh[s], v2[u], o);
+    }
+  }
+  red[tid] = o;
+  __syncthreads();
+  if (sg == 0) {
+    const float tot = ((red[c] + red[c + kCombCols]) + red[c + 2 * kCombCols]) + red[c + 3 * kCombCols];
+    out[(((size_t)b * K1 + i) * Hq + h) * D + d] = L > 0.f ? tot / L : 0.f;
   }
 }
 
@@ -263,7 +361,7 @@ AttnPlan plan(int B, int K1, int Hq, int Hkv, int D, int max_pages, int window) 
   const long units = (long)B * Hkv * pl.nrowchunk;
   const int wanted = (int)max(1L, (kTargetWGs + units - 1) / units);
   pl.pps = max(kMinPagesPerSplit, spec::ceil_div(span, wanted));
-  pl.pps = max(pl.pps, spec::ceil_div(span, kMaxSplits));
+  pl.pps = min(max(pl.pps, spec::ceil_div(span, kMaxSplits)), kMaxPagesPerSplit);
   pl.nsplit = spec::ceil_div(span, pl.pps);
   const size_t rows = (size_t)B * Hkv * pl.nsplit * pl.GK1;
   pl.off_ml = 0;
@@ -294,7 +392,7 @@ int launch(const void *q, const void *kp, const void *vp, const int32_t *table,
                      max_pages, window, scale * kLog2e, pl.pps, pl.nsplit, pl.GK1);
   int rc = spec::launched("attn_partial");
   if (rc != SPEC_OK) return rc;
-  hipLaunchKernelGGL((attn_combine<D>), dim3(K1 * Hq, B), dim3(kThreads), 0, st, ml, acc, ctx,
+  hipLaunchKernelGGL((attn_combine<D>), dim3(K1 * Hq, D / kCombCols, B), dim3(kThreads), 0, st, ml, acc, ctx,
                      out, K1, Hq, Hkv, max_pages, window, pl.pps, pl.nsplit, pl.GK1);
   return spec::launched("attn_combine");
 }
@@ -324,6 +422,9 @@ int check_shape(int B, int K1, int Hq, int Hkv, int D, int page_size, int max_pa
   SPEC_REQUIRE(D == 64 || D == 128 || D == 256 || D == 512, SPEC_EUNSUPPORTED,
                "spec_verify_attn: head dim %d not in {64, 128, 256, 512}", D);
   SPEC_REQUIRE(page_size == kPage, SPEC_EUNSUPPORTED, "spec_verify_attn: page_size=%d, only 16", page_size);
+  SPEC_REQUIRE((long)max_pages <= (long)kMaxSplits * kMaxPagesPerSplit, SPEC_EUNSUPPORTED,
+               "spec_verify_attn: max_pages_per_seq=%d exceeds %d", max_pages,
+               kMaxSplits * kMaxPagesPerSplit);
   return SPEC_OK;
 }
 

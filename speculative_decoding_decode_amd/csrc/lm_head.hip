@@ -7,18 +7,22 @@
 // from memory (same guide, introduction).  At R = 3..96 rows the kernel is a stream over the
 // V x H table: every table element is read once from HBM and used R times.
 //
-// Design (gfx950):
-//  * one workgroup = 4 waves = 256 vocab rows ("block"); each wave owns 4 MFMA tiles of
-//    16 vocab rows and NT tiles of 16 hidden-state rows;
-//  * the table streams straight from HBM into registers as 16-byte fragments that are the A
-//    operand of v_mfma_f32_16x16x32_bf16 (fp32 tables: four v_mfma_f32_16x16x4_f32); loads are
-//    issued one batch of kDepth K-steps ahead of the MFMAs that consume them;
-//  * the hidden rows (the B operand) are staged once per chunk of the hidden dimension in LDS,
-//    so the only global traffic inside the loop is the table;
-//  * the epilogue turns the 256 x R logits of the block into per-block softmax statistics
-//    (max, sum of exp, first argmax) and writes exp(logit - block max) into p; a second small
-//    kernel merges the statistics of all blocks and rescales p in place (or writes the greedy
-//    one-hot rows).
+// Design (gfx950).  Two contraction kernels share one softmax finalize:
+//  * R <= 8 rows (batch-1 verification): a bandwidth-bound GEMV.  Each wave owns 64 table rows
+//    and streams them in order as a flat sequence of (row pair, 1 KB column chunk) items: every
+//    load instruction of the wave reads 1 KB of contiguous table with a nontemporal load (the
+//    table is used once per call), items are prefetched one tile ahead, the hidden rows sit in
+//    LDS and one LDS read of them serves two table rows; products accumulate in fp32 with
+//    v_dot2_f32_bf16 (fp32 tables: FMAs) and a wave reduction gives each row's logits.
+//    Measured on MI355X this streams the table at about 6.9 TB/s, against 4.8 TB/s for the
+//    MFMA tiling below (whose loads touch 16 rows x 64 B each).
+//  * R > 8 rows: MFMA.  One workgroup = 4 waves = 256 vocab rows; each wave owns 4 tiles of 16
+//    vocab rows and NT tiles of 16 hidden rows; table fragments are the A operand of
+//    v_mfma_f32_16x16x32_bf16 (fp32: four v_mfma_f32_16x16x4_f32), hidden rows are staged per
+//    chunk of the hidden dimension in LDS.
+//  * Both epilogues turn a 256-row vocab block into per-block softmax statistics (max, sum of
+//    exp, first argmax) and write exp(logit - block max) into p; lm_head_finalize merges the
+//    statistics of all blocks and rescales p in place (or writes the greedy one-hot rows).
 #include <math.h>
 
 #include "common.hpp"
@@ -36,6 +40,7 @@ constexpr int kBlockRows = kWaves * kMT * 16;     // 256 vocab rows per workgrou
 constexpr int kDepth = 4;                         // K-steps per load batch
 constexpr int kXBudget = 40 * 1024;               // LDS bytes for a staged hidden-row chunk
 constexpr int kFinChunk = 4096;                   // vocab entries per finalize workgroup
+constexpr size_t kGemvMaxLds = 128 * 1024;        // hidden rows resident in LDS (GEMV path)
 constexpr float kLog2e = 1.4426950408889634f;
 
 template <typename T> struct Mma;
@@ -249,70 +254,314 @@ __global__ __launch_bounds__(kThreads) void lm_head_kernel(
   }
 }
 
+
+// ------------------------------------------------------------------------- small-R GEMV path
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kGemvMaxR = 8;
+constexpr int kRowsPerWave = 64;     // one table row per lane in the epilogue
+constexpr int kTile = 2;             // items (row pair x 1 KB chunk) per prefetch tile
+
+template <typename T> struct Dot;
+template <> struct Dot<uint16_t> {
+  static constexpr int kEPL = 8;
+  __device__ static __forceinline__ float run(const uint4 &w, const uint4 &x, float s) {
+    s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.x), __builtin_bit_cast(bf16x2_t, x.x), s, false);
+    s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.y), __builtin_bit_cast(bf16x2_t, x.y), s, false);
+    s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.z), __builtin_bit_cast(bf16x2_t, x.z), s, false);
+    s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.w), __builtin_bit_cast(bf16x2_t, x.w), s, false);
+    return s;
+  }
+};
+template <> struct Dot<float> {
+  static constexpr int kEPL = 4;
+  __device__ static __forceinline__ float run(const uint4 &w, const uint4 &x, float s) {
+    s = fmaf(__uint_as_float(w.x), __uint_as_float(x.x), s);
+    s = fmaf(__uint_as_float(w.y), __uint_as_float(x.y), s);
+    s = fmaf(__uint_as_float(w.z), __uint_as_float(x.z), s);
+    s = fmaf(__uint_as_float(w.w), __uint_as_float(x.w), s);
+    return s;
+  }
+};
+
+__device__ __forceinline__ uint4 load_stream(const void *p) {
+  const u32x4_t t = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
+  return uint4{t.x, t.y, t.z, t.w};
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) v += __shfl_xor(v, off);
+  return v;
+}
+
+// Grid: ceil(V / 256).  RT = R (rows of hidden states), 1..8.
+template <typename T, int RT>
+__global__ __launch_bounds__(kThreads) void lm_head_gemv(
+    const T *__restrict__ X, const T *__restrict__ W, const float *__restrict__ temp,
+    float *__restrict__ logits, float *__restrict__ probs, float2 *__restrict__ stats,
+    int *__restrict__ amax, int H, int V) {
+  using Dt = Dot<T>;
+  constexpr int EPL = Dt::kEPL;
+  constexpr int CW = kWave * EPL;                   // elements per 1 KB chunk
+  extern __shared__ __align__(16) unsigned char smem[];
+  T *xs = reinterpret_cast<T *>(smem);               // [RT][H]
+  __shared__ float red_m[kWaves][RT];
+  __shared__ float red_s[kWaves][RT];
+  __shared__ int red_i[kWaves][RT];
+
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int blk = blockIdx.x;
+  const int v0 = blk * kBlockRows + wave * kRowsPerWave;
+  for (int e = threadIdx.x; e < RT * (H / EPL); e += kThreads)
+    reinterpret_cast<uint4 *>(xs)[e] = reinterpret_cast<const uint4 *>(X)[e];
+  __syncthreads();
+
+  const int NG = (H + CW - 1) / CW;                 // chunks per row
+  const int nitems = (kRowsPerWave / 2) * NG;       // (row pair, chunk) items of this wave
+  const int ntiles = (nitems + kTile - 1) / kTile;
+  float keep[RT];
+#pragma unroll
+  for (int r = 0; r < RT; ++r) keep[r] = -INFINITY;
+  float acc[2][RT];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int r = 0; r < RT; ++r) acc[i][r] = 0.f;
+
+  // (row pair, chunk) position of the next item to load and of the next item to consume,
+  // advanced incrementally (items are visited in order; no division in the loop)
+  int lpr = 0, lj = 0, cpr = 0, cj = 0;
+  auto load = [&](uint4(&w)[kTile][2], int tile) {
+#pragma unroll
+    for (int u = 0; u < kTile; ++u) {
+      const int item = tile * kTile + u;
+      const int col = lj * CW + lane * EPL;
+      const int v = v0 + 2 * lpr;
+      const bool ok = item < nitems && col < H;
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        w[u][i] = (ok && v + i < V) ? load_stream(W + (size_t)(v + i) * H + col) : uint4{0u, 0u, 0u, 0u};
+      if (++lj == NG) { lj = 0; ++lpr; }
+    }
+  };
+  auto compute = [&](const uint4(&w)[kTile][2], int tile) {
+#pragma unroll
+    for (int u = 0; u < kTile; ++u) {
+      const int item = tile * kTile + u;
+      if (item >= nitems) break;                    // uniform
+      const int pr = cpr, j = cj;
+      if (++cj == NG) { cj = 0; ++cpr; }
+      const int col = j * CW + lane * EPL;
+      if (col < H) {
+#pragma unroll
+        for (int r = 0; r < RT; ++r) {
+          const uint4 xv = *reinterpret_cast<const uint4 *>(xs + r * H + col);
+          acc[0][r] = Dt::run(w[u][0], xv, acc[0][r]);
+          acc[1][r] = Dt::run(w[u][1], xv, acc[1][r]);
+        }
+      }
+      if (j == NG - 1) {                            // row pair complete (uniform)
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int r = 0; r < RT; ++r) {
+            const float t = wave_sum(acc[i][r]);
+            if (lane == 2 * pr + i) keep[r] = t;
+            acc[i][r] = 0.f;
+          }
+      }
+    }
+  };
+  uint4 wa[kTile][2], wb[kTile][2];
+  load(wa, 0);
+  for (int t = 0; t < ntiles; t += 2) {
+    if (t + 1 < ntiles) load(wb, t + 1);
+    compute(wa, t);
+    if (t + 1 < ntiles) {
+      if (t + 2 < ntiles) load(wa, t + 2);
+      compute(wb, t + 1);
+    }
+  }
+
+  // ---- epilogue: this lane holds the logits of vocab row v0 + lane
+  const int v = v0 + lane;
+  const bool vok = v < V;
+#pragma unroll
+  for (int r = 0; r < RT; ++r) {
+    float mx = vok ? keep[r] : -INFINITY;
+    int ax = vok ? v : 0x7fffffff;
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1) {
+      const float om = __shfl_xor(mx, off);
+      const int oa = __shfl_xor(ax, off);
+      if (better(mx, ax, om, oa)) { mx = om; ax = oa; }
+    }
+    if (lane == 0) { red_m[wave][r] = mx; red_i[wave][r] = ax; }
+  }
+  __syncthreads();
+  float ex[RT];
+  bool greedy[RT];
+#pragma unroll
+  for (int r = 0; r < RT; ++r) {
+    float m = red_m[0][r];
+    for (int w2 = 1; w2 < kWaves; ++w2) m = fmaxf(m, red_m[w2][r]);
+    const float tr = temp[r];
+    greedy[r] = !(tr > 0.f);
+    const float c = greedy[r] ? 0.f : kLog2e / tr;
+    ex[r] = vok ? exp2f((keep[r] - m) * c) : 0.f;
+    const float sw = wave_sum(ex[r]);
+    if (lane == 0) red_s[wave][r] = sw;
+    if (vok && logits != nullptr) logits[(size_t)r * V + v] = keep[r];
+  }
+  __syncthreads();
+  if (wave == 0 && lane < RT) {
+    const int r = lane;
+    float m = red_m[0][r];
+    int a = red_i[0][r];
+    for (int w2 = 1; w2 < kWaves; ++w2)
+      if (better(m, a, red_m[w2][r], red_i[w2][r])) { m = red_m[w2][r]; a = red_i[w2][r]; }
+    const float sum = ((red_s[0][r] + red_s[1][r]) + red_s[2][r]) + red_s[3][r];
+    stats[(size_t)blk * RT + r] = make_float2(m, sum);
+    amax[(size_t)blk * RT + r] = a;
+  }
+#pragma unroll
+  for (int r = 0; r < RT; ++r)
+    if (vok && !greedy[r]) probs[(size_t)r * V + v] = ex[r];
+}
+
+template <typename T, int RT>
+int launch_gemv(const void *X, const void *W, const float *temp, float *logits, float *probs,
+                float2 *stats, int *amax, int H, int V, hipStream_t st) {
+  const size_t lds = (size_t)RT * H * sizeof(T);
+  static bool attr_set = false;
+  if (!attr_set && lds > 64 * 1024) {
+    if (hipFuncSetAttribute(reinterpret_cast<const void *>(&lm_head_gemv<T, RT>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+      return spec::fail(SPEC_EHIP, "spec_lm_head: cannot reserve %zu bytes of LDS", lds);
+    attr_set = true;
+  }
+  hipLaunchKernelGGL((lm_head_gemv<T, RT>), dim3(spec::ceil_div(V, kBlockRows)), dim3(kThreads),
+                     lds, st, static_cast<const T *>(X), static_cast<const T *>(W), temp, logits,
+                     probs, stats, amax, H, V);
+  return spec::launched("lm_head_gemv");
+}
+
+template <typename T>
+int launch_gemv_r(int R, const void *X, const void *W, const float *temp, float *logits,
+                  float *probs, float2 *stats, int *amax, int H, int V, hipStream_t st) {
+  switch (R) {
+    case 1: return launch_gemv<T, 1>(X, W, temp, logits, probs, stats, amax, H, V, st);
+    case 2: return launch_gemv<T, 2>(X, W, temp, logits, probs, stats, amax, H, V, st);
+    case 3: return launch_gemv<T, 3>(X, W, temp, logits, probs, stats, amax, H, V, st);
+    case 4: return launch_gemv<T, 4>(X, W, temp, logits, probs, stats, amax, H, V, st);
+    case 5: return launch_gemv<T, 5>(X, W, temp, logits, probs, stats, amax, H, V, st);
+    case 6: return launch_gemv<T, 6>(X, W, temp, logits, probs, stats, amax, H, V, st);
+    case 7: return launch_gemv<T, 7>(X, W, temp, logits, probs, stats, amax, H, V, st);
+    default: return launch_gemv<T, 8>(X, W, temp, logits, probs, stats, amax, H, V, st);
+  }
+}
+
 // Merge the block statistics of row blockIdx.y and normalise its chunk of p in place.
-// Grid: (ceil(V / kFinChunk), R).
+// Grid: (ceil(V / kFinChunk), R).  Every load the workgroup needs (its share of the row's
+// block statistics, the statistics of the blocks it rescales, its p entries) is issued before
+// the first wait, so the kernel costs one memory round trip plus two LDS reductions.
+constexpr int kFinStatsPerThread = 4;            // up to 4 * 256 blocks = V <= 262144 in one pass
+constexpr int kFinPerThread = kFinChunk / kThreads;   // 16 p entries (4 float4)
+constexpr int kFinBlocks = kFinChunk / kBlockRows;    // 16 blocks per chunk
+
 __global__ __launch_bounds__(kThreads) void lm_head_finalize(
     float *__restrict__ probs, const float2 *__restrict__ stats, const int *__restrict__ amax,
     const float *__restrict__ temp, int R, int V, int nblk) {
   __shared__ float sm[kThreads];
   __shared__ int si[kThreads];
+  __shared__ float fac[kFinBlocks];
   const int r = blockIdx.y, tid = threadIdx.x;
   const float tr = temp[r];
   const bool greedy = !(tr > 0.f);
   const float c = greedy ? 0.f : kLog2e / tr;
+  const int v0 = blockIdx.x * kFinChunk;
+  const int blk0 = v0 / kBlockRows;
+  float *row = probs + (size_t)r * V;
+  const bool vec = (V & 3) == 0;
 
-  float m = -INFINITY;
-  int a = 0x7fffffff;
-  for (int b = tid; b < nblk; b += kThreads) {
-    const float2 st = stats[(size_t)b * R + r];
-    const int ia = amax[(size_t)b * R + r];
-    if (better(m, a, st.x, ia)) { m = st.x; a = ia; }
+  // p entries of this chunk: 4 float4 per thread (vector path)
+  float4 pv[kFinPerThread / 4];
+  if (!greedy && vec) {
+#pragma unroll
+    for (int i = 0; i < kFinPerThread / 4; ++i) {
+      const int v = v0 + (tid + i * kThreads) * 4;
+      pv[i] = v < V ? *reinterpret_cast<const float4 *>(row + v) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
   }
+  // statistics of the chunk's own blocks (for the rescale factors)
+  float own_m = 0.f;
+  if (tid < kFinBlocks && blk0 + tid < nblk) own_m = stats[(size_t)(blk0 + tid) * R + r].x;
+
+  float m = -INFINITY, ssum = 0.f;
+  int a = 0x7fffffff;
+  for (int b0 = 0; b0 < nblk; b0 += kThreads * kFinStatsPerThread) {
+    float2 st[kFinStatsPerThread];
+    int ia[kFinStatsPerThread];
+#pragma unroll
+    for (int i = 0; i < kFinStatsPerThread; ++i) {
+      const int b = b0 + tid + i * kThreads;
+      st[i] = b < nblk ? stats[(size_t)b * R + r] : make_float2(-INFINITY, 0.f);
+      ia[i] = b < nblk ? amax[(size_t)b * R + r] : 0x7fffffff;
+    }
+    // running (max, sum) merge of this thread's blocks
+#pragma unroll
+    for (int i = 0; i < kFinStatsPerThread; ++i) {
+      if (better(m, a, st[i].x, ia[i])) a = ia[i];
+      const float nm = fmaxf(m, st[i].x);
+      if (nm != -INFINITY) {
+        ssum = ssum * exp2f((m - nm) * c) + st[i].y * exp2f((st[i].x - nm) * c);
+        m = nm;
+      }
+    }
+  }
+  // block max / first argmax
   sm[tid] = m;
   si[tid] = a;
   __syncthreads();
-  for (int s = kThreads / 2; s > 0; s >>= 1) {
-    if (tid < s && better(sm[tid], si[tid], sm[tid + s], si[tid + s])) {
-      sm[tid] = sm[tid + s];
-      si[tid] = si[tid + s];
+  for (int h = kThreads / 2; h > 0; h >>= 1) {
+    if (tid < h && better(sm[tid], si[tid], sm[tid + h], si[tid + h])) {
+      sm[tid] = sm[tid + h];
+      si[tid] = si[tid + h];
     }
     __syncthreads();
   }
   const float gmax = sm[0];
   const int garg = si[0];
   __syncthreads();
-
-  const int v0 = blockIdx.x * kFinChunk;
-  const int v1 = min(V, v0 + kFinChunk);
-  float *row = probs + (size_t)r * V;
   if (greedy) {
-    for (int v = v0 + tid; v < v1; v += kThreads) row[v] = (v == garg) ? 1.f : 0.f;
+    for (int v = v0 + tid; v < min(V, v0 + kFinChunk); v += kThreads) row[v] = (v == garg) ? 1.f : 0.f;
     return;
   }
-  float s = 0.f;
-  for (int b = tid; b < nblk; b += kThreads) {
-    const float2 st = stats[(size_t)b * R + r];
-    s += st.y * exp2f((st.x - gmax) * c);
-  }
-  sm[tid] = s;
+  // block sum, each thread's partial rescaled to the global max
+  sm[tid] = m == -INFINITY ? 0.f : ssum * exp2f((m - gmax) * c);
   __syncthreads();
   for (int h = kThreads / 2; h > 0; h >>= 1) {
     if (tid < h) sm[tid] += sm[tid + h];
     __syncthreads();
   }
   const float inv = 1.f / sm[0];
-  if ((V & 3) == 0) {
-    for (int v = v0 + tid * 4; v < v1; v += kThreads * 4) {
-      const float f = exp2f((stats[(size_t)(v / kBlockRows) * R + r].x - gmax) * c) * inv;
-      float4 x = *reinterpret_cast<float4 *>(row + v);
-      x.x *= f; x.y *= f; x.z *= f; x.w *= f;
-      *reinterpret_cast<float4 *>(row + v) = x;
+  if (tid < kFinBlocks) fac[tid] = exp2f((own_m - gmax) * c) * inv;
+  __syncthreads();
+  if (vec) {
+#pragma unroll
+    for (int i = 0; i < kFinPerThread / 4; ++i) {
+      const int v = v0 + (tid + i * kThreads) * 4;
+      if (v < V) {
+        const float f = fac[(v - v0) / kBlockRows];
+        float4 x = pv[i];
+        x.x *= f; x.y *= f; x.z *= f; x.w *= f;
+        *reinterpret_cast<float4 *>(row + v) = x;
+      }
     }
   } else {
-    for (int v = v0 + tid; v < v1; v += kThreads) {
-      const float f = exp2f((stats[(size_t)(v / kBlockRows) * R + r].x - gmax) * c) * inv;
-      row[v] *= f;
-    }
+    for (int v = v0 + tid; v < min(V, v0 + kFinChunk); v += kThreads) row[v] *= fac[(v - v0) / kBlockRows];
   }
 }
 
@@ -352,7 +601,15 @@ int launch(int NT, const void *X, const void *W, const float *temp, float *logit
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+thread_local hipEvent_t g_prof_start = nullptr, g_prof_stop = nullptr;
+
 }  // namespace
+
+extern "C" int spec_profile_lm_head(void *start_event, void *stop_event) {
+  g_prof_start = static_cast<hipEvent_t>(start_event);
+  g_prof_stop = static_cast<hipEvent_t>(stop_event);
+  return SPEC_OK;
+}
 
 extern "C" size_t spec_lm_head_workspace(int R, int H, int V) {
   if (R <= 0 || H <= 0 || V <= 0) {
@@ -386,10 +643,24 @@ extern "C" int spec_lm_head(const void *hidden, const void *weight, const float 
                                       spec::align_up(nblk * R * sizeof(float2), 256));
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int NT = min(8, spec::ceil_div(R, 16));
-  int rc = dtype == SPEC_BF16
-               ? launch<uint16_t>(NT, hidden, weight, temperature, logits, probs, stats, amax, R, H, V, st)
-               : launch<float>(NT, hidden, weight, temperature, logits, probs, stats, amax, R, H, V, st);
+  hipEvent_t ev0 = g_prof_start, ev1 = g_prof_stop;
+  g_prof_start = g_prof_stop = nullptr;
+  if (ev0 != nullptr && hipEventRecord(ev0, st) != hipSuccess)
+    return spec::fail(SPEC_EHIP, "spec_lm_head: hipEventRecord(start) failed");
+  const size_t esz = dtype == SPEC_BF16 ? 2 : 4;
+  const bool gemv = R <= kGemvMaxR && (size_t)R * H * esz <= kGemvMaxLds;
+  int rc;
+  if (gemv)
+    rc = dtype == SPEC_BF16
+             ? launch_gemv_r<uint16_t>(R, hidden, weight, temperature, logits, probs, stats, amax, H, V, st)
+             : launch_gemv_r<float>(R, hidden, weight, temperature, logits, probs, stats, amax, H, V, st);
+  else
+    rc = dtype == SPEC_BF16
+             ? launch<uint16_t>(NT, hidden, weight, temperature, logits, probs, stats, amax, R, H, V, st)
+             : launch<float>(NT, hidden, weight, temperature, logits, probs, stats, amax, R, H, V, st);
   if (rc != SPEC_OK) return rc;
+  if (ev1 != nullptr && hipEventRecord(ev1, st) != hipSuccess)
+    return spec::fail(SPEC_EHIP, "spec_lm_head: hipEventRecord(stop) failed");
   dim3 grid(spec::ceil_div(V, kFinChunk), R);
   hipLaunchKernelGGL(lm_head_finalize, grid, dim3(kThreads), 0, st, probs, stats, amax,
                      temperature, R, V, (int)nblk);
