@@ -40,6 +40,14 @@ NSETS = 64
 SAMPLE_EVERY = 16     # steps whose contraction kernel is bracketed by HIP events
 HBM_PEAK_GBS = 8000.0
 METRIC = "verified tokens/sec and verify-step HBM GB/s (% peak), batch 1, k=2, 8K ctx"
+# HBM bytes per launch of the contraction kernel from rocprofv3 FETCH_SIZE / WRITE_SIZE runs,
+# scaled by a 1 GiB copy (profiles/lm_head_gemv_b1_k2_sliding256_8k_traffic.md).  Valid only
+# for the kernel source those counters were taken on.
+PROFILED_TRAFFIC = {
+    "source": "speculative_decoding_decode_amd/csrc/lm_head.hip",
+    "sha256": "88c48b7f182af3098546a237cbb456e6817d3b2992f1170f1af99d12381984c1",
+    "bytes_per_launch": 1345677306,
+}
 
 
 class HipEvents:
@@ -72,6 +80,15 @@ class HipEvents:
     def close(self):
         for e in self.ev:
             self.hip.hipEventDestroy(e)
+
+
+def profiled_traffic():
+    """Measured HBM bytes per launch, or None if the kernel source changed since profiling."""
+    import hashlib
+    path = os.path.join(ROOT, PROFILED_TRAFFIC["source"])
+    with open(path, "rb") as f:
+        ok = hashlib.sha256(f.read()).hexdigest() == PROFILED_TRAFFIC["sha256"]
+    return PROFILED_TRAFFIC["bytes_per_launch"] if ok else None
 
 
 def log(*a):
@@ -174,6 +191,9 @@ def main():
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device copy 10 times (the reference kernel that "
+                         "scales rocprofv3 FETCH_SIZE / WRITE_SIZE counters to bytes)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the verify step "
@@ -188,6 +208,14 @@ def main():
 
     if not torch.cuda.is_available():
         raise RuntimeError("bench.py needs a GPU")
+    if args.calibrate_copy:
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")     # 1 GiB
+        dst = torch.empty_like(src)
+        for _ in range(10):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_per_dispatch": src.numel() * 4, "dispatches": 10}))
+        return
     if not os.path.exists(_lib.LIB_PATH):
         from speculative_decoding_decode_amd import build
         build.build()
@@ -281,6 +309,8 @@ def main():
     ms_per_step = wall * 1e3 / K
     lm_avg_ms = float(lm_ms.mean())
     achieved = table_bytes / (lm_avg_ms * 1e-3) / 1e9
+    traffic_bytes = profiled_traffic()
+    traffic = None if traffic_bytes is None else round(traffic_bytes / (lm_avg_ms * 1e-3) / 1e9, 1)
     step_gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
     log(f"[bench] gpu {gpu_total_ms * 1e3 / K:.1f} us/step; lm-head contraction {lm_avg_ms * 1e3:.1f} us = {achieved:.0f} GB/s; "
         f"wall {ms_per_step * 1e3:.1f} us/step; acceptance pos {stats.per_position}")
@@ -315,7 +345,8 @@ def main():
         "acceptance_per_position": [round(a, 4) for a in stats.per_position],
         "roofline": {"kernel": "lm_head_kernel (vocab-table contraction)", "bound": "hbm",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "traffic_bytes_per_launch": traffic_bytes,
                      "bytes_per_launch": table_bytes, "avg_launch_us": round(lm_avg_ms * 1e3, 2),
                      "launches_timed": int(nsamp)},
         "cpu_baseline": cpu,
