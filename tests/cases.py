@@ -80,3 +80,33 @@ def gpu_accept(draft, q, p, u, device):
                        torch.from_numpy(p).to(device), torch.from_numpy(u).to(device))
     torch.cuda.synchronize(device)
     return n.cpu().numpy(), tok.cpu().numpy()
+
+
+def explain_difference(draft, q, p_ref32, u, n_gpu, tok_gpu, n_ref, tok_ref, p_tol=1e-5):
+    """Return None if the GPU chain's accept result equals the oracle chain's, else a reason the
+    difference is a floating-point knife edge (decision margin or draw threshold within the p
+    tolerance), or raise AssertionError if it is not."""
+    from oracle.accept import sample_weights, uniform_index
+    B, k = np.asarray(draft).shape
+    V = p_ref32.shape[-1]
+    reasons = []
+    for b in range(B):
+        if n_gpu[b] == n_ref[b] and np.array_equal(tok_gpu[b], tok_ref[b]):
+            continue
+        nmin = int(min(n_gpu[b], n_ref[b]))
+        if n_gpu[b] != n_ref[b]:
+            d = int(draft[b, nmin])
+            margin = abs(float(u[b, nmin]) * float(q[b, nmin, d]) - float(p_ref32[b, nmin, d]))
+            assert margin <= p_tol, f"sequence {b}: accept decision differs with margin {margin}"
+            reasons.append(f"seq {b}: decision at position {nmin} within {margin:.2e}")
+            continue
+        w = sample_weights(p_ref32[b, nmin], q[b, nmin] if nmin < k else None)
+        W = int(w.sum())
+        t = (uniform_index(u[b, k]) * W) >> 24
+        cum = np.cumsum(w)
+        yg = int(tok_gpu[b, nmin])
+        assert 0 <= yg < V and w[yg] > 0, f"sequence {b}: drawn token {yg} has no weight"
+        gap = min(abs(int(cum[yg]) - t), abs(int(cum[yg] - w[yg]) - t)) / W
+        assert gap <= p_tol, f"sequence {b}: draw differs, threshold {gap} from the boundary"
+        reasons.append(f"seq {b}: draw threshold within {gap:.2e} of a boundary")
+    return reasons or None
