@@ -23,9 +23,10 @@
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
 constexpr int kPage = 16;
 constexpr int kRows = 32;            // query rows per workgroup
-constexpr int kTargetWGs = 4096;     // splits are sized so the grid reaches about this many
+constexpr int kTargetWGs = 2048;     // splits are sized so the grid reaches about this many
 constexpr int kMinPagesPerSplit = 1;
 constexpr int kMaxPagesPerSplit = 256;   // page ids of a split are staged in LDS
 constexpr int kMaxSplits = 4096;
@@ -48,26 +49,79 @@ __device__ __host__ inline Span seq_span(int ctx, int K1, int window, int max_pa
   return s;
 }
 
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
 template <int D, typename T>
 struct AttnShape {
   static constexpr int kEPG = 16 / (int)sizeof(T);       // elements per 16-byte group
   static constexpr int kGPR = D / kEPG;                  // 16-byte groups per row
-  static constexpr int kKStr = D + kEPG;                 // LDS row stride of K/V tiles
+  static constexpr int kStr = D + kEPG;                  // LDS row stride (elements), 16-byte pad
   static constexpr int kTileG = kPage * kGPR;            // 16-byte groups per K (or V) page tile
   static constexpr int kGPT = (kTileG + kThreads - 1) / kThreads;   // per thread
   static constexpr int kQPT = (kRows * kGPR + kThreads - 1) / kThreads;
-  static constexpr int kCPT = D >= 256 ? D / 256 : 1;    // output columns per thread
-  static constexpr int kNCol = D / kCPT;                 // threads covering one row's columns
-  static constexpr int kRG = kThreads / kNCol;           // row groups
-  static constexpr int kRPT = kRows / kRG;               // rows per thread
-  static constexpr size_t kLds = (size_t)kRows * D * 4 + 2ull * kPage * kKStr * sizeof(T) +
-                                 (size_t)kRows * kPage * 4;
+  static constexpr int kDT = D / 16;                     // 16-wide tiles of the head dim
+  static constexpr int kDTW = kDT / kWaves;              // of them per wave
+  static constexpr size_t kLds = (size_t)(kRows + 2 * kPage) * kStr * sizeof(T);
+};
+
+// MFMA helpers: QK^T per K-step, PV per page.  16x16 accumulator layout: lane l holds rows
+// (or d) 4*(l/16) + i, i = 0..3, of column l % 16.
+template <typename T> struct AttnMma;
+template <> struct AttnMma<uint16_t> {
+  static constexpr int kStepQK = 32;   // head-dim elements per QK MFMA step (16x16x32 bf16)
+  // S^T[key][row] += K[key][d0 + ...] . Q[row][d0 + ...]
+  __device__ static __forceinline__ f32x4_t qk(const uint16_t *krow, const uint16_t *qrow, int lq, f32x4_t c) {
+    const uint4 a = *reinterpret_cast<const uint4 *>(krow + lq * 8);
+    const uint4 b = *reinterpret_cast<const uint4 *>(qrow + lq * 8);
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+  }
+  // O^T[d][row] += V^T[d][keys 4*lq + i] . P^T[keys 4*lq + i][row].  P is split into a bf16
+  // head and a bf16 tail (p = hi + lo to 2^-17 relative), two MFMAs, so the products keep
+  // fp32-level accuracy while V stays exact bf16.
+  __device__ static __forceinline__ f32x4_t pv(const uint16_t *vs, int str, int dcol, int lq,
+                                               const float (&p)[4], f32x4_t c) {
+    bf16x4_t a, hi, lo;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      a[i] = __builtin_bit_cast(__bf16, vs[(4 * lq + i) * str + dcol]);
+      hi[i] = static_cast<__bf16>(p[i]);
+      lo[i] = static_cast<__bf16>(p[i] - static_cast<float>(hi[i]));
+    }
+    c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, hi, c, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, lo, c, 0, 0, 0);
+  }
+};
+template <> struct AttnMma<float> {
+  static constexpr int kStepQK = 16;   // four 16x16x4 fp32 MFMAs, one per fragment element
+  __device__ static __forceinline__ f32x4_t qk(const float *krow, const float *qrow, int lq, f32x4_t c) {
+    const float4 a = *reinterpret_cast<const float4 *>(krow + lq * 4);
+    const float4 b = *reinterpret_cast<const float4 *>(qrow + lq * 4);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.x, b.x, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.y, b.y, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.z, b.z, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.w, b.w, c, 0, 0, 0);
+    return c;
+  }
+  // MFMA j contracts the keys 4*lq + j (K slot lq), so P stays in fp32 and needs no transpose.
+  __device__ static __forceinline__ f32x4_t pv(const float *vs, int str, int dcol, int lq,
+                                               const float (&p)[4], f32x4_t c) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      c = __builtin_amdgcn_mfma_f32_16x16x4f32(vs[(4 * lq + j) * str + dcol], p[j], c, 0, 0, 0);
+    return c;
+  }
 };
 
 // Grid: (nsplit, Hkv * nrowchunk, B).
-// Memory round trips before the first page is in LDS: the split's page ids (issued first),
-// then the queries and the first page's K/V together; while a page is being scored the next
-// page's K/V are already in flight in registers.
+// Round trips before the first page is in LDS: the split's page ids, then the queries and the
+// first page's K/V together; while a page is being processed the next page's K/V are in flight
+// in registers.  Per page, every wave computes the whole 16-key x (up to 32)-row score tile
+// with MFMAs (so scores never go through LDS), runs the online softmax in registers (4 keys
+// per lane, two cross-lane shuffles for the row max and sum), and accumulates its quarter of
+// the head dim with MFMAs whose B operand is the probability tile as the score MFMA left it.
 template <int D, typename T>
 __global__ __launch_bounds__(kThreads) void attn_partial(
     const T *__restrict__ q, const T *__restrict__ kpool, const T *__restrict__ vpool,
@@ -75,16 +129,16 @@ __global__ __launch_bounds__(kThreads) void attn_partial(
     float2 *__restrict__ part_ml, float *__restrict__ part_acc, int K1, int Hq, int Hkv,
     int num_pages, int max_pages, int window, float qscale, int pps, int nsplit, int GK1) {
   using S = AttnShape<D, T>;
+  using M = AttnMma<T>;
+  constexpr int RT = kRows / 16;                                   // row tiles
   extern __shared__ __align__(16) unsigned char smem[];
-  float *qs = reinterpret_cast<float *>(smem);                     // [kRows][D]
-  T *ks = reinterpret_cast<T *>(qs + kRows * D);                   // [16][kKStr]
-  T *vs = ks + kPage * S::kKStr;                                   // [16][kKStr]
-  float *ss = reinterpret_cast<float *>(vs + kPage * S::kKStr);    // [kRows][16]
-  __shared__ float m_sh[kRows], l_sh[kRows], alpha_sh[kRows];
-  __shared__ int tq_sh[kRows];
+  T *qs = reinterpret_cast<T *>(smem);                             // [kRows][kStr]
+  T *ks = qs + kRows * S::kStr;                                    // [16][kStr]
+  T *vs = ks + kPage * S::kStr;                                    // [16][kStr]
   __shared__ int pid_sh[kMaxPagesPerSplit];
 
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & (spec::kWave - 1), wave = tid / spec::kWave;
+  const int lr = lane & 15, lq = lane >> 4;
   const int b = blockIdx.z, g = blockIdx.y % Hkv, rc = blockIdx.y / Hkv, s = blockIdx.x;
   const int G = Hq / Hkv;
   const Span sp = seq_span(ctx_lens[b], K1, window, max_pages);
@@ -95,8 +149,8 @@ __global__ __launch_bounds__(kThreads) void attn_partial(
   const int rr0 = rc * kRows;
   const int nr = min(kRows, GK1 - rr0);
 
-  // (1) page ids of the split, then the queries (registers).  Loads are unconditional with
-  // clamped indices so the wait counts the compiler inserts stay exact.
+  // (1) page ids of the split, then the queries.  Loads are unconditional with clamped
+  // indices so the wait counts the compiler inserts stay exact.
   const int pid_reg = table[(size_t)b * max_pages + pg_begin + min(tid, npg - 1)];
   uint4 qraw[S::kQPT];
 #pragma unroll
@@ -107,14 +161,9 @@ __global__ __launch_bounds__(kThreads) void attn_partial(
     qraw[x] = *reinterpret_cast<const uint4 *>(q + (((size_t)b * K1 + i) * Hq + h) * D + gi * S::kEPG);
   }
   if (tid < npg) pid_sh[tid] = (pid_reg >= 0 && pid_reg < num_pages) ? pid_reg : -1;
-  if (tid < kRows) {
-    m_sh[tid] = -INFINITY;
-    l_sh[tid] = 0.f;
-    tq_sh[tid] = tid < nr ? sp.ctx - K1 + (rr0 + tid) / G : -1;
-  }
   __syncthreads();
 
-  // (2) K/V of page 0 in flight while the queries land in LDS
+  // (2) K/V of page 0 in flight while the queries land in LDS (rows >= nr zero)
   uint4 kcur[S::kGPT], vcur[S::kGPT], knxt[S::kGPT], vnxt[S::kGPT];
   auto fetch = [&](uint4(&kr)[S::kGPT], uint4(&vr)[S::kGPT], int i) {
     const int pid = pid_sh[i];
@@ -132,20 +181,27 @@ __global__ __launch_bounds__(kThreads) void attn_partial(
 #pragma unroll
   for (int x = 0; x < S::kQPT; ++x) {
     const int e = tid + x * kThreads;
-    if (e < nr * S::kGPR) {
-      float f[S::kEPG];
-      spec::unpack16(qraw[x], f, T{});
-#pragma unroll
-      for (int y = 0; y < S::kEPG; ++y) qs[e * S::kEPG + y] = f[y] * qscale;   // row-major [r][D]
+    if (e < kRows * S::kGPR) {
+      const int r = e / S::kGPR, gi = e - r * S::kGPR;
+      *reinterpret_cast<uint4 *>(qs + r * S::kStr + gi * S::kEPG) =
+          e < nr * S::kGPR ? qraw[x] : uint4{0u, 0u, 0u, 0u};
     }
   }
 
-  float acc[S::kRPT][S::kCPT];
+  // per-lane rows: rt * 16 + lr; their query positions and running (max, sum)
+  int trow[RT];
+  float m_run[RT], l_run[RT];
+  f32x4_t o[RT][S::kDTW];
 #pragma unroll
-  for (int ri = 0; ri < S::kRPT; ++ri)
+  for (int rt = 0; rt < RT; ++rt) {
+    const int r = rt * 16 + lr;
+    trow[rt] = r < nr ? sp.ctx - K1 + (rr0 + r) / G : -1;
+    m_run[rt] = -INFINITY;
+    l_run[rt] = 0.f;
 #pragma unroll
-    for (int c = 0; c < S::kCPT; ++c) acc[ri][c] = 0.f;
-  const int rg = tid / S::kNCol, col0 = tid - rg * S::kNCol;
+    for (int dt = 0; dt < S::kDTW; ++dt) o[rt][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  const bool two_tiles = nr > 16;   // uniform
 
   for (int i = 0; i < npg; ++i) {
 #pragma unroll
@@ -153,8 +209,8 @@ __global__ __launch_bounds__(kThreads) void attn_partial(
       const int e = tid + x * kThreads;
       if (e < S::kTileG) {
         const int row = e / S::kGPR, gi = e - row * S::kGPR;
-        *reinterpret_cast<uint4 *>(ks + row * S::kKStr + gi * S::kEPG) = kcur[x];
-        *reinterpret_cast<uint4 *>(vs + row * S::kKStr + gi * S::kEPG) = vcur[x];
+        *reinterpret_cast<uint4 *>(ks + row * S::kStr + gi * S::kEPG) = kcur[x];
+        *reinterpret_cast<uint4 *>(vs + row * S::kStr + gi * S::kEPG) = vcur[x];
       }
     }
     if (i + 1 < npg) fetch(knxt, vnxt, i + 1);
@@ -162,74 +218,42 @@ __global__ __launch_bounds__(kThreads) void attn_partial(
     const int pg = pg_begin + i;
     __syncthreads();
 
-    // scores and online-softmax state: 16 consecutive lanes = one query row x 16 keys
-    for (int base = 0; base < nr * kPage; base += kThreads) {
-      const int idx = base + tid, rr = idx >> 4, j = idx & 15;
-      const bool rowok = rr < nr;
-      float sc = -INFINITY;
-      if (rowok && page_ok) {
-        const int pos = pg * kPage + j, t = tq_sh[rr];
-        if (pos <= t && (window == 0 || t - pos < window)) {
-          const T *kr = ks + j * S::kKStr;
-          const float *qr = qs + rr * D;
-          float dot = 0.f;
-#pragma unroll 4
-          for (int d0 = 0; d0 < D; d0 += S::kEPG) {
-            float kf[S::kEPG];
-            spec::unpack16(*reinterpret_cast<const uint4 *>(kr + d0), kf, T{});
+    if (page_ok) {
 #pragma unroll
-            for (int x = 0; x < S::kEPG; ++x) dot = fmaf(qr[d0 + x], kf[x], dot);
-          }
-          sc = dot;
+      for (int rt = 0; rt < RT; ++rt) {
+        if (rt == 1 && !two_tiles) break;
+        // scores S^T[key 4*lq + e][row rt*16 + lr]
+        f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int d0 = 0; d0 < D; d0 += M::kStepQK)
+          sc = M::qk(ks + lr * S::kStr + d0, qs + (rt * 16 + lr) * S::kStr + d0, lq, sc);
+        float sv[4];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int pos = pg * kPage + 4 * lq + e, t = trow[rt];
+          const bool vis = pos <= t && (window == 0 || t - pos < window);
+          sv[e] = vis ? sc[e] * qscale : -INFINITY;
+          mx = fmaxf(mx, sv[e]);
         }
-      }
-      float mx = sc;
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_new = fmaxf(m_run[rt], mx);
+        float pr[4], sum = 0.f;
 #pragma unroll
-      for (int off = 8; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 16));
-      const float m_old = rowok ? m_sh[rr] : -INFINITY;
-      const float m_new = fmaxf(m_old, mx);
-      const float pj = sc == -INFINITY ? 0.f : exp2f(sc - m_new);
-      float sum = pj;
-#pragma unroll
-      for (int off = 8; off > 0; off >>= 1) sum += __shfl_xor(sum, off, 16);
-      if (rowok) {
-        ss[rr * kPage + j] = pj;
-        if (j == 0) {
-          const float alpha = m_old == -INFINITY ? 0.f : exp2f(m_old - m_new);
-          l_sh[rr] = l_sh[rr] * alpha + sum;
-          m_sh[rr] = m_new;
-          alpha_sh[rr] = alpha;
+        for (int e = 0; e < 4; ++e) {
+          pr[e] = sv[e] == -INFINITY ? 0.f : exp2f(sv[e] - m_new);
+          sum += pr[e];
         }
-      }
-    }
-    __syncthreads();
-
-    // value update: acc[row][col] = alpha * acc + sum_j p_j v_j[col]; the 16 values of this
-    // thread's columns are read once and reused for every row
-    float vv[kPage][S::kCPT];
+        sum += __shfl_xor(sum, 16);
+        sum += __shfl_xor(sum, 32);
+        const float alpha = m_run[rt] == -INFINITY ? 0.f : exp2f(m_run[rt] - m_new);
+        l_run[rt] = l_run[rt] * alpha + sum;
+        m_run[rt] = m_new;
 #pragma unroll
-    for (int j = 0; j < kPage; ++j)
-#pragma unroll
-      for (int c = 0; c < S::kCPT; ++c)
-        vv[j][c] = spec::Elem<T>::to_f32(vs[j * S::kKStr + col0 + c * S::kNCol]);
-#pragma unroll
-    for (int ri = 0; ri < S::kRPT; ++ri) {
-      const int rr = rg + ri * S::kRG;
-      if (rr < nr) {
-        const float a = alpha_sh[rr];
-        const float4 *pr4 = reinterpret_cast<const float4 *>(ss + rr * kPage);
-        float pj[kPage];
-#pragma unroll
-        for (int j4 = 0; j4 < kPage / 4; ++j4) {
-          const float4 t = pr4[j4];
-          pj[4 * j4] = t.x; pj[4 * j4 + 1] = t.y; pj[4 * j4 + 2] = t.z; pj[4 * j4 + 3] = t.w;
-        }
-#pragma unroll
-        for (int c = 0; c < S::kCPT; ++c) {
-          float o = acc[ri][c] * a;
-#pragma unroll
-          for (int j = 0; j < kPage; ++j) o = fmaf(pj[j], vv[j][c], o);
-          acc[ri][c] = o;
+        for (int dt = 0; dt < S::kDTW; ++dt) {
+          o[rt][dt] *= alpha;
+          o[rt][dt] = M::pv(vs, S::kStr, (wave * S::kDTW + dt) * 16 + lr, lq, pr, o[rt][dt]);
         }
       }
     }
@@ -238,15 +262,19 @@ __global__ __launch_bounds__(kThreads) void attn_partial(
     for (int x = 0; x < S::kGPT; ++x) { kcur[x] = knxt[x]; vcur[x] = vnxt[x]; }
   }
 
+  // partial outputs: lane holds O^T[d = dtile*16 + 4*lq + e][row rt*16 + lr]
   const size_t base = ((size_t)(b * Hkv + g) * nsplit + s) * GK1 + rr0;
-  if (tid < nr) part_ml[base + tid] = make_float2(m_sh[tid], l_sh[tid]);
 #pragma unroll
-  for (int ri = 0; ri < S::kRPT; ++ri) {
-    const int rr = rg + ri * S::kRG;
-    if (rr < nr) {
+  for (int rt = 0; rt < RT; ++rt) {
+    const int r = rt * 16 + lr;
+    if (r < nr) {
+      if (wave == 0 && lq == 0) part_ml[base + r] = make_float2(m_run[rt], l_run[rt]);
 #pragma unroll
-      for (int c = 0; c < S::kCPT; ++c)
-        part_acc[(base + rr) * D + col0 + c * S::kNCol] = acc[ri][c];
+      for (int dt = 0; dt < S::kDTW; ++dt) {
+        const int d = (wave * S::kDTW + dt) * 16 + 4 * lq;
+        *reinterpret_cast<float4 *>(part_acc + (base + r) * D + d) =
+            make_float4(o[rt][dt][0], o[rt][dt][1], o[rt][dt][2], o[rt][dt][3]);
+      }
     }
   }
 }
@@ -360,7 +388,10 @@ AttnPlan plan(int B, int K1, int Hq, int Hkv, int D, int max_pages, int window) 
   span = max(span, 1);
   const long units = (long)B * Hkv * pl.nrowchunk;
   const int wanted = (int)max(1L, (kTargetWGs + units - 1) / units);
-  pl.pps = max(kMinPagesPerSplit, spec::ceil_div(span, wanted));
+  // When there is more work than the target grid, splits hold at least GK1 / 2 pages so the
+  // partial outputs (GK1 x D fp32 per split) stay within 1/8 of the KV bytes they summarise.
+  const int pmin = (long)span * units > kTargetWGs ? max(1, spec::ceil_div(pl.GK1, 2)) : 1;
+  pl.pps = max(max(kMinPagesPerSplit, pmin), spec::ceil_div(span, wanted));
   pl.pps = min(max(pl.pps, spec::ceil_div(span, kMaxSplits)), kMaxPagesPerSplit);
   pl.nsplit = spec::ceil_div(span, pl.pps);
   const size_t rows = (size_t)B * Hkv * pl.nsplit * pl.GK1;

@@ -35,10 +35,8 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;          // 4
-constexpr int kMT = 4;                            // 16-row vocab tiles per wave
-constexpr int kBlockRows = kWaves * kMT * 16;     // 256 vocab rows per workgroup
+constexpr int kBlockRows = 256;                   // vocab rows per statistics block
 constexpr int kDepth = 4;                         // K-steps per load batch
-constexpr int kXBudget = 40 * 1024;               // LDS bytes for a staged hidden-row chunk
 constexpr int kFinChunk = 4096;                   // vocab entries per finalize workgroup
 constexpr size_t kGemvMaxLds = 128 * 1024;        // hidden rows resident in LDS (GEMV path)
 constexpr float kLog2e = 1.4426950408889634f;
@@ -68,170 +66,178 @@ __device__ __forceinline__ bool better(float m, int a, float om, int oa) {
   return om > m || (om == m && oa < a);
 }
 
-// Contraction + per-block statistics.  Grid: (ceil(V / 256), ceil(R / (16 NT))).
-// MFMA operand roles: A = 16 vocab rows x K of the table, B = K x 16 hidden rows, so the
-// accumulator lane l holds logits of vocab rows 4*(l/16) + e (e = 0..3) for hidden row l % 16.
+// Contraction + per-block statistics for R > 8 rows.  Grid: (ceil(V / 256), ceil(R / (16 NT))),
+// 1024 threads: 16 waves, each owning one 16-row vocab tile of the 256-row block and all NT
+// tiles of 16 hidden rows.  MFMA operand roles: A = 16 vocab rows x K of the table (straight
+// from HBM into registers, one batch of kDepth K-steps ahead), B = K x 16 hidden rows from an
+// LDS chunk of kChunkSteps K-steps; chunks are double-buffered and the next chunk's global
+// loads are issued a whole chunk ahead, so neither the table stream nor the chunk staging ever
+// drains the other.  Accumulator lane l holds logits of vocab rows 4*(l/16) + e (e = 0..3) of
+// the wave's tile for hidden row n*16 + l % 16.
+constexpr int kMmaThreads = 1024;
+constexpr int kMmaWaves = kMmaThreads / kWave;     // 16
+constexpr int kChunkSteps = 2 * kDepth;           // K-steps per staged hidden-row chunk
+constexpr int kMaxNT = 6;                         // hidden-row tiles per pass
+
 template <typename T, int NT>
-__global__ __launch_bounds__(kThreads) void lm_head_kernel(
+__global__ __launch_bounds__(kMmaThreads) void lm_head_mfma(
     const T *__restrict__ X, const T *__restrict__ W, const float *__restrict__ temp,
     float *__restrict__ logits, float *__restrict__ probs, float2 *__restrict__ stats,
-    int *__restrict__ amax, int R, int H, int V, int kcs) {
+    int *__restrict__ amax, int R, int H, int V) {
   using M = Mma<T>;
+  constexpr int KC = kChunkSteps * M::kStep;             // elements per chunk
+  constexpr int XSTR = KC + M::kEPL;                     // LDS row stride, 16-byte pad
+  constexpr int GPRC = KC / M::kEPL;                     // 16-byte groups per row per chunk
+  constexpr int XPT = (NT * 16 * GPRC + kMmaThreads - 1) / kMmaThreads;
   extern __shared__ __align__(16) unsigned char smem[];
-  T *xs = reinterpret_cast<T *>(smem);
-  __shared__ float red_m[kWaves][NT * 16];
-  __shared__ float red_s[kWaves][NT * 16];
-  __shared__ int red_i[kWaves][NT * 16];
+  T *xs = reinterpret_cast<T *>(smem);                   // [2][NT*16][XSTR]
 
-  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const int lr = lane & 15, lq = lane >> 4;
   const int blk = blockIdx.x;
   const int r0 = blockIdx.y * NT * 16;
   const int nrows = min(NT * 16, R - r0);
-  const int vrow0 = blk * kBlockRows + wave * kMT * 16;
-  const int xstride = kcs * M::kStep + M::kEPL;   // LDS row stride (elements), 16-byte pad
-
-  const T *wrow[kMT];
-#pragma unroll
-  for (int t = 0; t < kMT; ++t) {
-    const int v = min(vrow0 + t * 16 + lr, V - 1);    // tail rows are read but discarded
-    wrow[t] = W + (size_t)v * H + lq * M::kEPL;
-  }
-
-  f32x4_t acc[kMT][NT];
-#pragma unroll
-  for (int t = 0; t < kMT; ++t)
-#pragma unroll
-    for (int n = 0; n < NT; ++n) acc[t][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
+  const int vrow0 = blk * kBlockRows + wave * 16;
+  const T *wrow = W + (size_t)min(vrow0 + lr, V - 1) * H + lq * M::kEPL;   // tail rows discarded
   const int nks = (H + M::kStep - 1) / M::kStep;
-  for (int c0 = 0; c0 < nks; c0 += kcs) {
-    const int cn = min(kcs, nks - c0);
-    const int cn_pad = (cn + kDepth - 1) / kDepth * kDepth;
-    __syncthreads();
-    {  // stage hidden rows [r0, r0 + nrows) x K-steps [c0, c0 + cn_pad) into LDS
-      const int groups = cn_pad * M::kStep / M::kEPL;
-      for (int e = threadIdx.x; e < nrows * groups; e += kThreads) {
-        const int r = e / groups, g = e - r * groups;
-        const int k = c0 * M::kStep + g * M::kEPL;
-        uint4 val = {0u, 0u, 0u, 0u};
-        if (k < H) val = *reinterpret_cast<const uint4 *>(X + (size_t)(r0 + r) * H + k);
-        *reinterpret_cast<uint4 *>(xs + r * xstride + g * M::kEPL) = val;
+  const int nchunks = (nks + kChunkSteps - 1) / kChunkSteps;
+
+  uint4 xr[XPT];
+  auto xload = [&](int c) {
+#pragma unroll
+    for (int x = 0; x < XPT; ++x) {
+      const int e = tid + x * kMmaThreads;
+      const int r = e / GPRC, g = e - r * GPRC;
+      const int k = c * KC + g * M::kEPL;
+      xr[x] = (r < nrows && k < H) ? *reinterpret_cast<const uint4 *>(X + (size_t)(r0 + r) * H + k)
+                                   : uint4{0u, 0u, 0u, 0u};
+    }
+  };
+  auto xstore = [&](int buf) {
+#pragma unroll
+    for (int x = 0; x < XPT; ++x) {
+      const int e = tid + x * kMmaThreads;
+      const int r = e / GPRC, g = e - r * GPRC;
+      if (r < NT * 16) *reinterpret_cast<uint4 *>(xs + (buf * NT * 16 + r) * XSTR + g * M::kEPL) = xr[x];
+    }
+  };
+  auto wload = [&](uint4(&a)[kDepth], int batch) {      // global batch index
+#pragma unroll
+    for (int d = 0; d < kDepth; ++d) {
+      const int ks = batch * kDepth + d;
+      const bool ok = ks < nks && ks * M::kStep + lq * M::kEPL < H;
+      a[d] = ok ? *reinterpret_cast<const uint4 *>(wrow + (size_t)ks * M::kStep) : uint4{0u, 0u, 0u, 0u};
+    }
+  };
+  f32x4_t acc[NT];
+#pragma unroll
+  for (int n = 0; n < NT; ++n) acc[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](const uint4(&a)[kDepth], int buf, int step0) {   // step0: local K-step
+#pragma unroll
+    for (int d = 0; d < kDepth; ++d) {
+      const int kl = (step0 + d) * M::kStep + lq * M::kEPL;
+#pragma unroll
+      for (int n = 0; n < NT; ++n) {
+        const int r = n * 16 + lr;
+        uint4 bv = {0u, 0u, 0u, 0u};
+        if (r < nrows) bv = *reinterpret_cast<const uint4 *>(xs + (buf * NT * 16 + r) * XSTR + kl);
+        acc[n] = M::run(a[d], bv, acc[n]);
       }
     }
-    __syncthreads();
+  };
 
-    uint4 a0[kDepth][kMT], a1[kDepth][kMT];
-    auto load = [&](uint4(&a)[kDepth][kMT], int batch) {
-#pragma unroll
-      for (int d = 0; d < kDepth; ++d) {
-        const int ks = c0 + batch * kDepth + d;
-        const bool ok = ks < nks && ks * M::kStep + lq * M::kEPL < H;
-#pragma unroll
-        for (int t = 0; t < kMT; ++t)
-          a[d][t] = ok ? *reinterpret_cast<const uint4 *>(wrow[t] + (size_t)ks * M::kStep)
-                       : uint4{0u, 0u, 0u, 0u};
-      }
-    };
-    auto compute = [&](const uint4(&a)[kDepth][kMT], int batch) {
-#pragma unroll
-      for (int d = 0; d < kDepth; ++d) {
-        const int kl = (batch * kDepth + d) * M::kStep + lq * M::kEPL;
-#pragma unroll
-        for (int n = 0; n < NT; ++n) {
-          const int r = n * 16 + lr;
-          uint4 b = {0u, 0u, 0u, 0u};
-          if (r < nrows) b = *reinterpret_cast<const uint4 *>(xs + r * xstride + kl);
-#pragma unroll
-          for (int t = 0; t < kMT; ++t) acc[t][n] = M::run(a[d][t], b, acc[t][n]);
-        }
-      }
-    };
-    const int nb = cn_pad / kDepth;
-    load(a0, 0);
-    for (int bi = 0; bi < nb; bi += 2) {
-      if (bi + 1 < nb) load(a1, bi + 1);
-      compute(a0, bi);
-      if (bi + 1 < nb) {
-        if (bi + 2 < nb) load(a0, bi + 2);
-        compute(a1, bi + 1);
-      }
+  xload(0);
+  xstore(0);
+  __syncthreads();
+  if (nchunks > 1) xload(1);
+  uint4 a0[kDepth], a1[kDepth];
+  wload(a0, 0);
+  for (int c = 0; c < nchunks; ++c) {
+    const int buf = c & 1;
+    wload(a1, 2 * c + 1);
+    compute(a0, buf, 0);
+    if (c + 1 < nchunks) wload(a0, 2 * c + 2);
+    compute(a1, buf, kDepth);
+    if (c + 1 < nchunks) {
+      xstore(buf ^ 1);
+      __syncthreads();
+      if (c + 2 < nchunks) xload(c + 2);
     }
   }
 
-  // ---- epilogue: block max and first argmax per hidden row
+  // ---- epilogue: block max / first argmax, then sum of exp, per hidden row (LDS reuses xs)
+  __syncthreads();
+  float *red_m = reinterpret_cast<float *>(smem);               // [16 waves][NT*16]
+  float *red_s = red_m + kMmaWaves * NT * 16;
+  int *red_i = reinterpret_cast<int *>(red_s + kMmaWaves * NT * 16);
 #pragma unroll
   for (int n = 0; n < NT; ++n) {
     float mx = -INFINITY;
     int ax = 0x7fffffff;
 #pragma unroll
-    for (int t = 0; t < kMT; ++t)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int v = vrow0 + t * 16 + lq * 4 + e;
-        const float z = acc[t][n][e];
-        if (v < V && z > mx) { mx = z; ax = v; }
-      }
+    for (int e = 0; e < 4; ++e) {
+      const int v = vrow0 + lq * 4 + e;
+      const float z = acc[n][e];
+      if (v < V && z > mx) { mx = z; ax = v; }
+    }
 #pragma unroll
     for (int off = 16; off < kWave; off <<= 1) {
       const float om = __shfl_xor(mx, off);
       const int oa = __shfl_xor(ax, off);
       if (better(mx, ax, om, oa)) { mx = om; ax = oa; }
     }
-    if (lq == 0) { red_m[wave][n * 16 + lr] = mx; red_i[wave][n * 16 + lr] = ax; }
+    if (lq == 0) { red_m[wave * NT * 16 + n * 16 + lr] = mx; red_i[wave * NT * 16 + n * 16 + lr] = ax; }
   }
   __syncthreads();
-
-  float bmax[NT], cexp[NT];
+  float cexp[NT];
   bool live[NT];
 #pragma unroll
   for (int n = 0; n < NT; ++n) {
     const int c = n * 16 + lr;
-    float m = red_m[0][c];
-    for (int w = 1; w < kWaves; ++w) m = fmaxf(m, red_m[w][c]);
-    bmax[n] = m;
+    float m = red_m[c];
+    for (int w = 1; w < kMmaWaves; ++w) m = fmaxf(m, red_m[w * NT * 16 + c]);
     const int r = r0 + c;
     live[n] = r < R;
     const float tr = live[n] ? temp[r] : 1.f;
     cexp[n] = tr > 0.f ? kLog2e / tr : 0.f;   // 0: greedy row, p is written by the finalize
-    float s = 0.f;
-#pragma unroll
-    for (int t = 0; t < kMT; ++t) {
-      const int v0 = vrow0 + t * 16 + lq * 4;
-      if (live[n] && logits != nullptr) {
-        float *dst = logits + (size_t)r * V + v0;
-        if (v0 + 3 < V && (V & 3) == 0) {
-          *reinterpret_cast<float4 *>(dst) =
-              make_float4(acc[t][n][0], acc[t][n][1], acc[t][n][2], acc[t][n][3]);
-        } else {
-          for (int e = 0; e < 4; ++e)
-            if (v0 + e < V) dst[e] = acc[t][n][e];
-        }
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float ex = (v0 + e < V) ? exp2f((acc[t][n][e] - m) * cexp[n]) : 0.f;
-        acc[t][n][e] = ex;
-        s += ex;
+    const int v0 = vrow0 + lq * 4;
+    if (live[n] && logits != nullptr) {
+      float *dst = logits + (size_t)r * V + v0;
+      if (v0 + 3 < V && (V & 3) == 0) {
+        *reinterpret_cast<float4 *>(dst) = make_float4(acc[n][0], acc[n][1], acc[n][2], acc[n][3]);
+      } else {
+        for (int e = 0; e < 4; ++e)
+          if (v0 + e < V) dst[e] = acc[n][e];
       }
     }
+    float sacc = 0.f;
 #pragma unroll
-    for (int off = 16; off < kWave; off <<= 1) s += __shfl_xor(s, off);
-    if (lq == 0) red_s[wave][c] = s;
+    for (int e = 0; e < 4; ++e) {
+      const float ex = (v0 + e < V) ? exp2f((acc[n][e] - m) * cexp[n]) : 0.f;
+      acc[n][e] = ex;
+      sacc += ex;
+    }
+#pragma unroll
+    for (int off = 16; off < kWave; off <<= 1) sacc += __shfl_xor(sacc, off);
+    if (lq == 0) red_s[wave * NT * 16 + c] = sacc;
   }
   __syncthreads();
-
   if (wave == 0 && lq == 0) {
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
       const int c = n * 16 + lr, r = r0 + c;
       if (r >= R) continue;
-      float m = red_m[0][c];
-      int a = red_i[0][c];
-      for (int w = 1; w < kWaves; ++w)
-        if (better(m, a, red_m[w][c], red_i[w][c])) { m = red_m[w][c]; a = red_i[w][c]; }
-      const float s = ((red_s[0][c] + red_s[1][c]) + red_s[2][c]) + red_s[3][c];
-      stats[(size_t)blk * R + r] = make_float2(m, s);
+      float m = red_m[c];
+      int a = red_i[c];
+      float sum = red_s[c];
+      for (int w = 1; w < kMmaWaves; ++w) {
+        if (better(m, a, red_m[w * NT * 16 + c], red_i[w * NT * 16 + c])) {
+          m = red_m[w * NT * 16 + c];
+          a = red_i[w * NT * 16 + c];
+        }
+        sum += red_s[w * NT * 16 + c];
+      }
+      stats[(size_t)blk * R + r] = make_float2(m, sum);
       amax[(size_t)blk * R + r] = a;
     }
   }
@@ -239,21 +245,16 @@ __global__ __launch_bounds__(kThreads) void lm_head_kernel(
   for (int n = 0; n < NT; ++n) {
     const int r = r0 + n * 16 + lr;
     if (!live[n] || cexp[n] == 0.f) continue;
-#pragma unroll
-    for (int t = 0; t < kMT; ++t) {
-      const int v0 = vrow0 + t * 16 + lq * 4;
-      float *dst = probs + (size_t)r * V + v0;
-      if (v0 + 3 < V && (V & 3) == 0) {
-        *reinterpret_cast<float4 *>(dst) =
-            make_float4(acc[t][n][0], acc[t][n][1], acc[t][n][2], acc[t][n][3]);
-      } else {
-        for (int e = 0; e < 4; ++e)
-          if (v0 + e < V) dst[e] = acc[t][n][e];
-      }
+    const int v0 = vrow0 + lq * 4;
+    float *dst = probs + (size_t)r * V + v0;
+    if (v0 + 3 < V && (V & 3) == 0) {
+      *reinterpret_cast<float4 *>(dst) = make_float4(acc[n][0], acc[n][1], acc[n][2], acc[n][3]);
+    } else {
+      for (int e = 0; e < 4; ++e)
+        if (v0 + e < V) dst[e] = acc[n][e];
     }
   }
 }
-
 
 // ------------------------------------------------------------------------- small-R GEMV path
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -569,19 +570,23 @@ template <typename T, int NT>
 int launch_nt(const void *X, const void *W, const float *temp, float *logits, float *probs,
               float2 *stats, int *amax, int R, int H, int V, hipStream_t st) {
   using M = Mma<T>;
-  const int nks = (H + M::kStep - 1) / M::kStep;
-  const int rows = min(NT * 16, R);
-  const int esz = (int)sizeof(T);
-  int kcs = (kXBudget / (rows * esz) - M::kEPL) / M::kStep;
-  kcs = max(kDepth, kcs / kDepth * kDepth);
-  kcs = min(kcs, (nks + kDepth - 1) / kDepth * kDepth);
-  const size_t lds = (size_t)rows * (kcs * M::kStep + M::kEPL) * esz;
+  constexpr int KC = kChunkSteps * M::kStep;
+  const size_t xs_bytes = 2ull * NT * 16 * (KC + M::kEPL) * sizeof(T);
+  const size_t red_bytes = 3ull * kMmaWaves * NT * 16 * 4;
+  const size_t lds = xs_bytes > red_bytes ? xs_bytes : red_bytes;
+  static bool attr_set = false;
+  if (!attr_set && lds > 64 * 1024) {
+    if (hipFuncSetAttribute(reinterpret_cast<const void *>(&lm_head_mfma<T, NT>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+      return spec::fail(SPEC_EHIP, "spec_lm_head: cannot reserve %zu bytes of LDS", lds);
+    attr_set = true;
+  }
   const int nblk = spec::ceil_div(V, kBlockRows);
   dim3 grid(nblk, spec::ceil_div(R, NT * 16));
-  hipLaunchKernelGGL((lm_head_kernel<T, NT>), grid, dim3(kThreads), lds, st,
+  hipLaunchKernelGGL((lm_head_mfma<T, NT>), grid, dim3(kMmaThreads), lds, st,
                      static_cast<const T *>(X), static_cast<const T *>(W), temp, logits, probs,
-                     stats, amax, R, H, V, kcs);
-  return spec::launched("lm_head_kernel");
+                     stats, amax, R, H, V);
+  return spec::launched("lm_head_mfma");
 }
 
 template <typename T>
@@ -593,9 +598,7 @@ int launch(int NT, const void *X, const void *W, const float *temp, float *logit
     case 3: return launch_nt<T, 3>(X, W, temp, logits, probs, stats, amax, R, H, V, st);
     case 4: return launch_nt<T, 4>(X, W, temp, logits, probs, stats, amax, R, H, V, st);
     case 5: return launch_nt<T, 5>(X, W, temp, logits, probs, stats, amax, R, H, V, st);
-    case 6: return launch_nt<T, 6>(X, W, temp, logits, probs, stats, amax, R, H, V, st);
-    case 7: return launch_nt<T, 7>(X, W, temp, logits, probs, stats, amax, R, H, V, st);
-    default: return launch_nt<T, 8>(X, W, temp, logits, probs, stats, amax, R, H, V, st);
+    default: return launch_nt<T, 6>(X, W, temp, logits, probs, stats, amax, R, H, V, st);
   }
 }
 
@@ -642,7 +645,9 @@ extern "C" int spec_lm_head(const void *hidden, const void *weight, const float 
   int *amax = reinterpret_cast<int *>(static_cast<char *>(workspace) +
                                       spec::align_up(nblk * R * sizeof(float2), 256));
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const int NT = min(8, spec::ceil_div(R, 16));
+  // MFMA path: up to 6 tiles of 16 hidden rows per pass over the table (128 VGPRs per lane at
+  // 1024 threads); more rows take further passes.
+  const int NT = min(kMaxNT, spec::ceil_div(R, 16));
   hipEvent_t ev0 = g_prof_start, ev1 = g_prof_stop;
   g_prof_start = g_prof_stop = nullptr;
   if (ev0 != nullptr && hipEventRecord(ev0, st) != hipSuccess)
