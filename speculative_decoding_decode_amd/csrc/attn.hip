@@ -26,7 +26,8 @@ constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kPage = 16;
 constexpr int kRows = 32;            // query rows per workgroup
-constexpr int kTargetWGs = 2048;     // splits are sized so the grid reaches about this many
+constexpr int kTargetWGs = 4096;     // splits are sized so the grid reaches about this many
+constexpr long kSmallWork = 2048;    // page-heads below which splits may be a single page
 constexpr int kMinPagesPerSplit = 1;
 constexpr int kMaxPagesPerSplit = 256;   // page ids of a split are staged in LDS
 constexpr int kMaxSplits = 4096;
@@ -115,7 +116,7 @@ template <> struct AttnMma<float> {
   }
 };
 
-// Grid: (nsplit, Hkv * nrowchunk, B).
+// Grid: (B * Hkv * nrowchunk, nsplit).
 // Round trips before the first page is in LDS: the split's page ids, then the queries and the
 // first page's K/V together; while a page is being processed the next page's K/V are in flight
 // in registers.  Per page, every wave computes the whole 16-key x (up to 32)-row score tile
@@ -139,7 +140,12 @@ __global__ __launch_bounds__(kThreads) void attn_partial(
 
   const int tid = threadIdx.x, lane = tid & (spec::kWave - 1), wave = tid / spec::kWave;
   const int lr = lane & 15, lq = lane >> 4;
-  const int b = blockIdx.z, g = blockIdx.y % Hkv, rc = blockIdx.y / Hkv, s = blockIdx.x;
+  // blockIdx.x enumerates (sequence, KV head, row chunk) units and blockIdx.y the splits in
+  // reverse: the highest splits, which only the longest sequences have, are dispatched first,
+  // so ragged batches run longest-first instead of ending on a few long workgroups.
+  const int nrc = (GK1 + kRows - 1) / kRows;
+  const int unit = blockIdx.x, s = nsplit - 1 - (int)blockIdx.y;
+  const int b = unit / (Hkv * nrc), g = (unit / nrc) % Hkv, rc = unit % nrc;
   const int G = Hq / Hkv;
   const Span sp = seq_span(ctx_lens[b], K1, window, max_pages);
   const int ns = (sp.np + pps - 1) / pps;
@@ -388,9 +394,10 @@ AttnPlan plan(int B, int K1, int Hq, int Hkv, int D, int max_pages, int window) 
   span = max(span, 1);
   const long units = (long)B * Hkv * pl.nrowchunk;
   const int wanted = (int)max(1L, (kTargetWGs + units - 1) / units);
-  // When there is more work than the target grid, splits hold at least GK1 / 2 pages so the
-  // partial outputs (GK1 x D fp32 per split) stay within 1/8 of the KV bytes they summarise.
-  const int pmin = (long)span * units > kTargetWGs ? max(1, spec::ceil_div(pl.GK1, 2)) : 1;
+  // Beyond a small amount of work, splits hold at least GK1 / 2 pages so the partial outputs
+  // (GK1 x D fp32 per split) stay within 1/8 of the KV bytes they summarise; below it, latency
+  // rules and splits may be single pages.
+  const int pmin = (long)span * units > kSmallWork ? max(1, spec::ceil_div(pl.GK1, 2)) : 1;
   pl.pps = max(max(kMinPagesPerSplit, pmin), spec::ceil_div(span, wanted));
   pl.pps = min(max(pl.pps, spec::ceil_div(span, kMaxSplits)), kMaxPagesPerSplit);
   pl.nsplit = spec::ceil_div(span, pl.pps);
@@ -416,7 +423,7 @@ int launch(const void *q, const void *kp, const void *vp, const int32_t *table,
   }
   float2 *ml = reinterpret_cast<float2 *>(ws + pl.off_ml);
   float *acc = reinterpret_cast<float *>(ws + pl.off_acc);
-  dim3 grid(pl.nsplit, Hkv * pl.nrowchunk, B);
+  dim3 grid(B * Hkv * pl.nrowchunk, pl.nsplit);
   hipLaunchKernelGGL((attn_partial<D, T>), grid, dim3(kThreads), S::kLds, st,
                      static_cast<const T *>(q), static_cast<const T *>(kp),
                      static_cast<const T *>(vp), table, ctx, ml, acc, K1, Hq, Hkv, num_pages,
