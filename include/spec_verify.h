@@ -149,6 +149,31 @@ int spec_accept(const int32_t *draft, const float *q, const float *p, const floa
                 int32_t *n_accepted, int32_t *tokens, int B, int k, int V,
                 void *workspace, size_t workspace_bytes, void *stream);
 
+/* ------------------------------------------------------------------------------------------
+ * KV-cache bookkeeping around the verify step.  Drafts from the first rejected one on are
+ * discarded and the target generates the token there (butteryoon "Gemma 4 MTP 서빙 가이드
+ * 해설", section 4 accept/reject step; llm-wiki "Gemma 4 MTP ...", section "투기적 디코딩의
+ * 기본 구조").  The verify forward's K1 input positions are the last committed token and the k
+ * drafts; their K/V go into the cache before spec_verify_attn reads it:
+ *
+ *   spec_kv_append  writes k_new / v_new [B, K1, Hkv, D] (dtype) to positions
+ *                   ctx_lens[b] - K1 + i of each sequence's pages (ctx_lens already counts
+ *                   them, as in spec_verify_attn).  Positions outside the page table or on a
+ *                   page id outside [0, num_pages) are skipped.  D * element size must be a
+ *                   multiple of 16 bytes.
+ *   spec_kv_commit  after spec_accept: ctx_lens[b] -= K1 - 1 - n_accepted[b] (n clamped to
+ *                   [0, K1 - 1]), keeping the last committed token and the n accepted drafts;
+ *                   the rejected slots are overwritten by the next append, and the correction
+ *                   or bonus token's K/V arrive with the next step.
+ * Both are asynchronous on `stream` and allocate nothing.
+ * ---------------------------------------------------------------------------------------- */
+int spec_kv_append(const void *k_new, const void *v_new, void *k_pool, void *v_pool,
+                   const int32_t *page_table, const int32_t *ctx_lens, int B, int K1, int Hkv,
+                   int D, int page_size, int num_pages, int max_pages_per_seq, spec_dtype dtype,
+                   void *stream);
+
+int spec_kv_commit(int32_t *ctx_lens, const int32_t *n_accepted, int B, int K1, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -190,5 +190,38 @@ def accept(draft, q, p, uniforms, n_accepted=None, tokens=None, workspace=None, 
     return n_accepted, tokens
 
 
+def kv_append(k_new, v_new, k_pool, v_pool, page_table, ctx_lens, stream=None):
+    """Write the K/V of the K1 verified positions, [B, K1, Hkv, D], into their cache pages
+    (positions ctx_lens[b] - K1 + i; ctx_lens already counts them)."""
+    torch = _torch()
+    dev = k_pool.device
+    _need(k_pool, "k_pool", device=dev)
+    _need(v_pool, "v_pool", k_pool.dtype, dev)
+    _need(k_new, "k_new", k_pool.dtype, dev)
+    _need(v_new, "v_new", k_pool.dtype, dev)
+    _need(page_table, "page_table", torch.int32, dev)
+    _need(ctx_lens, "ctx_lens", torch.int32, dev)
+    B, K1, Hkv, D = k_new.shape
+    P, Hkv2, ps, D2 = k_pool.shape
+    if (Hkv2, D2) != (Hkv, D) or tuple(v_new.shape) != tuple(k_new.shape):
+        raise ValueError("k_new / v_new must be [B, K1, Hkv, D] matching the pools")
+    rc = _lib.load().spec_kv_append(
+        k_new.data_ptr(), v_new.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
+        page_table.data_ptr(), ctx_lens.data_ptr(), B, K1, Hkv, D, ps, P, page_table.shape[1],
+        _dtype_code(k_pool), _stream_ptr(dev, stream))
+    _lib.check("spec_kv_append", rc)
+
+
+def kv_commit(ctx_lens, n_accepted, K1: int, stream=None):
+    """Keep the last committed token and the accepted drafts: ctx -= K1 - 1 - n (in place)."""
+    torch = _torch()
+    dev = ctx_lens.device
+    _need(ctx_lens, "ctx_lens", torch.int32, dev)
+    _need(n_accepted, "n_accepted", torch.int32, dev)
+    rc = _lib.load().spec_kv_commit(ctx_lens.data_ptr(), n_accepted.data_ptr(),
+                                    ctx_lens.shape[0], int(K1), _stream_ptr(dev, stream))
+    _lib.check("spec_kv_commit", rc)
+
+
 def version() -> int:
     return int(_lib.load().spec_version())

@@ -25,6 +25,8 @@ SIGNATURES = {
     "spec_profile_lm_head": (c_int, [c_void_p, c_void_p]),
     "spec_accept_workspace": (c_size_t, [c_int] * 3),
     "spec_accept": (c_int, [c_void_p] * 6 + [c_int] * 3 + [c_void_p, c_size_t, c_void_p]),
+    "spec_kv_append": (c_int, [c_void_p] * 6 + [c_int] * 7 + [c_int, c_void_p]),
+    "spec_kv_commit": (c_int, [c_void_p, c_void_p, c_int, c_int, c_void_p]),
 }
 
 _lib = None

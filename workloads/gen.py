@@ -26,7 +26,7 @@ import numpy as np
 from .configs import Workload, noise_sigma
 
 STREAM_QKV, STREAM_LMHEAD, STREAM_BASE, STREAM_NOISE = 0, 1, 2, 3
-STREAM_DRAFT, STREAM_UNIFORM, STREAM_LAYOUT = 4, 5, 6
+STREAM_DRAFT, STREAM_UNIFORM, STREAM_LAYOUT, STREAM_DRAFTER_Q = 4, 5, 6, 7
 
 
 def seed_words(w: Workload, stream: int, step: int = 0, sub: int = 0) -> np.random.SeedSequence:
@@ -118,6 +118,16 @@ def queries(w: Workload, layer: int, device="cpu", step: int = 0):
     L = w.layers[layer]
     return normal_tensor((w.batch, w.k1, L.hq, L.head_dim),
                          torch_seed(w, STREAM_QKV, step, 3 * layer), device, w.dtype)
+
+
+def drafter_queries(w: Workload, layer: int, hq: int, draft_step: int, device="cpu",
+                    step: int = 0):
+    """Queries [B, 1, hq, D] of one drafter step that reads layer `layer`'s KV pool: one query
+    position per sequence, the drafter's own head count over the target's KV heads."""
+    L = w.layers[layer]
+    return normal_tensor((w.batch, 1, hq, L.head_dim),
+                         torch_seed(w, STREAM_DRAFTER_Q, step, 64 * layer + draft_step), device,
+                         w.dtype)
 
 
 def kv_pools(w: Workload, layer: int, num_pages: int, device="cpu", step: int = 0):
