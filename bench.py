@@ -52,8 +52,8 @@ METRIC = "verified tokens/sec and verify-step HBM GB/s (% peak), batch 1, k=2, 8
 PROFILED_TRAFFIC = {
     "workload": DEFAULT_WORKLOAD,
     "source": "speculative_decoding_decode_amd/csrc/lm_head.hip",
-    "sha256": "88c48b7f182af3098546a237cbb456e6817d3b2992f1170f1af99d12381984c1",
-    "bytes_per_launch": 1345677306,
+    "sha256": "12312b34c7d418cbdb6a767765c54207a72c2514dc8bd4356d144b2646c44a9a",
+    "bytes_per_launch": 1345675513,
 }
 
 
@@ -207,6 +207,68 @@ def cpu_baseline(w, gen, seconds_target=12.0, max_steps=400):
                       f"{t_total:.1f} s"}
 
 
+def adjacent_calls(w, inp, lib, sv, gen, torch, device, sptr, dt, ws_attn, n_out, n0,
+                   iters=200):
+    """The calls on either side of the verify step, timed after it with HIP events on the
+    same stream and pools: KV append of the K1 verified positions for every layer plus the
+    commit, and the drafter's cross-attention (one query per sequence and draft step, K1 = 1,
+    over the committed context of the same pools), k draft steps per verify step."""
+    from speculative_decoding_decode_amd import _lib
+    B, k, K1 = w.batch, w.k, w.k1
+    esz = 2 if w.dtype == "bf16" else 4
+    s0 = inp["sets"][0]
+    ctx_c = (s0["ctx"] - K1).contiguous()                   # committed context of set 0
+    ctx_scratch = s0["ctx"].clone()
+    knew = [gen.normal_tensor((B, K1, L.hkv, L.head_dim), 99 + li, device, w.dtype)
+            for li, L in enumerate(w.layers)]
+    dq = [gen.drafter_queries(w, li, L.hq, 0, device) for li, L in enumerate(w.layers)]
+    dout = [torch.empty((B, 1, L.hq, L.head_dim), dtype=torch.float32, device=device)
+            for L in w.layers]
+    ev = HipEvents(4)
+    ev.record(0, sptr)
+    for it in range(iters):
+        for li, L in enumerate(w.layers):
+            kp, vp = inp["pools"][li]
+            rc = lib.spec_kv_append(knew[li].data_ptr(), knew[li].data_ptr(), kp.data_ptr(),
+                                    vp.data_ptr(), s0["table"].data_ptr(), s0["ctx"].data_ptr(),
+                                    B, K1, L.hkv, L.head_dim, w.page_size, inp["P"],
+                                    inp["max_pages"], dt, sptr)
+            if rc:
+                _lib.check("spec_kv_append", rc)
+        n_row = n_out[(n0 + it) % n_out.shape[0]]
+        rc = lib.spec_kv_commit(ctx_scratch.data_ptr(), n_row.data_ptr(), B, K1, sptr)
+        if rc:
+            _lib.check("spec_kv_commit", rc)
+    ev.record(1, sptr)
+    for it in range(iters):
+        for j in range(k):
+            for li, L in enumerate(w.layers):
+                kp, vp = inp["pools"][li]
+                rc = lib.spec_verify_attn(
+                    dq[li].data_ptr(), kp.data_ptr(), vp.data_ptr(), s0["table"].data_ptr(),
+                    ctx_c.data_ptr(), dout[li].data_ptr(), B, 1, L.hq, L.hkv, L.head_dim,
+                    w.page_size, inp["P"], inp["max_pages"], L.window,
+                    1.0 / math.sqrt(L.head_dim), dt, ws_attn.data_ptr(), ws_attn.numel(), sptr)
+                if rc:
+                    _lib.check("spec_verify_attn", rc)
+    ev.record(2, sptr)
+    torch.cuda.synchronize(device)
+    kv_us = ev.ms(0, 1) * 1e3 / iters
+    dr_us = ev.ms(1, 2) * 1e3 / (iters * max(k, 1))
+    ev.close()
+    # algorithmic bytes: append reads and writes K1 rows of K and V per layer and sequence
+    app_bytes = sum(2 * 2 * B * K1 * L.hkv * L.head_dim * esz for L in w.layers)
+    ctx_committed = [int(c) - K1 for c in inp["ctx"]]
+    dr_bytes = sum(visible_tokens(c, 1, L.window) * L.hkv * L.head_dim * esz * 2
+                   for L in w.layers for c in ctx_committed)
+    return {"kv_append_commit_us_per_step": round(kv_us, 2),
+            "kv_append_bytes_per_step": app_bytes,
+            "drafter_xattn_us_per_draft_step": round(dr_us, 2),
+            "drafter_xattn_kv_bytes_per_draft_step": dr_bytes,
+            "drafter_xattn_gbs": round(dr_bytes / (dr_us * 1e-6) / 1e9, 1),
+            "iterations": iters}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -355,6 +417,9 @@ def main():
         f"{lm_avg_ms * 1e3:.1f} us = {achieved:.0f} GB/s; wall {ms_per_step * 1e3:.1f} us/step; "
         f"acceptance pos {stats.per_position}")
 
+    adjacent = adjacent_calls(w, inp, lib, sv, gen, torch, device, sptr, dt, ws_attn, n_out,
+                              args.warmup)
+
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (fp64 oracle)")
@@ -395,6 +460,7 @@ def main():
                      "traffic_bytes_per_launch": traffic_bytes,
                      "bytes_per_launch": table_bytes, "avg_launch_us": round(lm_avg_ms * 1e3, 2),
                      "launches_timed": int(nsamp)},
+        "adjacent": adjacent,
         "cpu_baseline": cpu,
     }
     print(json.dumps(result), flush=True)

@@ -8,14 +8,19 @@
 // sits at position t = ctx_b - K1 + i and sees keys s in [lo, t], lo = 0 (global) or
 // t - window + 1 (sliding), clipped at 0.
 //
-// Design (gfx950): the visible page range of a sequence is split across workgroups
-// ("split-K" over the context).  A workgroup owns one (sequence, KV head, split, chunk of up
-// to 32 query rows) and walks its pages: each 16-token page of K and of V is one contiguous
-// 16*D block per head, read with coalesced 16-byte loads into LDS; 16 lanes score one query
-// row against the 16 keys and keep the running max / sum with wavefront shuffles (online
-// softmax); the value update then runs one output column per thread.  The workgroup writes
-// (max, sum, unnormalised output) and a second kernel merges the splits with log-sum-exp
-// weights.  All exponentials are base 2 with log2(e) folded into the query scale.
+// Design (gfx950): the work is the flat list of (sequence, KV head, row chunk, visible page)
+// items, and the grid is about one workgroup per resident slot of the GPU ("stream-K"): every
+// workgroup takes an equal contiguous share of the list, whatever the lengths of the sequences
+// in a ragged batch, so all slots stay busy until the end.  The share is computed on the
+// device from the context lengths (each workgroup and each merge wave derives the same
+// numbers).  Within a share a workgroup walks the pages of each (sequence, KV head, row chunk)
+// unit it touches: each 16-token page of K and of V is one contiguous 16*D block per head,
+// read with coalesced 16-byte loads two pages ahead and staged through LDS; scores come from
+// MFMAs (keys x rows tile), the online softmax runs in registers with wavefront shuffles, and
+// the value update is a second MFMA per 16 columns of the head dim.  For every unit it touches
+// the workgroup writes one partial (max, sum, unnormalised output); a second kernel merges the
+// partials of each output row with log-sum-exp weights, one wave per row.  All exponentials
+// are base 2 with log2(e) folded into the query scale.
 #include <math.h>
 
 #include "common.hpp"
@@ -25,12 +30,8 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kPage = 16;
-constexpr int kRows = 32;            // query rows per workgroup
-constexpr int kTargetWGs = 4096;     // splits are sized so the grid reaches about this many
-constexpr long kSmallWork = 2048;    // page-heads below which splits may be a single page
-constexpr int kMinPagesPerSplit = 1;
-constexpr int kMaxPagesPerSplit = 256;   // page ids of a split are staged in LDS
-constexpr int kMaxSplits = 4096;
+constexpr int kMaxPagesPerPiece = 256;   // page ids of one piece are staged in LDS
+constexpr int kMaxPiecesPerUnit = 4096;  // partials merged for one output row
 constexpr float kLog2e = 1.4426950408889634f;
 
 struct Span {
@@ -53,18 +54,27 @@ __device__ __host__ inline Span seq_span(int ctx, int K1, int window, int max_pa
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));   // one 16-byte group
 
-template <int D, typename T>
+template <int D, typename T, int RT>
 struct AttnShape {
   static constexpr int kEPG = 16 / (int)sizeof(T);       // elements per 16-byte group
   static constexpr int kGPR = D / kEPG;                  // 16-byte groups per row
   static constexpr int kStr = D + kEPG;                  // LDS row stride (elements), 16-byte pad
   static constexpr int kTileG = kPage * kGPR;            // 16-byte groups per K (or V) page tile
   static constexpr int kGPT = (kTileG + kThreads - 1) / kThreads;   // per thread
-  static constexpr int kQPT = (kRows * kGPR + kThreads - 1) / kThreads;
+  static constexpr int kRowsWG = 16 * RT;                // query rows of one workgroup
+  static constexpr int kQPT = (kRowsWG * kGPR + kThreads - 1) / kThreads;
   static constexpr int kDT = D / 16;                     // 16-wide tiles of the head dim
   static constexpr int kDTW = kDT / kWaves;              // of them per wave
-  static constexpr size_t kLds = (size_t)(kRows + 2 * kPage) * kStr * sizeof(T);
+  static constexpr size_t kLds = (size_t)(kRowsWG + 2 * kPage) * kStr * sizeof(T);
+  // Waves per SIMD the register budget is set for (one wave of each workgroup per SIMD): as
+  // many workgroups as a CU's 160 KB of LDS holds, capped where the page buffers and output
+  // tiles (growing with D * RT * element size) would no longer fit the registers.
+  static constexpr int kLdsWGs = (int)((160u * 1024u) / kLds);
+  static constexpr int kRowBytes = D * RT * (int)sizeof(T);
+  static constexpr int kRegCap = kRowBytes <= 512 ? 4 : kRowBytes <= 1024 ? 3 : kRowBytes <= 2048 ? 2 : 1;
+  static constexpr int kWavesPerEU = kLdsWGs < kRegCap ? kLdsWGs : kRegCap;
 };
 
 // MFMA helpers: QK^T per K-step, PV per page.  16x16 accumulator layout: lane l holds rows
@@ -116,115 +126,257 @@ template <> struct AttnMma<float> {
   }
 };
 
-// Grid: (B * Hkv * nrowchunk, nsplit).
-// Round trips before the first page is in LDS: the split's page ids, then the queries and the
-// first page's K/V together; while a page is being processed the next page's K/V are in flight
-// in registers.  Per page, every wave computes the whole 16-key x (up to 32)-row score tile
-// with MFMAs (so scores never go through LDS), runs the online softmax in registers (4 keys
-// per lane, two cross-lane shuffles for the row max and sum), and accumulates its quarter of
-// the head dim with MFMAs whose B operand is the probability tile as the score MFMA left it.
-template <int D, typename T>
-__global__ __launch_bounds__(kThreads) void attn_partial(
+// ---------------------------------------------------------------- the stream-K split
+// Item list: for b = 0..B-1, unit j = 0..U-1 (U = Hkv * row chunks, j = g * nrc + rc), the
+// np_b visible pages of sequence b.  Unit (b, j) starts at U * P_b + j * np_b, P_b = sum of
+// np over the sequences before b.  Workgroup w owns items [w * C, (w + 1) * C); the piece it
+// computes of unit u = b * U + j is stored at partial index w + u (consecutive pieces along
+// the list raise w, u or both, so the index is unique and below nwg + B * U).
+
+__device__ __forceinline__ int wave_sum_i(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+__device__ __forceinline__ int wave_max_i(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ __forceinline__ float wave_max_f(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ __forceinline__ float wave_sum_f(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(v, o);
+    if (lane >= o) v += t;
+  }
+  return v;
+}
+__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ long long uni64(long long v) {
+  const unsigned long long u = static_cast<unsigned long long>(v);
+  const unsigned lo = __builtin_amdgcn_readfirstlane(static_cast<unsigned>(u));
+  const unsigned hi = __builtin_amdgcn_readfirstlane(static_cast<unsigned>(u >> 32));
+  return static_cast<long long>((static_cast<unsigned long long>(hi) << 32) | lo);
+}
+
+struct StreamPlan {
+  long long total;   // items
+  int C;             // items per workgroup
+  int ctx0, np0, incl0;   // this lane's sequence (= lane) of the first 64: context, visible
+                          // pages, inclusive prefix sum of visible pages
+};
+
+// Quotient of non-negative a / b, in 32 bits when both fit.
+__device__ __forceinline__ long long div_nn(long long a, long long b) {
+  if (((a | b) >> 31) == 0) return (long long)((unsigned)a / (unsigned)b);
+  return a / b;
+}
+
+// Same result in every lane of every wave that calls it with the same arguments.  c_floor
+// (from the host) keeps the pieces of one unit within kMaxPiecesPerUnit.
+__device__ StreamPlan stream_plan(const int32_t *__restrict__ ctx_lens, int B, int K1, int window,
+                                  int max_pages, int U, int nwg, int c_floor, int lane) {
+  StreamPlan pl;
+  long long tot = 0;
+  for (int c0 = 0; c0 < B; c0 += spec::kWave) {
+    const int c = ctx_lens[min(c0 + lane, B - 1)];
+    const int np = c0 + lane < B ? seq_span(c, K1, window, max_pages).np : 0;
+    const int incl = wave_incl_scan(np, lane);
+    if (c0 == 0) {
+      pl.ctx0 = c;
+      pl.np0 = np;
+      pl.incl0 = incl;
+    }
+    tot += __shfl(incl, spec::kWave - 1);
+  }
+  pl.total = uni64(tot * U);
+  const long long c = div_nn(pl.total + nwg - 1, nwg);
+  pl.C = uni((int)max((long long)c_floor, c));
+  return pl;
+}
+
+// Context length of sequence b (uniform b): from the plan's registers for the first 64.
+__device__ __forceinline__ int ctx_of(const int32_t *__restrict__ ctx_lens, const StreamPlan &pl, int b) {
+  return b < spec::kWave ? uni(__shfl(pl.ctx0, b)) : ctx_lens[b];
+}
+
+// Visible pages of the sequences before b (uniform b).
+__device__ __forceinline__ long long pages_before(const int32_t *__restrict__ ctx_lens,
+                                                  const StreamPlan &pl, int b, int K1, int window,
+                                                  int max_pages, int lane) {
+  if (b < spec::kWave) return b == 0 ? 0 : uni(__shfl(pl.incl0, b - 1));
+  long long Pb = __shfl(pl.incl0, spec::kWave - 1);
+  for (int c0 = spec::kWave; c0 < b; c0 += spec::kWave) {
+    const int bb = min(c0 + lane, b - 1);
+    Pb += wave_sum_i(c0 + lane < b ? seq_span(ctx_lens[bb], K1, window, max_pages).np : 0);
+  }
+  return uni64(Pb);
+}
+
+// Grid: nwg workgroups (one per resident slot, or more for very long contexts); a row chunk
+// is 16 * RT query rows.  Per unit: round trips before the first page is in LDS are the
+// piece's page ids, then the queries and the first two pages' K/V together.  Two register
+// buffers alternate, so while page i is processed pages i + 1 and i + 2 are in flight.  Every
+// fetch is unconditional (an invalid page id re-reads page 0 of the pool, whose data is never
+// used; a fetch past the piece reads a 16-byte location every lane shares), which keeps the
+// wait before each LDS write at "all but the newest page".  Per page, every wave computes the
+// whole 16-key x (16 * RT)-row score tile with MFMAs (so scores never go through LDS), runs
+// the online softmax in registers (4 keys per lane, two cross-lane shuffles for the row max
+// and sum), and accumulates its quarter of the head dim with MFMAs whose B operand is the
+// probability tile as the score MFMA left it.
+template <int D, typename T, int RT>
+__global__ __launch_bounds__(kThreads, (AttnShape<D, T, RT>::kWavesPerEU)) void attn_partial(
     const T *__restrict__ q, const T *__restrict__ kpool, const T *__restrict__ vpool,
     const int32_t *__restrict__ table, const int32_t *__restrict__ ctx_lens,
-    float2 *__restrict__ part_ml, float *__restrict__ part_acc, int K1, int Hq, int Hkv,
-    int num_pages, int max_pages, int window, float qscale, int pps, int nsplit, int GK1) {
-  using S = AttnShape<D, T>;
+    float2 *__restrict__ part_ml, float *__restrict__ part_acc, int B, int K1, int Hq, int Hkv,
+    int num_pages, int max_pages, int window, float qscale, int nwg, int c_floor, int GK1) {
+  using S = AttnShape<D, T, RT>;
   using M = AttnMma<T>;
-  constexpr int RT = kRows / 16;                                   // row tiles
+  constexpr int kRowsWG = S::kRowsWG;
   extern __shared__ __align__(16) unsigned char smem[];
-  T *qs = reinterpret_cast<T *>(smem);                             // [kRows][kStr]
-  T *ks = qs + kRows * S::kStr;                                    // [16][kStr]
+  T *qs = reinterpret_cast<T *>(smem);                             // [kRowsWG][kStr]
+  T *ks = qs + kRowsWG * S::kStr;                                  // [16][kStr]
   T *vs = ks + kPage * S::kStr;                                    // [16][kStr]
-  __shared__ int pid_sh[kMaxPagesPerSplit];
+  __shared__ int pid_sh[kMaxPagesPerPiece];
 
   const int tid = threadIdx.x, lane = tid & (spec::kWave - 1), wave = tid / spec::kWave;
   const int lr = lane & 15, lq = lane >> 4;
-  // blockIdx.x enumerates (sequence, KV head, row chunk) units and blockIdx.y the splits in
-  // reverse: the highest splits, which only the longest sequences have, are dispatched first,
-  // so ragged batches run longest-first instead of ending on a few long workgroups.
-  const int nrc = (GK1 + kRows - 1) / kRows;
-  const int unit = blockIdx.x, s = nsplit - 1 - (int)blockIdx.y;
-  const int b = unit / (Hkv * nrc), g = (unit / nrc) % Hkv, rc = unit % nrc;
   const int G = Hq / Hkv;
-  const Span sp = seq_span(ctx_lens[b], K1, window, max_pages);
-  const int ns = (sp.np + pps - 1) / pps;
-  if (s >= ns) return;
-  const int pg_begin = sp.p0 + s * pps;
-  const int npg = min(sp.p0 + sp.np, pg_begin + pps) - pg_begin;
-  const int rr0 = rc * kRows;
-  const int nr = min(kRows, GK1 - rr0);
+  const int nrc = (GK1 + kRowsWG - 1) / kRowsWG, U = Hkv * nrc;
+  const int rstride = min(GK1, kRowsWG);
+  const int w = blockIdx.x;
 
-  // (1) page ids of the split, then the queries.  Loads are unconditional with clamped
-  // indices so the wait counts the compiler inserts stay exact.
-  const int pid_reg = table[(size_t)b * max_pages + pg_begin + min(tid, npg - 1)];
-  uint4 qraw[S::kQPT];
-#pragma unroll
-  for (int x = 0; x < S::kQPT; ++x) {
-    const int e = min(tid + x * kThreads, nr * S::kGPR - 1);
-    const int r = e / S::kGPR, gi = e - r * S::kGPR;
-    const int rr = rr0 + r, i = rr / G, h = g * G + (rr - i * G);
-    qraw[x] = *reinterpret_cast<const uint4 *>(q + (((size_t)b * K1 + i) * Hq + h) * D + gi * S::kEPG);
-  }
-  if (tid < npg) pid_sh[tid] = (pid_reg >= 0 && pid_reg < num_pages) ? pid_reg : -1;
-  __syncthreads();
+  const StreamPlan sp_all = stream_plan(ctx_lens, B, K1, window, max_pages, U, nwg, c_floor, lane);
+  long long p = (long long)w * sp_all.C;
+  const long long pend = min(sp_all.total, p + sp_all.C);
+  if (p >= pend) return;
 
-  // (2) K/V of page 0 in flight while the queries land in LDS (rows >= nr zero)
-  uint4 kcur[S::kGPT], vcur[S::kGPT], knxt[S::kGPT], vnxt[S::kGPT];
-  auto fetch = [&](uint4(&kr)[S::kGPT], uint4(&vr)[S::kGPT], int i) {
-    const int pid = pid_sh[i];
-    const T *kb = kpool + ((size_t)(pid < 0 ? 0 : pid) * Hkv + g) * kPage * D;
-    const T *vb = vpool + ((size_t)(pid < 0 ? 0 : pid) * Hkv + g) * kPage * D;
-#pragma unroll
-    for (int x = 0; x < S::kGPT; ++x) {
-      const int e = tid + x * kThreads;
-      const bool ok = pid >= 0 && e < S::kTileG;
-      kr[x] = ok ? *reinterpret_cast<const uint4 *>(kb + e * S::kEPG) : uint4{0u, 0u, 0u, 0u};
-      vr[x] = ok ? *reinterpret_cast<const uint4 *>(vb + e * S::kEPG) : uint4{0u, 0u, 0u, 0u};
-    }
-  };
-  fetch(kcur, vcur, 0);
-#pragma unroll
-  for (int x = 0; x < S::kQPT; ++x) {
-    const int e = tid + x * kThreads;
-    if (e < kRows * S::kGPR) {
-      const int r = e / S::kGPR, gi = e - r * S::kGPR;
-      *reinterpret_cast<uint4 *>(qs + r * S::kStr + gi * S::kEPG) =
-          e < nr * S::kGPR ? qraw[x] : uint4{0u, 0u, 0u, 0u};
-    }
-  }
-
-  // per-lane rows: rt * 16 + lr; their query positions and running (max, sum)
-  int trow[RT];
-  float m_run[RT], l_run[RT];
-  f32x4_t o[RT][S::kDTW];
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    const int r = rt * 16 + lr;
-    trow[rt] = r < nr ? sp.ctx - K1 + (rr0 + r) / G : -1;
-    m_run[rt] = -INFINITY;
-    l_run[rt] = 0.f;
-#pragma unroll
-    for (int dt = 0; dt < S::kDTW; ++dt) o[rt][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  }
-  const bool two_tiles = nr > 16;   // uniform
-
-  for (int i = 0; i < npg; ++i) {
-#pragma unroll
-    for (int x = 0; x < S::kGPT; ++x) {
-      const int e = tid + x * kThreads;
-      if (e < S::kTileG) {
-        const int row = e / S::kGPR, gi = e - row * S::kGPR;
-        *reinterpret_cast<uint4 *>(ks + row * S::kStr + gi * S::kEPG) = kcur[x];
-        *reinterpret_cast<uint4 *>(vs + row * S::kStr + gi * S::kEPG) = vcur[x];
+  // the sequence holding item p: U * P_b <= p < U * P_(b+1)
+  int b = 0;
+  long long Pb = 0;
+  {
+    unsigned long long hit = __ballot(sp_all.np0 > 0 && (long long)(sp_all.incl0 - sp_all.np0) * U <= p &&
+                                      p < (long long)sp_all.incl0 * U);
+    if (hit) {
+      const int l = __ffsll(static_cast<long long>(hit)) - 1;
+      b = uni(l);
+      Pb = uni(__shfl(sp_all.incl0 - sp_all.np0, l));
+    } else {
+      long long carry = __shfl(sp_all.incl0, spec::kWave - 1);
+      for (int c0 = spec::kWave; c0 < B; c0 += spec::kWave) {
+        const int np = c0 + lane < B
+                           ? seq_span(ctx_lens[min(c0 + lane, B - 1)], K1, window, max_pages).np
+                           : 0;
+        const int incl = wave_incl_scan(np, lane);
+        const long long lo = (carry + incl - np) * U, hi = (carry + incl) * U;
+        hit = __ballot(np > 0 && lo <= p && p < hi);
+        if (hit) {
+          const int l = __ffsll(static_cast<long long>(hit)) - 1;
+          b = uni(c0 + l);
+          Pb = uni64(carry + __shfl(incl - np, l));
+          break;
+        }
+        carry += __shfl(incl, spec::kWave - 1);
       }
     }
-    if (i + 1 < npg) fetch(knxt, vnxt, i + 1);
-    const bool page_ok = pid_sh[i] >= 0;   // uniform
-    const int pg = pg_begin + i;
+  }
+  Span sp = seq_span(ctx_of(ctx_lens, sp_all, b), K1, window, max_pages);
+  if (sp.np == 0) return;   // no sequence holds p: cannot happen for consistent inputs
+  const long long off0 = p - Pb * U;
+  int j = uni((int)div_nn(off0, sp.np));
+  int o = uni((int)(off0 - (long long)j * sp.np));
+
+  while (true) {
+    const int take = (int)min((long long)(sp.np - o), pend - p);
+    if (take <= 0) break;   // cannot happen for consistent inputs; keeps every wave finite
+    const int g = j / nrc, rc = j - (j / nrc) * nrc;
+    const int pg_begin = sp.p0 + o;
+    const int npg = take;
+    const int rr0 = rc * kRowsWG;
+    const int nr = min(kRowsWG, GK1 - rr0);
+    const long long piece = (long long)w + (long long)b * U + j;
+
+    // (1) page ids of the piece, then the queries.  Loads are unconditional with clamped
+    // indices so the wait counts the compiler inserts stay exact.
+    const int pid_reg = table[(size_t)b * max_pages + pg_begin + min(tid, npg - 1)];
+    u32x4_t qraw[S::kQPT];
+#pragma unroll
+    for (int x = 0; x < S::kQPT; ++x) {
+      const int e = min(tid + x * kThreads, nr * S::kGPR - 1);
+      const int r = e / S::kGPR, gi = e - r * S::kGPR;
+      const int rr = rr0 + r, i = rr / G, h = g * G + (rr - i * G);
+      qraw[x] = *reinterpret_cast<const u32x4_t *>(q + (((size_t)b * K1 + i) * Hq + h) * D + gi * S::kEPG);
+    }
+    if (tid < npg) pid_sh[tid] = (pid_reg >= 0 && pid_reg < num_pages) ? pid_reg : -1;
     __syncthreads();
 
-    if (page_ok) {
+    // (2) K/V of pages 0 and 1 in flight while the queries land in LDS (rows >= nr zero)
+    u32x4_t ka[S::kGPT], va[S::kGPT], kb[S::kGPT], vb[S::kGPT];
+    // A fetch past the piece reads the pools' first 16 bytes in every lane (an L1 hit after
+    // the first), so the loads stay unconditional without costing a trip to memory.
+    auto fetch = [&](u32x4_t(&kr)[S::kGPT], u32x4_t(&vr)[S::kGPT], int i) __attribute__((always_inline)) {
+      const bool real = i < npg;
+      const int pid = pid_sh[min(i, npg - 1)];
+      const size_t off = real ? ((size_t)(pid < 0 ? 0 : pid) * Hkv + g) * kPage * D : 0;
+#pragma unroll
+      for (int x = 0; x < S::kGPT; ++x) {
+        const int e = real ? min(tid + x * kThreads, S::kTileG - 1) : 0;
+        kr[x] = *reinterpret_cast<const u32x4_t *>(kpool + off + e * S::kEPG);
+        vr[x] = *reinterpret_cast<const u32x4_t *>(vpool + off + e * S::kEPG);
+      }
+    };
+    auto stage = [&](const u32x4_t(&kr)[S::kGPT], const u32x4_t(&vr)[S::kGPT]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int x = 0; x < S::kGPT; ++x) {
+        const int e = tid + x * kThreads;
+        if (S::kTileG % kThreads == 0 || e < S::kTileG) {   // static except at D = 64
+          const int row = e / S::kGPR, gi = e - row * S::kGPR;
+          *reinterpret_cast<u32x4_t *>(ks + row * S::kStr + gi * S::kEPG) = kr[x];
+          *reinterpret_cast<u32x4_t *>(vs + row * S::kStr + gi * S::kEPG) = vr[x];
+        }
+      }
+    };
+    fetch(ka, va, 0);
+    fetch(kb, vb, 1);
+#pragma unroll
+    for (int x = 0; x < S::kQPT; ++x) {
+      const int e = tid + x * kThreads;
+      if ((kRowsWG * S::kGPR) % kThreads == 0 || e < kRowsWG * S::kGPR) {
+        const int r = e / S::kGPR, gi = e - r * S::kGPR;
+        *reinterpret_cast<u32x4_t *>(qs + r * S::kStr + gi * S::kEPG) =
+            e < nr * S::kGPR ? qraw[x] : u32x4_t{0u, 0u, 0u, 0u};
+      }
+    }
+
+    // per-lane rows: rt * 16 + lr; their query positions and running (max, sum)
+    int trow[RT];
+    float m_run[RT], l_run[RT];
+    f32x4_t acc[RT][S::kDTW];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      const int r = rt * 16 + lr;
+      trow[rt] = r < nr ? sp.ctx - K1 + (rr0 + r) / G : -1;
+      m_run[rt] = -INFINITY;
+      l_run[rt] = 0.f;
+#pragma unroll
+      for (int dt = 0; dt < S::kDTW; ++dt) acc[rt][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+    const bool two_tiles = nr > 16;   // uniform
+
+    // one page of the piece, already in LDS
+    auto page = [&](int i) __attribute__((always_inline)) {
+      if (pid_sh[i] < 0) return;       // uniform: an invalid page id hides its keys
+      const int pg = pg_begin + i;
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
         if (rt == 1 && !two_tiles) break;
@@ -258,154 +410,216 @@ __global__ __launch_bounds__(kThreads) void attn_partial(
         m_run[rt] = m_new;
 #pragma unroll
         for (int dt = 0; dt < S::kDTW; ++dt) {
-          o[rt][dt] *= alpha;
-          o[rt][dt] = M::pv(vs, S::kStr, (wave * S::kDTW + dt) * 16 + lr, lq, pr, o[rt][dt]);
+          acc[rt][dt] *= alpha;
+          acc[rt][dt] = M::pv(vs, S::kStr, (wave * S::kDTW + dt) * 16 + lr, lq, pr, acc[rt][dt]);
+        }
+      }
+    };
+
+    // Both halves always stage and fetch (an exit between them would reach the next stage on
+    // a path without the second half's loads, and its wait would then have to drain
+    // everything).
+    for (int i = 0; i < npg; i += 2) {
+      stage(ka, va);
+      fetch(ka, va, i + 2);
+      __syncthreads();
+      page(i);
+      __syncthreads();
+      stage(kb, vb);
+      fetch(kb, vb, i + 3);
+      __syncthreads();
+      if (i + 1 < npg) page(i + 1);
+      __syncthreads();
+    }
+
+    // the piece's partial: lane holds O^T[d = dtile*16 + 4*lq + e][row rt*16 + lr]
+    const size_t base = (size_t)piece * rstride;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      const int r = rt * 16 + lr;
+      if (r < nr) {
+        if (wave == 0 && lq == 0) part_ml[base + r] = make_float2(m_run[rt], l_run[rt]);
+#pragma unroll
+        for (int dt = 0; dt < S::kDTW; ++dt) {
+          const int d = (wave * S::kDTW + dt) * 16 + 4 * lq;
+          *reinterpret_cast<float4 *>(part_acc + (base + r) * D + d) =
+              make_float4(acc[rt][dt][0], acc[rt][dt][1], acc[rt][dt][2], acc[rt][dt][3]);
         }
       }
     }
-    __syncthreads();
-#pragma unroll
-    for (int x = 0; x < S::kGPT; ++x) { kcur[x] = knxt[x]; vcur[x] = vnxt[x]; }
-  }
 
-  // partial outputs: lane holds O^T[d = dtile*16 + 4*lq + e][row rt*16 + lr]
-  const size_t base = ((size_t)(b * Hkv + g) * nsplit + s) * GK1 + rr0;
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    const int r = rt * 16 + lr;
-    if (r < nr) {
-      if (wave == 0 && lq == 0) part_ml[base + r] = make_float2(m_run[rt], l_run[rt]);
-#pragma unroll
-      for (int dt = 0; dt < S::kDTW; ++dt) {
-        const int d = (wave * S::kDTW + dt) * 16 + 4 * lq;
-        *reinterpret_cast<float4 *>(part_acc + (base + r) * D + d) =
-            make_float4(o[rt][dt][0], o[rt][dt][1], o[rt][dt][2], o[rt][dt][3]);
+    p += take;
+    if (p >= pend) break;
+    o = 0;
+    if (++j == U) {   // next sequence with visible pages
+      j = 0;
+      bool more = false;
+      while (b + 1 < B) {
+        ++b;
+        sp = seq_span(ctx_of(ctx_lens, sp_all, b), K1, window, max_pages);
+        if (sp.np > 0) { more = true; break; }
       }
+      if (!more) break;   // items left but no sequence: cannot happen for consistent inputs
     }
   }
 }
 
-// Grid: (K1 * Hq, D / 64, B).  Merges the splits of one output row (64 columns per workgroup)
-// with log-sum-exp weights.  Thread (c, sg) sums the splits s = sg (mod 4) of column c; the
-// split loads are issued 16 at a time so a merge costs a few memory round trips.
-constexpr int kCombCols = 64;
-constexpr int kCombGroups = kThreads / kCombCols;   // 4
-constexpr int kCombBatch = 32;
+// Grid: B * K1 * Hq workgroups of kCombWaves waves, one per output row (b, i, h).  Every
+// wave finds the row's pieces (the same plan as the partial kernel) and their common maximum;
+// wave v then sums the weighted partial outputs of pieces v, v + kCombWaves, ..., D / 64
+// columns per lane, with the loads of up to kBatch pieces issued together, and one LDS
+// exchange adds the waves' sums.
+constexpr int kCombWaves = 8;
 
 template <int D>
-__global__ __launch_bounds__(kThreads) void attn_combine(
+__global__ __launch_bounds__(kCombWaves * 64) void attn_combine(
     const float2 *__restrict__ part_ml, const float *__restrict__ part_acc,
-    const int32_t *__restrict__ ctx_lens, float *__restrict__ out, int K1, int Hq, int Hkv,
-    int max_pages, int window, int pps, int nsplit, int GK1) {
-  __shared__ float w_sh[kMaxSplits];
-  __shared__ float red[kThreads];
-  const int tid = threadIdx.x;
-  const int row = blockIdx.x, b = blockIdx.z;
-  const int i = row / Hq, h = row - i * Hq;
+    const int32_t *__restrict__ ctx_lens, float *__restrict__ out, int B, int K1, int Hq, int Hkv,
+    int max_pages, int window, int nwg, int c_floor, int GK1, int rows_wg) {
+  constexpr int NC = D / spec::kWave;                 // columns per lane
+  constexpr int kBatch = NC >= 8 ? 8 : 64 / NC > 16 ? 16 : 64 / NC;
+  typedef float vecc_t __attribute__((ext_vector_type(NC)));
+  __shared__ __align__(16) float red_acc[kCombWaves - 1][D];
+  __shared__ float red_l[kCombWaves];
+  const int tid = threadIdx.x, lane = tid & (spec::kWave - 1), wave = tid / spec::kWave;
+  const long long row = blockIdx.x;
+  const int h = (int)(row % Hq), i = (int)((row / Hq) % K1), b = (int)(row / ((long long)Hq * K1));
   const int G = Hq / Hkv, g = h / G, rr = i * G + (h - g * G);
-  const Span sp = seq_span(ctx_lens[b], K1, window, max_pages);
-  const int ns = (sp.np + pps - 1) / pps;
-  const size_t base = (size_t)(b * Hkv + g) * nsplit * GK1 + rr;   // + s * GK1
+  const int nrc = (GK1 + rows_wg - 1) / rows_wg, U = Hkv * nrc;
+  const int rc = rr / rows_wg, r = rr - rc * rows_wg;
+  const int rstride = min(GK1, rows_wg);
+  float *o = out + row * D + lane * NC;
 
-  // all loads of the merge at once: (max, sum) of every split and up to kCombBatch partial
-  // outputs per thread (split s = sg + kCombGroups * u of column d)
-  const int c = tid % kCombCols, sg = tid / kCombCols;
-  const int d = blockIdx.y * kCombCols + c;
-  float2 ml[kMaxSplits / kThreads];
-#pragma unroll
-  for (int x = 0; x < kMaxSplits / kThreads; ++x) {
-    const int s = tid + x * kThreads;
-    ml[x] = s < ns ? part_ml[base + (size_t)s * GK1] : make_float2(-INFINITY, 0.f);
+  const StreamPlan pl = stream_plan(ctx_lens, B, K1, window, max_pages, U, nwg, c_floor, lane);
+  const long long Pb = pages_before(ctx_lens, pl, b, K1, window, max_pages, lane);
+  const Span sp = seq_span(ctx_of(ctx_lens, pl, b), K1, window, max_pages);
+  if (sp.np == 0) {   // uniform over the workgroup
+    if (wave == 0) *reinterpret_cast<vecc_t *>(o) = vecc_t(0.f);
+    return;
   }
-  float v[kCombBatch];
+  const int j = g * nrc + rc;
+  const long long start = Pb * U + (long long)j * sp.np;
+  const long long w0 = div_nn(start, pl.C), w1 = div_nn(start + sp.np - 1, pl.C);
+  const int n = (int)(w1 - w0 + 1);
+  const long long piece0 = w0 + (long long)b * U + j;
+  const float2 *mlp = part_ml + (size_t)piece0 * rstride + r;
+  const float *ap = part_acc + ((size_t)piece0 * rstride + r) * D + lane * NC;
+  const size_t astep = (size_t)rstride * D;
+  const int nmine = n > wave ? (n - wave + kCombWaves - 1) / kCombWaves : 0;   // pieces wave, wave + kCombWaves, ..
+
+  // this wave's first batch of partial outputs is in flight while the maximum is reduced
+  vecc_t v[kBatch];
 #pragma unroll
-  for (int u = 0; u < kCombBatch; ++u) {
-    const int s = sg + u * kCombGroups;
-    v[u] = s < ns ? part_acc[(base + (size_t)s * GK1) * D + d] : 0.f;
+  for (int t = 0; t < kBatch; ++t)
+    v[t] = *reinterpret_cast<const vecc_t *>(ap + (size_t)min(wave + kCombWaves * t, n - 1) * astep);
+  float mx = -INFINITY;
+  for (int c0 = 0; c0 < n; c0 += spec::kWave) {
+    const float2 x = mlp[(size_t)min(c0 + lane, n - 1) * rstride];
+    if (c0 + lane < n) mx = fmaxf(mx, x.x);
   }
-  float m = -INFINITY;
-#pragma unroll
-  for (int x = 0; x < kMaxSplits / kThreads; ++x) m = fmaxf(m, ml[x].x);
-  red[tid] = m;
-  __syncthreads();
-  for (int h2 = kThreads / 2; h2 > 0; h2 >>= 1) {
-    if (tid < h2) red[tid] = fmaxf(red[tid], red[tid + h2]);
-    __syncthreads();
-  }
-  const float M = red[0];
-  __syncthreads();
+  const float m = wave_max_f(mx);
+
+  // weights of this wave's pieces: lane t of a round holds piece wave + 4 * (t0 + t)
+  vecc_t a = vecc_t(0.f);
   float l = 0.f;
+  for (int t0 = 0; t0 < nmine; t0 += spec::kWave) {
+    const int k = wave + kCombWaves * min(t0 + lane, nmine - 1);
+    const float2 x = mlp[(size_t)k * rstride];
+    const float wk = (t0 + lane < nmine && x.x != -INFINITY) ? exp2f(x.x - m) : 0.f;
+    l += wk * x.y;
+    const int cnt = min(spec::kWave, nmine - t0);
+    for (int u0 = 0; u0 < cnt; u0 += kBatch) {
+      if (t0 + u0 > 0) {
 #pragma unroll
-  for (int x = 0; x < kMaxSplits / kThreads; ++x) {
-    const int s = tid + x * kThreads;
-    if (s < ns) {
-      const float w = ml[x].x == -INFINITY ? 0.f : exp2f(ml[x].x - M);
-      w_sh[s] = w;
-      l += w * ml[x].y;
+        for (int t = 0; t < kBatch; ++t)
+          v[t] = *reinterpret_cast<const vecc_t *>(
+              ap + (size_t)(wave + kCombWaves * min(t0 + u0 + t, nmine - 1)) * astep);
+      }
+#pragma unroll
+      for (int t = 0; t < kBatch; ++t) {
+        const float wt = __shfl(wk, u0 + t);
+        if (u0 + t < cnt) a += wt * v[t];
+      }
     }
   }
-  red[tid] = l;
-  __syncthreads();
-  for (int h2 = kThreads / 2; h2 > 0; h2 >>= 1) {
-    if (tid < h2) red[tid] += red[tid + h2];
-    __syncthreads();
+  l = wave_sum_f(l);
+  if (wave > 0) {
+    *reinterpret_cast<vecc_t *>(&red_acc[wave - 1][lane * NC]) = a;
+    if (lane == 0) red_l[wave] = l;
   }
-  const float L = red[0];
   __syncthreads();
-
-  float o = 0.f;
+  if (wave == 0) {
+    float L = l;
 #pragma unroll
-  for (int u = 0; u < kCombBatch; ++u) {
-    const int s = sg + u * kCombGroups;
-    if (s < ns) o = fmaf(w_sh[s], v[u], o);
-  }
-  for (int s0 = sg + kCombGroups * kCombBatch; s0 < ns; s0 += kCombGroups * kCombBatch) {
-    float v2[kCombBatch];
-#pragma unroll
-    for (int u = 0; u < kCombBatch; ++u) {
-      const int s = s0 + u * kCombGroups;
-      v2[u] = s < ns ? part_acc[(base + (size_t)s * GK1) * D + d] : 0.f;
+    for (int x = 0; x < kCombWaves - 1; ++x) {
+      a += *reinterpret_cast<const vecc_t *>(&red_acc[x][lane * NC]);
+      L += red_l[x + 1];
     }
-#pragma unroll
-    for (int u = 0; u < kCombBatch; ++u) {
-      const int s = s0 + u * kCombGroups;
-      if (s < ns) o = fmaf(w_sh[s], v2[u], o);
-    }
-  }
-  red[tid] = o;
-  __syncthreads();
-  if (sg == 0) {
-    const float tot = ((red[c] + red[c + kCombCols]) + red[c + 2 * kCombCols]) + red[c + 3 * kCombCols];
-    out[(((size_t)b * K1 + i) * Hq + h) * D + d] = L > 0.f ? tot / L : 0.f;
+    *reinterpret_cast<vecc_t *>(o) = L > 0.f ? a / L : vecc_t(0.f);
   }
 }
 
 struct AttnPlan {
-  int pps, nsplit, nrowchunk, GK1;
+  int GK1, rt, rows_wg, nwg, c_floor;
   size_t off_ml, off_acc, bytes;
 };
 
-AttnPlan plan(int B, int K1, int Hq, int Hkv, int D, int max_pages, int window) {
+template <int D, typename T, int RT>
+int waves_per_eu() { return AttnShape<D, T, RT>::kWavesPerEU; }
+
+int slots_per_cu(int D, bool bf16, int rt) {
+#define SLOT_CASE(DD)                                                                           \
+  if (D == DD)                                                                                 \
+    return bf16 ? (rt == 1 ? waves_per_eu<DD, uint16_t, 1>() : waves_per_eu<DD, uint16_t, 2>()) \
+                : (rt == 1 ? waves_per_eu<DD, float, 1>() : waves_per_eu<DD, float, 2>());
+  SLOT_CASE(64) SLOT_CASE(128) SLOT_CASE(256) SLOT_CASE(512)
+#undef SLOT_CASE
+  return 1;
+}
+
+AttnPlan plan(int B, int K1, int Hq, int Hkv, int D, int max_pages, int window, bool bf16) {
   AttnPlan pl;
   pl.GK1 = (Hq / Hkv) * K1;
-  pl.nrowchunk = spec::ceil_div(pl.GK1, kRows);
+  pl.rt = pl.GK1 <= 16 ? 1 : 2;
+  pl.rows_wg = 16 * pl.rt;
+  const int nrc = spec::ceil_div(pl.GK1, pl.rows_wg);
   int span = max_pages;
   if (window > 0) span = min(max_pages, spec::ceil_div(window + K1 - 1, kPage) + 1);
   span = max(span, 1);
-  const long units = (long)B * Hkv * pl.nrowchunk;
-  const int wanted = (int)max(1L, (kTargetWGs + units - 1) / units);
-  // Beyond a small amount of work, splits hold at least GK1 / 2 pages so the partial outputs
-  // (GK1 x D fp32 per split) stay within 1/8 of the KV bytes they summarise; below it, latency
-  // rules and splits may be single pages.
-  const int pmin = (long)span * units > kSmallWork ? max(1, spec::ceil_div(pl.GK1, 2)) : 1;
-  pl.pps = max(max(kMinPagesPerSplit, pmin), spec::ceil_div(span, wanted));
-  pl.pps = min(max(pl.pps, spec::ceil_div(span, kMaxSplits)), kMaxPagesPerSplit);
-  pl.nsplit = spec::ceil_div(span, pl.pps);
-  const size_t rows = (size_t)B * Hkv * pl.nsplit * pl.GK1;
+  const long long units = (long long)B * Hkv * nrc;
+  const long long upper = units * span;                 // items, at most
+  const long long slots = (long long)spec::device_cus() * slots_per_cu(D, bf16, pl.rt);
+  long long nwg = max(slots, (upper + kMaxPagesPerPiece - 1) / kMaxPagesPerPiece);
+  nwg = max(1LL, min(nwg, upper));
+  pl.nwg = (int)nwg;
+  // pieces of one unit stay within kMaxPiecesPerUnit: np / C + 2 <= kMaxPiecesPerUnit
+  pl.c_floor = max(1, spec::ceil_div(max_pages, kMaxPiecesPerUnit - 2));
+  const size_t pieces = (size_t)nwg + (size_t)units;
+  const size_t rows = pieces * (size_t)min(pl.GK1, pl.rows_wg);
   pl.off_ml = 0;
   pl.off_acc = spec::align_up(rows * sizeof(float2), 256);
   pl.bytes = pl.off_acc + spec::align_up(rows * D * sizeof(float), 256);
   return pl;
+}
+
+template <int D, typename T, int RT>
+int launch_partial(const void *q, const void *kp, const void *vp, const int32_t *table,
+                   const int32_t *ctx, int B, int K1, int Hq, int Hkv, int num_pages,
+                   int max_pages, int window, float scale, const AttnPlan &pl, float2 *ml,
+                   float *acc, hipStream_t st) {
+  using S = AttnShape<D, T, RT>;
+  static bool attr_set = false;   // per instantiation; setting it twice is harmless
+  if (!attr_set) {
+    if (hipFuncSetAttribute(reinterpret_cast<const void *>(&attn_partial<D, T, RT>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)S::kLds) != hipSuccess)
+      return spec::fail(SPEC_EHIP, "spec_verify_attn: cannot reserve %zu bytes of LDS", S::kLds);
+    attr_set = true;
+  }
+  hipLaunchKernelGGL((attn_partial<D, T, RT>), dim3(pl.nwg), dim3(kThreads), S::kLds, st,
+                     static_cast<const T *>(q), static_cast<const T *>(kp),
+                     static_cast<const T *>(vp), table, ctx, ml, acc, B, K1, Hq, Hkv, num_pages,
+                     max_pages, window, scale * kLog2e, pl.nwg, pl.c_floor, pl.GK1);
+  return spec::launched("attn_partial");
 }
 
 template <int D, typename T>
@@ -413,25 +627,18 @@ int launch(const void *q, const void *kp, const void *vp, const int32_t *table,
            const int32_t *ctx, float *out, int B, int K1, int Hq, int Hkv, int num_pages,
            int max_pages, int window, float scale, const AttnPlan &pl, char *ws,
            hipStream_t st) {
-  using S = AttnShape<D, T>;
-  static bool attr_set = false;   // per instantiation; setting it twice is harmless
-  if (!attr_set) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void *>(&attn_partial<D, T>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)S::kLds) != hipSuccess)
-      return spec::fail(SPEC_EHIP, "spec_verify_attn: cannot reserve %zu bytes of LDS", S::kLds);
-    attr_set = true;
-  }
   float2 *ml = reinterpret_cast<float2 *>(ws + pl.off_ml);
   float *acc = reinterpret_cast<float *>(ws + pl.off_acc);
-  dim3 grid(B * Hkv * pl.nrowchunk, pl.nsplit);
-  hipLaunchKernelGGL((attn_partial<D, T>), grid, dim3(kThreads), S::kLds, st,
-                     static_cast<const T *>(q), static_cast<const T *>(kp),
-                     static_cast<const T *>(vp), table, ctx, ml, acc, K1, Hq, Hkv, num_pages,
-                     max_pages, window, scale * kLog2e, pl.pps, pl.nsplit, pl.GK1);
-  int rc = spec::launched("attn_partial");
+  int rc = pl.rt == 1
+               ? launch_partial<D, T, 1>(q, kp, vp, table, ctx, B, K1, Hq, Hkv, num_pages,
+                                         max_pages, window, scale, pl, ml, acc, st)
+               : launch_partial<D, T, 2>(q, kp, vp, table, ctx, B, K1, Hq, Hkv, num_pages,
+                                         max_pages, window, scale, pl, ml, acc, st);
   if (rc != SPEC_OK) return rc;
-  hipLaunchKernelGGL((attn_combine<D>), dim3(K1 * Hq, D / kCombCols, B), dim3(kThreads), 0, st, ml, acc, ctx,
-                     out, K1, Hq, Hkv, max_pages, window, pl.pps, pl.nsplit, pl.GK1);
+  const long long rows = (long long)B * K1 * Hq;
+  hipLaunchKernelGGL((attn_combine<D>), dim3((unsigned)rows),
+                     dim3(kCombWaves * 64), 0, st, ml, acc, ctx, out, B, K1, Hq, Hkv, max_pages,
+                     window, pl.nwg, pl.c_floor, pl.GK1, pl.rows_wg);
   return spec::launched("attn_combine");
 }
 
@@ -460,9 +667,9 @@ int check_shape(int B, int K1, int Hq, int Hkv, int D, int page_size, int max_pa
   SPEC_REQUIRE(D == 64 || D == 128 || D == 256 || D == 512, SPEC_EUNSUPPORTED,
                "spec_verify_attn: head dim %d not in {64, 128, 256, 512}", D);
   SPEC_REQUIRE(page_size == kPage, SPEC_EUNSUPPORTED, "spec_verify_attn: page_size=%d, only 16", page_size);
-  SPEC_REQUIRE((long)max_pages <= (long)kMaxSplits * kMaxPagesPerSplit, SPEC_EUNSUPPORTED,
+  SPEC_REQUIRE((long)max_pages <= (long)(kMaxPiecesPerUnit - 2) * kMaxPagesPerPiece, SPEC_EUNSUPPORTED,
                "spec_verify_attn: max_pages_per_seq=%d exceeds %d", max_pages,
-               kMaxSplits * kMaxPagesPerSplit);
+               (kMaxPiecesPerUnit - 2) * kMaxPagesPerPiece);
   return SPEC_OK;
 }
 
@@ -472,7 +679,9 @@ extern "C" size_t spec_verify_attn_workspace(int B, int K1, int Hq, int Hkv, int
                                              int page_size, int max_pages_per_seq, int window) {
   spec::clear_error();
   if (check_shape(B, K1, Hq, Hkv, D, page_size, max_pages_per_seq, window) != SPEC_OK) return 0;
-  return plan(B, K1, Hq, Hkv, D, max_pages_per_seq, window).bytes;
+  // the grid (and with it the workspace) depends on the element type; size for either
+  return max(plan(B, K1, Hq, Hkv, D, max_pages_per_seq, window, true).bytes,
+             plan(B, K1, Hq, Hkv, D, max_pages_per_seq, window, false).bytes);
 }
 
 extern "C" int spec_verify_attn(const void *q, const void *k_pool, const void *v_pool,
@@ -491,7 +700,7 @@ extern "C" int spec_verify_attn(const void *q, const void *k_pool, const void *v
                "spec_verify_attn: unsupported dtype %d", (int)dtype);
   SPEC_REQUIRE(aligned16(q) && aligned16(k_pool) && aligned16(v_pool), SPEC_EINVAL,
                "spec_verify_attn: q, k_pool and v_pool need 16-byte alignment");
-  const AttnPlan pl = plan(B, K1, Hq, Hkv, D, max_pages_per_seq, window);
+  const AttnPlan pl = plan(B, K1, Hq, Hkv, D, max_pages_per_seq, window, dtype == SPEC_BF16);
   SPEC_REQUIRE(workspace != nullptr && workspace_bytes >= pl.bytes, SPEC_EWORKSPACE,
                "spec_verify_attn: workspace of %zu bytes needed, %zu given", pl.bytes, workspace_bytes);
   hipStream_t st = static_cast<hipStream_t>(stream);
