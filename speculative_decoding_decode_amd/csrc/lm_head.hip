@@ -286,9 +286,8 @@ template <> struct Dot<float> {
   }
 };
 
-__device__ __forceinline__ uint4 load_stream(const void *p) {
-  const u32x4_t t = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
-  return uint4{t.x, t.y, t.z, t.w};
+__device__ __forceinline__ u32x4_t load_stream(const void *p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
@@ -298,7 +297,7 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 
 // Grid: ceil(V / 256).  RT = R (rows of hidden states), 1..8.
-template <typename T, int RT>
+template <typename T, int RT, bool Deep>
 __global__ __launch_bounds__(kThreads) void lm_head_gemv(
     const T *__restrict__ X, const T *__restrict__ W, const float *__restrict__ temp,
     float *__restrict__ logits, float *__restrict__ probs, float2 *__restrict__ stats,
@@ -332,22 +331,9 @@ __global__ __launch_bounds__(kThreads) void lm_head_gemv(
     for (int r = 0; r < RT; ++r) acc[i][r] = 0.f;
 
   // (row pair, chunk) position of the next item to load and of the next item to consume,
-  // advanced incrementally (items are visited in order; no division in the loop)
-  int lpr = 0, lj = 0, cpr = 0, cj = 0;
-  auto load = [&](uint4(&w)[kTile][2], int tile) {
-#pragma unroll
-    for (int u = 0; u < kTile; ++u) {
-      const int item = tile * kTile + u;
-      const int col = lj * CW + lane * EPL;
-      const int v = v0 + 2 * lpr;
-      const bool ok = item < nitems && col < H;
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-        w[u][i] = (ok && v + i < V) ? load_stream(W + (size_t)(v + i) * H + col) : uint4{0u, 0u, 0u, 0u};
-      if (++lj == NG) { lj = 0; ++lpr; }
-    }
-  };
-  auto compute = [&](const uint4(&w)[kTile][2], int tile) {
+  // advanced incrementally (items are visited in order; no division in the loop).
+  int lpr = 0, lj = 0, litem = 0, cpr = 0, cj = 0;
+  auto compute = [&](const u32x4_t(&w)[kTile][2], int tile) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < kTile; ++u) {
       const int item = tile * kTile + u;
@@ -356,11 +342,12 @@ __global__ __launch_bounds__(kThreads) void lm_head_gemv(
       if (++cj == NG) { cj = 0; ++cpr; }
       const int col = j * CW + lane * EPL;
       if (col < H) {
+        const uint4 w0 = __builtin_bit_cast(uint4, w[u][0]), w1 = __builtin_bit_cast(uint4, w[u][1]);
 #pragma unroll
         for (int r = 0; r < RT; ++r) {
           const uint4 xv = *reinterpret_cast<const uint4 *>(xs + r * H + col);
-          acc[0][r] = Dt::run(w[u][0], xv, acc[0][r]);
-          acc[1][r] = Dt::run(w[u][1], xv, acc[1][r]);
+          acc[0][r] = Dt::run(w0, xv, acc[0][r]);
+          acc[1][r] = Dt::run(w1, xv, acc[1][r]);
         }
       }
       if (j == NG - 1) {                            // row pair complete (uniform)
@@ -375,14 +362,60 @@ __global__ __launch_bounds__(kThreads) void lm_head_gemv(
       }
     }
   };
-  uint4 wa[kTile][2], wb[kTile][2];
-  load(wa, 0);
-  for (int t = 0; t < ntiles; t += 2) {
-    if (t + 1 < ntiles) load(wb, t + 1);
-    compute(wa, t);
-    if (t + 1 < ntiles) {
-      if (t + 2 < ntiles) load(wa, t + 2);
+  u32x4_t wa[kTile][2], wb[kTile][2];
+  if constexpr (Deep) {
+    // Few waves per SIMD (the hidden rows fill LDS): each wave keeps the next tile in flight
+    // while it computes.  Loads are unconditional so the compiler's wait before each compute
+    // leaves that tile outstanding: rows past V and tail-chunk lanes past H read a clamped
+    // valid address (their sums are never used), items past the wave's last read the table's
+    // first 16 bytes in every lane.
+    auto load = [&](u32x4_t(&w)[kTile][2]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int u = 0; u < kTile; ++u) {
+        const bool real = litem < nitems;
+        const int col = min(lj * CW + lane * EPL, H - EPL);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const int v = min(v0 + 2 * lpr + i, V - 1);
+          w[u][i] = load_stream(real ? W + (size_t)v * H + col : W);
+        }
+        ++litem;
+        if (++lj == NG) { lj = 0; ++lpr; }
+      }
+    };
+    load(wa);
+    load(wb);
+    for (int t = 0; t < ntiles; t += 2) {
+      compute(wa, t);
+      load(wa);
       compute(wb, t + 1);
+      load(wb);
+    }
+  } else {
+    // Many waves per SIMD: each wave loads the next tile and then computes the current one;
+    // the loads past the ends are skipped (the waits then drain each tile, and the
+    // parallelism comes from the other waves, which measured faster at this occupancy).
+    auto load = [&](u32x4_t(&w)[kTile][2]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int u = 0; u < kTile; ++u) {
+        const int col = lj * CW + lane * EPL;
+        const int v = v0 + 2 * lpr;
+        const bool ok = litem < nitems && col < H;
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+          w[u][i] = (ok && v + i < V) ? load_stream(W + (size_t)(v + i) * H + col) : u32x4_t{0u, 0u, 0u, 0u};
+        ++litem;
+        if (++lj == NG) { lj = 0; ++lpr; }
+      }
+    };
+    load(wa);
+    for (int t = 0; t < ntiles; t += 2) {
+      if (t + 1 < ntiles) load(wb);
+      compute(wa, t);
+      if (t + 1 < ntiles) {
+        if (t + 2 < ntiles) load(wa);
+        compute(wb, t + 1);
+      }
     }
   }
 
@@ -432,21 +465,33 @@ __global__ __launch_bounds__(kThreads) void lm_head_gemv(
     if (vok && !greedy[r]) probs[(size_t)r * V + v] = ex[r];
 }
 
-template <typename T, int RT>
-int launch_gemv(const void *X, const void *W, const float *temp, float *logits, float *probs,
-                float2 *stats, int *amax, int H, int V, hipStream_t st) {
-  const size_t lds = (size_t)RT * H * sizeof(T);
+// Above this LDS footprint of the hidden rows fewer than 8 workgroups fit a CU, and each
+// wave then keeps a tile in flight (Deep).
+constexpr size_t kDeepLds = 20 * 1024;
+
+template <typename T, int RT, bool Deep>
+int launch_gemv_p(const void *X, const void *W, const float *temp, float *logits, float *probs,
+                  float2 *stats, int *amax, int H, int V, size_t lds, hipStream_t st) {
   static bool attr_set = false;
   if (!attr_set && lds > 64 * 1024) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void *>(&lm_head_gemv<T, RT>),
+    if (hipFuncSetAttribute(reinterpret_cast<const void *>(&lm_head_gemv<T, RT, Deep>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
       return spec::fail(SPEC_EHIP, "spec_lm_head: cannot reserve %zu bytes of LDS", lds);
     attr_set = true;
   }
-  hipLaunchKernelGGL((lm_head_gemv<T, RT>), dim3(spec::ceil_div(V, kBlockRows)), dim3(kThreads),
-                     lds, st, static_cast<const T *>(X), static_cast<const T *>(W), temp, logits,
-                     probs, stats, amax, H, V);
+  hipLaunchKernelGGL((lm_head_gemv<T, RT, Deep>), dim3(spec::ceil_div(V, kBlockRows)),
+                     dim3(kThreads), lds, st, static_cast<const T *>(X), static_cast<const T *>(W),
+                     temp, logits, probs, stats, amax, H, V);
   return spec::launched("lm_head_gemv");
+}
+
+template <typename T, int RT>
+int launch_gemv(const void *X, const void *W, const float *temp, float *logits, float *probs,
+                float2 *stats, int *amax, int H, int V, hipStream_t st) {
+  const size_t lds = (size_t)RT * H * sizeof(T);
+  return lds > kDeepLds
+             ? launch_gemv_p<T, RT, true>(X, W, temp, logits, probs, stats, amax, H, V, lds, st)
+             : launch_gemv_p<T, RT, false>(X, W, temp, logits, probs, stats, amax, H, V, lds, st);
 }
 
 template <typename T>
