@@ -38,7 +38,8 @@ constexpr int kWaves = kThreads / kWave;          // 4
 constexpr int kBlockRows = 256;                   // vocab rows per statistics block
 constexpr int kDepth = 4;                         // K-steps per load batch
 constexpr int kFinChunk = 4096;                   // vocab entries per finalize workgroup
-constexpr size_t kGemvMaxLds = 128 * 1024;        // hidden rows resident in LDS (GEMV path)
+constexpr size_t kGemvMaxLds = 128 * 1024;
+constexpr bool kXrPrefetch = false;                 // register GEMV: issue next rows before consuming        // hidden rows resident in LDS (GEMV path)
 constexpr float kLog2e = 1.4426950408889634f;
 
 template <typename T> struct Mma;
@@ -296,6 +297,63 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// GEMV epilogue: lane l holds the logits keep[r] of vocab row v0 + l.  Per 256-row block and
+// hidden row: (max, sum of exp) and the first argmax into stats / amax; exp((z - block max) / T)
+// into probs (the finalize rescales it); logits stored when asked for.
+template <int RT>
+__device__ __forceinline__ void gemv_epilogue(const float (&keep)[RT], int v0, int lane, int wave,
+                                              int blk, const float *__restrict__ temp,
+                                              float *__restrict__ logits, float *__restrict__ probs,
+                                              float2 *__restrict__ stats, int *__restrict__ amax,
+                                              int V) {
+  __shared__ float red_m[kWaves][RT];
+  __shared__ float red_s[kWaves][RT];
+  __shared__ int red_i[kWaves][RT];
+  const int v = v0 + lane;
+  const bool vok = v < V;
+#pragma unroll
+  for (int r = 0; r < RT; ++r) {
+    float mx = vok ? keep[r] : -INFINITY;
+    int ax = vok ? v : 0x7fffffff;
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1) {
+      const float om = __shfl_xor(mx, off);
+      const int oa = __shfl_xor(ax, off);
+      if (better(mx, ax, om, oa)) { mx = om; ax = oa; }
+    }
+    if (lane == 0) { red_m[wave][r] = mx; red_i[wave][r] = ax; }
+  }
+  __syncthreads();
+  float ex[RT];
+  bool greedy[RT];
+#pragma unroll
+  for (int r = 0; r < RT; ++r) {
+    float m = red_m[0][r];
+    for (int w2 = 1; w2 < kWaves; ++w2) m = fmaxf(m, red_m[w2][r]);
+    const float tr = temp[r];
+    greedy[r] = !(tr > 0.f);
+    const float c = greedy[r] ? 0.f : kLog2e / tr;
+    ex[r] = vok ? exp2f((keep[r] - m) * c) : 0.f;
+    const float sw = wave_sum(ex[r]);
+    if (lane == 0) red_s[wave][r] = sw;
+    if (vok && logits != nullptr) logits[(size_t)r * V + v] = keep[r];
+  }
+  __syncthreads();
+  if (wave == 0 && lane < RT) {
+    const int r = lane;
+    float m = red_m[0][r];
+    int a = red_i[0][r];
+    for (int w2 = 1; w2 < kWaves; ++w2)
+      if (better(m, a, red_m[w2][r], red_i[w2][r])) { m = red_m[w2][r]; a = red_i[w2][r]; }
+    const float sum = ((red_s[0][r] + red_s[1][r]) + red_s[2][r]) + red_s[3][r];
+    stats[(size_t)blk * RT + r] = make_float2(m, sum);
+    amax[(size_t)blk * RT + r] = a;
+  }
+#pragma unroll
+  for (int r = 0; r < RT; ++r)
+    if (vok && !greedy[r]) probs[(size_t)r * V + v] = ex[r];
+}
+
 // Grid: ceil(V / 256).  RT = R (rows of hidden states), 1..8.
 template <typename T, int RT, bool Deep>
 __global__ __launch_bounds__(kThreads) void lm_head_gemv(
@@ -307,9 +365,6 @@ __global__ __launch_bounds__(kThreads) void lm_head_gemv(
   constexpr int CW = kWave * EPL;                   // elements per 1 KB chunk
   extern __shared__ __align__(16) unsigned char smem[];
   T *xs = reinterpret_cast<T *>(smem);               // [RT][H]
-  __shared__ float red_m[kWaves][RT];
-  __shared__ float red_s[kWaves][RT];
-  __shared__ int red_i[kWaves][RT];
 
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int blk = blockIdx.x;
@@ -419,50 +474,113 @@ __global__ __launch_bounds__(kThreads) void lm_head_gemv(
     }
   }
 
-  // ---- epilogue: this lane holds the logits of vocab row v0 + lane
-  const int v = v0 + lane;
-  const bool vok = v < V;
-#pragma unroll
-  for (int r = 0; r < RT; ++r) {
-    float mx = vok ? keep[r] : -INFINITY;
-    int ax = vok ? v : 0x7fffffff;
-#pragma unroll
-    for (int off = kWave / 2; off > 0; off >>= 1) {
-      const float om = __shfl_xor(mx, off);
-      const int oa = __shfl_xor(ax, off);
-      if (better(mx, ax, om, oa)) { mx = om; ax = oa; }
-    }
-    if (lane == 0) { red_m[wave][r] = mx; red_i[wave][r] = ax; }
-  }
-  __syncthreads();
-  float ex[RT];
-  bool greedy[RT];
-#pragma unroll
-  for (int r = 0; r < RT; ++r) {
-    float m = red_m[0][r];
-    for (int w2 = 1; w2 < kWaves; ++w2) m = fmaxf(m, red_m[w2][r]);
-    const float tr = temp[r];
-    greedy[r] = !(tr > 0.f);
-    const float c = greedy[r] ? 0.f : kLog2e / tr;
-    ex[r] = vok ? exp2f((keep[r] - m) * c) : 0.f;
-    const float sw = wave_sum(ex[r]);
-    if (lane == 0) red_s[wave][r] = sw;
-    if (vok && logits != nullptr) logits[(size_t)r * V + v] = keep[r];
-  }
-  __syncthreads();
-  if (wave == 0 && lane < RT) {
-    const int r = lane;
-    float m = red_m[0][r];
-    int a = red_i[0][r];
-    for (int w2 = 1; w2 < kWaves; ++w2)
-      if (better(m, a, red_m[w2][r], red_i[w2][r])) { m = red_m[w2][r]; a = red_i[w2][r]; }
-    const float sum = ((red_s[0][r] + red_s[1][r]) + red_s[2][r]) + red_s[3][r];
-    stats[(size_t)blk * RT + r] = make_float2(m, sum);
-    amax[(size_t)blk * RT + r] = a;
-  }
+  gemv_epilogue<RT>(keep, v0, lane, wave, blk, temp, logits, probs, stats, amax, V);
+}
+
+// Grid: ceil(V / 256).  Small R * H: the hidden rows live in registers (lane l holds columns
+// j * 512 + 8 l, j < NG, of every row; 1 KB of a table row per wave load), so the inner loop
+// is table loads and dot products only.  Each wave streams its 64 table rows kXrRows at a
+// time: all NG chunks of those rows are issued together and consumed in order (with PF the
+// next rows' loads are issued before the current rows are consumed).  A tail chunk past H is
+// masked to zero on both operands.
+constexpr int kXrRows = 2;
+
+template <typename T, int RT, int NG, bool PF>
+__global__ __launch_bounds__(kThreads) void lm_head_gemv_xr(
+    const T *__restrict__ X, const T *__restrict__ W, const float *__restrict__ temp,
+    float *__restrict__ logits, float *__restrict__ probs, float2 *__restrict__ stats,
+    int *__restrict__ amax, int H, int V) {
+  using Dt = Dot<T>;
+  constexpr int EPL = Dt::kEPL;
+  constexpr int CW = kWave * EPL;                   // elements per 1 KB chunk
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int blk = blockIdx.x;
+  const int v0 = blk * kBlockRows + wave * kRowsPerWave;
+
+  uint4 xr[RT][NG];
 #pragma unroll
   for (int r = 0; r < RT; ++r)
-    if (vok && !greedy[r]) probs[(size_t)r * V + v] = ex[r];
+#pragma unroll
+    for (int j = 0; j < NG; ++j) {
+      const int col = j * CW + lane * EPL;
+      xr[r][j] = col < H ? *reinterpret_cast<const uint4 *>(X + (size_t)r * H + col) : uint4{0u, 0u, 0u, 0u};
+    }
+  const bool tail_ok = (NG - 1) * CW + lane * EPL < H;   // this lane's part of the last chunk
+  float keep[RT];
+#pragma unroll
+  for (int r = 0; r < RT; ++r) keep[r] = -INFINITY;
+
+  auto load = [&](u32x4_t(&w)[kXrRows][NG], int rb) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < kXrRows; ++i) {
+      const T *row = W + (size_t)min(v0 + rb + i, V - 1) * H;
+#pragma unroll
+      for (int j = 0; j < NG; ++j)
+        w[i][j] = load_stream(row + min(j * CW + lane * EPL, H - EPL));
+    }
+  };
+  auto consume = [&](const u32x4_t(&w)[kXrRows][NG], int rb) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < kXrRows; ++i) {
+      float sdot[RT];
+#pragma unroll
+      for (int r = 0; r < RT; ++r) sdot[r] = 0.f;
+#pragma unroll
+      for (int j = 0; j < NG; ++j) {
+        uint4 wv = __builtin_bit_cast(uint4, w[i][j]);
+        if (j == NG - 1 && !tail_ok) wv = uint4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int r = 0; r < RT; ++r) sdot[r] = Dt::run(wv, xr[r][j], sdot[r]);
+      }
+#pragma unroll
+      for (int r = 0; r < RT; ++r) {
+        const float t = wave_sum(sdot[r]);
+        if (lane == rb + i) keep[r] = t;
+      }
+    }
+  };
+  if constexpr (PF) {
+    u32x4_t wa[kXrRows][NG], wb[kXrRows][NG];
+    load(wa, 0);
+    for (int rb = 0; rb < kRowsPerWave; rb += 2 * kXrRows) {
+      load(wb, rb + kXrRows);
+      consume(wa, rb);
+      load(wa, min(rb + 2 * kXrRows, kRowsPerWave - kXrRows));   // last one re-reads rows
+      consume(wb, rb + kXrRows);
+    }
+  } else {
+    for (int rb = 0; rb < kRowsPerWave; rb += kXrRows) {
+      u32x4_t w[kXrRows][NG];
+      load(w, rb);
+      consume(w, rb);
+    }
+  }
+  gemv_epilogue<RT>(keep, v0, lane, wave, blk, temp, logits, probs, stats, amax, V);
+}
+
+template <typename T, int RT, int NG>
+int launch_gemv_xr(const void *X, const void *W, const float *temp, float *logits, float *probs,
+                   float2 *stats, int *amax, int H, int V, hipStream_t st) {
+  hipLaunchKernelGGL((lm_head_gemv_xr<T, RT, NG, kXrPrefetch>), dim3(spec::ceil_div(V, kBlockRows)),
+                     dim3(kThreads), 0, st, static_cast<const T *>(X), static_cast<const T *>(W),
+                     temp, logits, probs, stats, amax, H, V);
+  return spec::launched("lm_head_gemv_xr");
+}
+
+// Register-resident hidden rows for R <= 3 and H within 5 chunks of 1 KB.
+constexpr int kXrMaxR = 3, kXrMaxChunks = 5;
+
+template <typename T>
+int launch_gemv_xr_r(int R, const void *X, const void *W, const float *temp, float *logits,
+                     float *probs, float2 *stats, int *amax, int H, int V, hipStream_t st) {
+  const int ng = spec::ceil_div(H, kWave * Dot<T>::kEPL);
+#define XR_CASE(RR, NN) \
+  if (R == RR && ng == NN) return launch_gemv_xr<T, RR, NN>(X, W, temp, logits, probs, stats, amax, H, V, st);
+#define XR_ROW(NN) XR_CASE(1, NN) XR_CASE(2, NN) XR_CASE(3, NN)
+  XR_ROW(1) XR_ROW(2) XR_ROW(3) XR_ROW(4) XR_ROW(5)
+#undef XR_ROW
+#undef XR_CASE
+  return spec::fail(SPEC_EHIP, "spec_lm_head: no register-resident GEMV for R=%d H=%d", R, H);
 }
 
 // Above this LDS footprint of the hidden rows fewer than 8 workgroups fit a CU, and each
@@ -699,8 +817,13 @@ extern "C" int spec_lm_head(const void *hidden, const void *weight, const float 
     return spec::fail(SPEC_EHIP, "spec_lm_head: hipEventRecord(start) failed");
   const size_t esz = dtype == SPEC_BF16 ? 2 : 4;
   const bool gemv = R <= kGemvMaxR && (size_t)R * H * esz <= kGemvMaxLds;
+  const bool gemv_xr = R <= kXrMaxR && spec::ceil_div(H, kWave * (int)(16 / esz)) <= kXrMaxChunks;
   int rc;
-  if (gemv)
+  if (gemv_xr)
+    rc = dtype == SPEC_BF16
+             ? launch_gemv_xr_r<uint16_t>(R, hidden, weight, temperature, logits, probs, stats, amax, H, V, st)
+             : launch_gemv_xr_r<float>(R, hidden, weight, temperature, logits, probs, stats, amax, H, V, st);
+  else if (gemv)
     rc = dtype == SPEC_BF16
              ? launch_gemv_r<uint16_t>(R, hidden, weight, temperature, logits, probs, stats, amax, H, V, st)
              : launch_gemv_r<float>(R, hidden, weight, temperature, logits, probs, stats, amax, H, V, st);
