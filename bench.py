@@ -47,13 +47,13 @@ SAMPLE_EVERY = 16     # steps whose contraction kernel is bracketed by HIP event
 HBM_PEAK_GBS = 8000.0
 METRIC = "verified tokens/sec and verify-step HBM GB/s (% peak), batch 1, k=2, 8K ctx"
 # HBM bytes per launch of the contraction kernel from rocprofv3 FETCH_SIZE / WRITE_SIZE runs,
-# scaled by a 1 GiB copy (profiles/lm_head_gemv_b1_k2_sliding256_8k_traffic.md).  Valid only
+# scaled by a 1 GiB copy (profiles/lm_head_b1_k2_sliding256_8k_traffic.md).  Valid only
 # for the default workload and the kernel source those counters were taken on.
 PROFILED_TRAFFIC = {
     "workload": DEFAULT_WORKLOAD,
     "source": "speculative_decoding_decode_amd/csrc/lm_head.hip",
-    "sha256": "12312b34c7d418cbdb6a767765c54207a72c2514dc8bd4356d144b2646c44a9a",
-    "bytes_per_launch": 1345675513,
+    "sha256": "b2f7fb52cc7b18f9a022b9d3b21d95a6313fd8d481bb9049c06c11b946a90004",
+    "bytes_per_launch": 1345616209,
 }
 
 

@@ -83,12 +83,15 @@ __device__ void block_inclusive_scan(uint64_t *sh) {
 
 // Chunk c of a sequence's row: elements [c * chunk, (c + 1) * chunk), chunk = kThreads * E;
 // thread t owns the E contiguous elements starting at c * chunk + t * E (E is 4 in the common
-// case, one float4 load per row).
+// case; a multiple of 4 is read as float4s).
 template <int E>
 __device__ __forceinline__ void load_run(const float *__restrict__ row, int j0, int V, float (&x)[E]) {
-  if (E == 4 && j0 + 3 < V && (V & 3) == 0) {
-    const float4 t = *reinterpret_cast<const float4 *>(row + j0);
-    x[0] = t.x; x[1] = t.y; x[2] = t.z; x[3] = t.w;
+  if (E % 4 == 0 && j0 + E <= V && (V & 3) == 0) {
+#pragma unroll
+    for (int g = 0; g < E / 4; ++g) {
+      const float4 t = *reinterpret_cast<const float4 *>(row + j0 + 4 * g);
+      x[4 * g] = t.x; x[4 * g + 1] = t.y; x[4 * g + 2] = t.z; x[4 * g + 3] = t.w;
+    }
   } else {
 #pragma unroll
     for (int e = 0; e < E; ++e) x[e] = j0 + e < V ? row[j0 + e] : 0.f;

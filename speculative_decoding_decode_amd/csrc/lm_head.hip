@@ -26,6 +26,7 @@
 #include <math.h>
 
 #include "common.hpp"
+#include "softmax_stats.hpp"
 
 namespace {
 
@@ -38,8 +39,9 @@ constexpr int kWaves = kThreads / kWave;          // 4
 constexpr int kBlockRows = 256;                   // vocab rows per statistics block
 constexpr int kDepth = 4;                         // K-steps per load batch
 constexpr int kFinChunk = 4096;                   // vocab entries per finalize workgroup
-constexpr size_t kGemvMaxLds = 128 * 1024;
-constexpr bool kXrPrefetch = false;                 // register GEMV: issue next rows before consuming        // hidden rows resident in LDS (GEMV path)
+constexpr long kFinWideWGs = 2048;                // above this many, 4x larger chunks
+constexpr size_t kGemvMaxLds = 128 * 1024;        // hidden rows resident in LDS (GEMV path)
+constexpr bool kXrPrefetch = false;               // register GEMV: issue next rows before consuming
 constexpr float kLog2e = 1.4426950408889634f;
 
 template <typename T> struct Mma;
@@ -628,94 +630,57 @@ int launch_gemv_r(int R, const void *X, const void *W, const float *temp, float 
 }
 
 // Merge the block statistics of row blockIdx.y and normalise its chunk of p in place.
-// Grid: (ceil(V / kFinChunk), R).  Every load the workgroup needs (its share of the row's
-// block statistics, the statistics of the blocks it rescales, its p entries) is issued before
-// the first wait, so the kernel costs one memory round trip plus two LDS reductions.
-constexpr int kFinStatsPerThread = 4;            // up to 4 * 256 blocks = V <= 262144 in one pass
-constexpr int kFinPerThread = kFinChunk / kThreads;   // 16 p entries (4 float4)
-constexpr int kFinBlocks = kFinChunk / kBlockRows;    // 16 blocks per chunk
-
+// Grid: (ceil(V / CH), R), CH = 4096 or 16384 vocabulary entries per workgroup (the larger
+// chunk when there are enough rows to fill the GPU, so fewer workgroups repeat the row's
+// statistics reduction and each thread streams more entries).  Every load the workgroup needs
+// (its share of the row's block statistics, the statistics of the blocks it rescales, its p
+// entries) is issued before the first wait, so the kernel costs one memory round trip plus two
+// cross-wave exchanges.
+template <int CH>
 __global__ __launch_bounds__(kThreads) void lm_head_finalize(
     float *__restrict__ probs, const float2 *__restrict__ stats, const int *__restrict__ amax,
     const float *__restrict__ temp, int R, int V, int nblk) {
-  __shared__ float sm[kThreads];
-  __shared__ int si[kThreads];
-  __shared__ float fac[kFinBlocks];
+  constexpr int kPer = CH / kThreads;             // p entries per thread
+  constexpr int kBlocks = CH / kBlockRows;        // statistics blocks per chunk
+  __shared__ float sm[spec::kStatWaves], ss[spec::kStatWaves];
+  __shared__ int si[spec::kStatWaves];
+  __shared__ float fac[kBlocks];
   const int r = blockIdx.y, tid = threadIdx.x;
   const float tr = temp[r];
   const bool greedy = !(tr > 0.f);
-  const float c = greedy ? 0.f : kLog2e / tr;
-  const int v0 = blockIdx.x * kFinChunk;
+  float c[1] = {spec::stat_scale(tr)};
+  const int v0 = blockIdx.x * CH;
   const int blk0 = v0 / kBlockRows;
   float *row = probs + (size_t)r * V;
   const bool vec = (V & 3) == 0;
 
-  // p entries of this chunk: 4 float4 per thread (vector path)
-  float4 pv[kFinPerThread / 4];
+  // p entries of this chunk: kPer / 4 float4 per thread (vector path)
+  float4 pv[kPer / 4];
   if (!greedy && vec) {
 #pragma unroll
-    for (int i = 0; i < kFinPerThread / 4; ++i) {
+    for (int i = 0; i < kPer / 4; ++i) {
       const int v = v0 + (tid + i * kThreads) * 4;
       pv[i] = v < V ? *reinterpret_cast<const float4 *>(row + v) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
   }
   // statistics of the chunk's own blocks (for the rescale factors)
   float own_m = 0.f;
-  if (tid < kFinBlocks && blk0 + tid < nblk) own_m = stats[(size_t)(blk0 + tid) * R + r].x;
+  if (tid < kBlocks && blk0 + tid < nblk) own_m = stats[(size_t)(blk0 + tid) * R + r].x;
 
-  float m = -INFINITY, ssum = 0.f;
-  int a = 0x7fffffff;
-  for (int b0 = 0; b0 < nblk; b0 += kThreads * kFinStatsPerThread) {
-    float2 st[kFinStatsPerThread];
-    int ia[kFinStatsPerThread];
-#pragma unroll
-    for (int i = 0; i < kFinStatsPerThread; ++i) {
-      const int b = b0 + tid + i * kThreads;
-      st[i] = b < nblk ? stats[(size_t)b * R + r] : make_float2(-INFINITY, 0.f);
-      ia[i] = b < nblk ? amax[(size_t)b * R + r] : 0x7fffffff;
-    }
-    // running (max, sum) merge of this thread's blocks
-#pragma unroll
-    for (int i = 0; i < kFinStatsPerThread; ++i) {
-      if (better(m, a, st[i].x, ia[i])) a = ia[i];
-      const float nm = fmaxf(m, st[i].x);
-      if (nm != -INFINITY) {
-        ssum = ssum * exp2f((m - nm) * c) + st[i].y * exp2f((st[i].x - nm) * c);
-        m = nm;
-      }
-    }
-  }
-  // block max / first argmax
-  sm[tid] = m;
-  si[tid] = a;
-  __syncthreads();
-  for (int h = kThreads / 2; h > 0; h >>= 1) {
-    if (tid < h && better(sm[tid], si[tid], sm[tid + h], si[tid + h])) {
-      sm[tid] = sm[tid + h];
-      si[tid] = si[tid + h];
-    }
-    __syncthreads();
-  }
-  const float gmax = sm[0];
-  const int garg = si[0];
-  __syncthreads();
+  const spec::RowPartial w[1] = {spec::stat_partial(stats, amax, R, r, nblk, c[0], tid)};
+  float gmax[1], gsum[1];
+  int garg[1];
+  spec::stat_reduce<1>(w, c, 1, gmax, garg, gsum, sm, si, ss);
   if (greedy) {
-    for (int v = v0 + tid; v < min(V, v0 + kFinChunk); v += kThreads) row[v] = (v == garg) ? 1.f : 0.f;
+    for (int v = v0 + tid; v < min(V, v0 + CH); v += kThreads) row[v] = (v == garg[0]) ? 1.f : 0.f;
     return;
   }
-  // block sum, each thread's partial rescaled to the global max
-  sm[tid] = m == -INFINITY ? 0.f : ssum * exp2f((m - gmax) * c);
-  __syncthreads();
-  for (int h = kThreads / 2; h > 0; h >>= 1) {
-    if (tid < h) sm[tid] += sm[tid + h];
-    __syncthreads();
-  }
-  const float inv = 1.f / sm[0];
-  if (tid < kFinBlocks) fac[tid] = exp2f((own_m - gmax) * c) * inv;
+  const float inv = 1.f / gsum[0];
+  if (tid < kBlocks) fac[tid] = spec::stat_factor(own_m, gmax[0], c[0], inv);
   __syncthreads();
   if (vec) {
 #pragma unroll
-    for (int i = 0; i < kFinPerThread / 4; ++i) {
+    for (int i = 0; i < kPer / 4; ++i) {
       const int v = v0 + (tid + i * kThreads) * 4;
       if (v < V) {
         const float f = fac[(v - v0) / kBlockRows];
@@ -725,7 +690,7 @@ __global__ __launch_bounds__(kThreads) void lm_head_finalize(
       }
     }
   } else {
-    for (int v = v0 + tid; v < min(V, v0 + kFinChunk); v += kThreads) row[v] *= fac[(v - v0) / kBlockRows];
+    for (int v = v0 + tid; v < min(V, v0 + CH); v += kThreads) row[v] *= fac[(v - v0) / kBlockRows];
   }
 }
 
@@ -769,6 +734,7 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 thread_local hipEvent_t g_prof_start = nullptr, g_prof_stop = nullptr;
 
+
 }  // namespace
 
 extern "C" int spec_profile_lm_head(void *start_event, void *stop_event) {
@@ -777,37 +743,46 @@ extern "C" int spec_profile_lm_head(void *start_event, void *stop_event) {
   return SPEC_OK;
 }
 
-extern "C" size_t spec_lm_head_workspace(int R, int H, int V) {
-  if (R <= 0 || H <= 0 || V <= 0) {
-    spec::fail(SPEC_EINVAL, "spec_lm_head_workspace: R=%d H=%d V=%d must be positive", R, H, V);
-    return 0;
-  }
-  const size_t nblk = (size_t)spec::ceil_div(V, kBlockRows);
-  return spec::align_up(nblk * R * sizeof(float2), 256) + spec::align_up(nblk * R * sizeof(int), 256);
+static_assert(kBlockRows == spec::kStatBlock && kThreads == spec::kStatThreads,
+              "statistics blocks and reducing workgroups must match the shared routine");
+
+namespace {
+
+// Workspace of the lm-head statistics: per 256-row vocabulary block and hidden row, (block
+// max, block sum of exp) as float2 [nblk][R] at offset 0, then the block's first argmax as int
+// [nblk][R] at amax_offset.
+struct LmStats {
+  size_t amax_offset, bytes;
+  int nblk;
+};
+
+LmStats lm_stats_layout(int R, int V) {
+  LmStats l;
+  l.nblk = spec::ceil_div(V, kBlockRows);
+  l.amax_offset = spec::align_up((size_t)l.nblk * R * sizeof(float2), 256);
+  l.bytes = l.amax_offset + spec::align_up((size_t)l.nblk * R * sizeof(int), 256);
+  return l;
 }
 
-extern "C" int spec_lm_head(const void *hidden, const void *weight, const float *temperature,
-                            float *logits, float *probs, int R, int H, int V, spec_dtype dtype,
-                            void *workspace, size_t workspace_bytes, void *stream) {
-  spec::clear_error();
+int lm_head_check(const void *hidden, const void *weight, const float *temperature,
+                  const float *probs, const float *logits, int R, int H, int V, spec_dtype dtype,
+                  const char *who) {
   SPEC_REQUIRE(hidden && weight && temperature && probs, SPEC_EINVAL,
-               "spec_lm_head: hidden, weight, temperature and probs must be non-null");
-  SPEC_REQUIRE(R > 0 && H > 0 && V > 0, SPEC_EINVAL,
-               "spec_lm_head: R=%d H=%d V=%d must be positive", R, H, V);
+               "%s: hidden, weight, temperature and probs must be non-null", who);
+  SPEC_REQUIRE(R > 0 && H > 0 && V > 0, SPEC_EINVAL, "%s: R=%d H=%d V=%d must be positive", who,
+               R, H, V);
   SPEC_REQUIRE(dtype == SPEC_F32 || dtype == SPEC_BF16, SPEC_EUNSUPPORTED,
-               "spec_lm_head: unsupported dtype %d", (int)dtype);
-  SPEC_REQUIRE(H % 8 == 0, SPEC_EUNSUPPORTED, "spec_lm_head: H=%d must be a multiple of 8", H);
+               "%s: unsupported dtype %d", who, (int)dtype);
+  SPEC_REQUIRE(H % 8 == 0, SPEC_EUNSUPPORTED, "%s: H=%d must be a multiple of 8", who, H);
   SPEC_REQUIRE(aligned16(hidden) && aligned16(weight) && aligned16(probs) &&
                    (logits == nullptr || aligned16(logits)),
-               SPEC_EINVAL, "spec_lm_head: hidden, weight, probs and logits need 16-byte alignment");
-  const size_t need = spec_lm_head_workspace(R, H, V);
-  SPEC_REQUIRE(workspace != nullptr && workspace_bytes >= need, SPEC_EWORKSPACE,
-               "spec_lm_head: workspace of %zu bytes needed, %zu given", need, workspace_bytes);
-  const size_t nblk = (size_t)spec::ceil_div(V, kBlockRows);
-  float2 *stats = static_cast<float2 *>(workspace);
-  int *amax = reinterpret_cast<int *>(static_cast<char *>(workspace) +
-                                      spec::align_up(nblk * R * sizeof(float2), 256));
-  hipStream_t st = static_cast<hipStream_t>(stream);
+               SPEC_EINVAL, "%s: hidden, weight, probs and logits need 16-byte alignment", who);
+  return SPEC_OK;
+}
+
+int lm_head_contract(const void *hidden, const void *weight, const float *temperature,
+                     float *logits, float *probs, float2 *stats, int *amax, int R, int H, int V,
+                     spec_dtype dtype, hipStream_t st) {
   // MFMA path: up to 6 tiles of 16 hidden rows per pass over the table (128 VGPRs per lane at
   // 1024 threads); more rows take further passes.
   const int NT = min(kMaxNT, spec::ceil_div(R, 16));
@@ -834,8 +809,47 @@ extern "C" int spec_lm_head(const void *hidden, const void *weight, const float 
   if (rc != SPEC_OK) return rc;
   if (ev1 != nullptr && hipEventRecord(ev1, st) != hipSuccess)
     return spec::fail(SPEC_EHIP, "spec_lm_head: hipEventRecord(stop) failed");
-  dim3 grid(spec::ceil_div(V, kFinChunk), R);
-  hipLaunchKernelGGL(lm_head_finalize, grid, dim3(kThreads), 0, st, probs, stats, amax,
-                     temperature, R, V, (int)nblk);
+  return SPEC_OK;
+}
+
+int lm_head_finalize_launch(float *probs, const float2 *stats, const int *amax,
+                            const float *temperature, int R, int V, hipStream_t st) {
+  const int nblk = spec::ceil_div(V, kBlockRows);
+  if ((long)R * spec::ceil_div(V, kFinChunk) > kFinWideWGs) {
+    hipLaunchKernelGGL(lm_head_finalize<4 * kFinChunk>, dim3(spec::ceil_div(V, 4 * kFinChunk), R),
+                       dim3(kThreads), 0, st, probs, stats, amax, temperature, R, V, nblk);
+  } else {
+    hipLaunchKernelGGL(lm_head_finalize<kFinChunk>, dim3(spec::ceil_div(V, kFinChunk), R),
+                       dim3(kThreads), 0, st, probs, stats, amax, temperature, R, V, nblk);
+  }
   return spec::launched("lm_head_finalize");
+}
+
+}  // namespace
+
+extern "C" size_t spec_lm_head_workspace(int R, int H, int V) {
+  if (R <= 0 || H <= 0 || V <= 0) {
+    spec::fail(SPEC_EINVAL, "spec_lm_head_workspace: R=%d H=%d V=%d must be positive", R, H, V);
+    return 0;
+  }
+  return lm_stats_layout(R, V).bytes;
+}
+
+extern "C" int spec_lm_head(const void *hidden, const void *weight, const float *temperature,
+                            float *logits, float *probs, int R, int H, int V, spec_dtype dtype,
+                            void *workspace, size_t workspace_bytes, void *stream) {
+  spec::clear_error();
+  int rc = lm_head_check(hidden, weight, temperature, probs, logits, R, H, V, dtype,
+                               "spec_lm_head");
+  if (rc != SPEC_OK) return rc;
+  const LmStats ls = lm_stats_layout(R, V);
+  SPEC_REQUIRE(workspace != nullptr && workspace_bytes >= ls.bytes, SPEC_EWORKSPACE,
+               "spec_lm_head: workspace of %zu bytes needed, %zu given", ls.bytes, workspace_bytes);
+  float2 *stats = static_cast<float2 *>(workspace);
+  int *amax = reinterpret_cast<int *>(static_cast<char *>(workspace) + ls.amax_offset);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  rc = lm_head_contract(hidden, weight, temperature, logits, probs, stats, amax, R, H, V,
+                              dtype, st);
+  if (rc != SPEC_OK) return rc;
+  return lm_head_finalize_launch(probs, stats, amax, temperature, R, V, st);
 }
