@@ -96,3 +96,18 @@ def test_deterministic_repeat():
     b = sv.verify_attn(**inp)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("dtype,window,k", [("bf16", 0, 2), ("f32", 40, 0)])
+def test_many_sequences(dtype, window, k):
+    """More than 64 sequences (the work split scans the context lengths 64 at a time), ragged,
+    with empty contexts and contexts holding only the verified positions."""
+    B = 150
+    w = small_workload(dtype, 4, 2, 128, window, k, batch=B)
+    rng = np.random.default_rng(21)
+    ctx = rng.integers(k + 1, 700, size=B).astype(np.int32)
+    ctx[[3, 70, 149]] = 0                                   # nothing cached
+    ctx[[5, 100]] = k + 1                                   # only the verified positions
+    table, P = gen.page_tables(w, ctx, max_pages=44)
+    inp = attn_inputs(w, 0, dev(), ctx=ctx, table=table, num_pages=P)
+    check(inp, dtype, f"{B} ragged sequences {dtype} window {window} k {k}")
