@@ -1,6 +1,7 @@
 """Benchmark of the verify step on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--workload NAME]
+    python bench.py --sweep-k KMAX [--workload NAME] [--steps K]
 
 Default workload (the headline line): batch 1, k = 2 drafts (3 verified positions), one
 sliding-window attention layer (8 query / 2 KV heads, head dim 256, window 1024) over a paged
@@ -17,6 +18,10 @@ Drafter stand-in: the drafter shares the target's vocab table (the serving guide
 table: the input embedding table is shared), so its distribution q is the lm-head call applied
 to the target hidden state plus N(0, sigma^2) noise; each step's drafts are drawn from q by the
 accept call with k = 0.  Both are prepared before timing.
+
+`--sweep-k KMAX` instead times the step at k = 0..KMAX drafts (k = 0: plain decoding) and
+prints one JSON line with the step time per k, the tokens per step (from the per-position
+acceptance measured at KMAX), verified tokens/s per k, and the k the telemetry picks.
 
 Prints one JSON line: verified tokens/s (accepted drafts + the correction/bonus token per
 sequence per step), the step's HBM GB/s for the algorithmic bytes (KV read + lm-head table), a
@@ -147,6 +152,10 @@ def prepare(w, device, torch, sv, gen, noise_sigma):
     for s in range(nsets):
         qs = [gen.queries(w, li, device, step=s) for li in range(len(w.layers))]
         x = gen.hidden_states(w, device, step=s)
+        if k == 0:                                           # plain decoding: no drafter
+            sets.append(dict(q=qs, x=x, qd=None, table=tables[s * B:(s + 1) * B],
+                             ctx=ctx_dev[s * B:(s + 1) * B]))
+            continue
         noise = gen.drafter_hidden_noise(w, device, step=s)
         xd = (x.float() + sigma * noise).to(x.dtype).view(B, K1, -1)[:, :k].reshape(B * k, -1)
         xd = xd.contiguous()
@@ -160,7 +169,7 @@ def prepare(w, device, torch, sv, gen, noise_sigma):
         sets.append(dict(q=qs, x=x, qd=qd.view(B, k, -1),
                          table=tables[s * B:(s + 1) * B], ctx=ctx_dev[s * B:(s + 1) * B]))
     torch.cuda.synchronize(device)
-    alpha_pos = torch.stack(alphas).mean(0).cpu().tolist()
+    alpha_pos = torch.stack(alphas).mean(0).cpu().tolist() if k else []
     return dict(pools=pools, W=W, temps=temps, sets=sets, P=P, ctx=ctx1, nsets=nsets,
                 max_pages=table_all.shape[1], alpha_pos=alpha_pos)
 
@@ -269,6 +278,161 @@ def adjacent_calls(w, inp, lib, sv, gen, torch, device, sptr, dt, ws_attn, n_out
             "iterations": iters}
 
 
+def measure(w, steps, warmup, device):
+    """Prepare w's input sets and time `steps` verify steps after `warmup` untimed ones."""
+    import torch
+    import speculative_decoding_decode_amd as sv
+    from speculative_decoding_decode_amd import _lib
+    from speculative_decoding_decode_amd.telemetry import accept_stats
+    from workloads import gen, noise_sigma
+
+    B, k, K1, V, H = w.batch, w.k, w.k1, w.vocab, w.hidden
+    R = B * K1
+
+    log(f"[bench] preparing input sets for {w.name}")
+    inp = prepare(w, device, torch, sv, gen, noise_sigma)
+    nsets = inp["nsets"]
+    lib = _lib.load()
+    stream = torch.cuda.current_stream(device)
+    sptr = ctypes.c_void_p(stream.cuda_stream) if stream.cuda_stream else None
+    nsteps = warmup + steps
+    U = torch.from_numpy(np.stack([gen.uniforms(w, step=1000 + s) for s in range(nsteps)])).to(device)
+    # the drafter samples its drafts anew every step: d ~ q of that step's input set, drawn by
+    # the accept call with k = 0 (plain sampling) before timing
+    Ud = torch.from_numpy(gen.rng(w, gen.STREAM_DRAFT, 0).random((nsteps, B * k, 1),
+                                                                 dtype=np.float32)).to(device)
+    drafts = torch.empty((nsteps, B, k), dtype=torch.int32, device=device)
+    for i in range(nsteps if k else 0):
+        qs = inp["sets"][i % nsets]["qd"]
+        _, tok = sv.accept(None, None, qs.view(B * k, 1, V), Ud[i])
+        drafts[i].copy_(tok[:, 0].view(B, k))
+    torch.cuda.synchronize(device)
+    n_out = torch.empty((nsteps, B), dtype=torch.int32, device=device)
+    tok_out = torch.empty((nsteps, B, K1), dtype=torch.int32, device=device)
+    attn_out = [torch.empty((B, K1, L.hq, L.head_dim), dtype=torch.float32, device=device)
+                for L in w.layers]
+    probs = torch.empty((R, V), dtype=torch.float32, device=device)
+    ws_attn = torch.empty(max(sv.verify_attn_workspace_bytes(B, K1, L.hq, L.hkv, L.head_dim,
+                                                             inp["max_pages"], L.window)
+                              for L in w.layers), dtype=torch.uint8, device=device)
+    ws_lm = torch.empty(sv.lm_head_workspace_bytes(R, H, V), dtype=torch.uint8, device=device)
+    ws_acc = torch.empty(sv.accept_workspace_bytes(B, k, V), dtype=torch.uint8, device=device)
+    dt = sv.SPEC_BF16 if w.dtype == "bf16" else sv.SPEC_F32
+
+    # argument tuples of the C calls for every input set (pointers only)
+    calls = []
+    for s in inp["sets"]:
+        attn = []
+        for li, L in enumerate(w.layers):
+            kp, vp = inp["pools"][li]
+            attn.append((s["q"][li].data_ptr(), kp.data_ptr(), vp.data_ptr(), s["table"].data_ptr(),
+                         s["ctx"].data_ptr(), attn_out[li].data_ptr(), B, K1, L.hq, L.hkv,
+                         L.head_dim, w.page_size, inp["P"], inp["max_pages"], L.window,
+                         1.0 / math.sqrt(L.head_dim), dt, ws_attn.data_ptr(), ws_attn.numel(),
+                         sptr))
+        m = (s["x"].data_ptr(), inp["W"].data_ptr(), inp["temps"].data_ptr(), None,
+             probs.data_ptr(), R, H, V, dt, ws_lm.data_ptr(), ws_lm.numel(), sptr)
+        calls.append((attn, m, s["qd"].data_ptr() if k else None))
+
+    def step(i, ev=None, evi=0):
+        attn, m, q_ptr = calls[i % nsets]
+        for a in attn:
+            rc = lib.spec_verify_attn(*a)
+            if rc:
+                _lib.check("spec_verify_attn", rc)
+        if ev is not None:
+            lib.spec_profile_lm_head(ev.ev[evi], ev.ev[evi + 1])
+        rc = lib.spec_lm_head(*m)
+        if rc:
+            _lib.check("spec_lm_head", rc)
+        rc = lib.spec_accept(drafts[i].data_ptr() if k else None, q_ptr, probs.data_ptr(), U[i].data_ptr(),
+                             n_out[i].data_ptr(), tok_out[i].data_ptr(), B, k, V,
+                             ws_acc.data_ptr(), ws_acc.numel(), sptr)
+        if rc:
+            _lib.check("spec_accept", rc)
+
+    log(f"[bench] warmup {warmup} steps ({nsets} input sets)")
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize(device)
+
+    K = steps
+    nsamp = (K + SAMPLE_EVERY - 1) // SAMPLE_EVERY
+    ev_lm = HipEvents(2 * nsamp)
+    ev_tot = HipEvents(2)
+    log(f"[bench] timing {K} steps (contraction bracketed on every {SAMPLE_EVERY}th step)")
+    torch.cuda.synchronize(device)
+    t0 = time.perf_counter()
+    ev_tot.record(0, sptr)
+    for j in range(K):
+        if j % SAMPLE_EVERY == 0:
+            step(warmup + j, ev_lm, 2 * (j // SAMPLE_EVERY))
+        else:
+            step(warmup + j)
+    ev_tot.record(1, sptr)
+    torch.cuda.synchronize(device)
+    t1 = time.perf_counter()
+    wall = t1 - t0
+
+    lm_ms = np.array([ev_lm.ms(2 * i, 2 * i + 1) for i in range(nsamp)])
+    gpu_total_ms = ev_tot.ms(0, 1)
+    ev_lm.close()
+    ev_tot.close()
+    n_all = n_out[warmup:].cpu().numpy()
+    tok_all = tok_out[warmup:].cpu().numpy()
+    assert ((tok_all >= -1) & (tok_all < V)).all()
+    emitted = int(np.sum(n_all + 1))
+    stats = accept_stats(n_all, k)
+    value = emitted / wall
+    kv_bytes, table_bytes = algorithmic_bytes(w, inp["ctx"])
+    step_bytes = kv_bytes + table_bytes
+    ms_per_step = wall * 1e3 / K
+    lm_avg_ms = float(lm_ms.mean())
+    achieved = table_bytes / (lm_avg_ms * 1e-3) / 1e9
+    traffic_bytes = profiled_traffic(w.name)
+    traffic = None if traffic_bytes is None else round(traffic_bytes / (lm_avg_ms * 1e-3) / 1e9, 1)
+    step_gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
+    log(f"[bench] gpu {gpu_total_ms * 1e3 / K:.1f} us/step; lm-head contraction "
+        f"{lm_avg_ms * 1e3:.1f} us = {achieved:.0f} GB/s; wall {ms_per_step * 1e3:.1f} us/step; "
+        f"acceptance pos {stats.per_position}")
+
+    return dict(inp=inp, lib=lib, sptr=sptr, dt=dt, ws_attn=ws_attn, n_out=n_out, wall=wall,
+                value=value, ms_per_step=ms_per_step, lm_avg_ms=lm_avg_ms, achieved=achieved,
+                traffic=traffic, traffic_bytes=traffic_bytes, step_gbs=step_gbs,
+                step_bytes=step_bytes, table_bytes=table_bytes, gpu_total_ms=gpu_total_ms,
+                stats=stats, nsamp=nsamp, nsets=nsets)
+
+
+def sweep_k(w, kmax, steps, warmup, device):
+    """The workload's verify step at k = 0..kmax drafts (plain decoding at k = 0): measured step
+    time and tokens per step at every k, the verified tokens per second they give, and the k
+    the telemetry picks (highest throughput; where the tokens per step plateau)."""
+    from speculative_decoding_decode_amd.telemetry import choose_k, mal_from_positions
+    us, mal, pos = {}, {}, {}
+    for k in range(kmax + 1):
+        wk = dataclasses.replace(w, k=k)
+        log(f"[bench] sweep: k = {k}")
+        r = measure(wk, steps, warmup, device)
+        us[k] = r["ms_per_step"] * 1e3
+        mal[k] = r["stats"].mean_accepted_length
+        pos[k] = [round(a, 4) for a in r["stats"].per_position]
+        del r
+    # tokens per step at every k from the per-position rates of the k = kmax run (one set of
+    # draws, so the curve is not perturbed by each run's own sampling noise)
+    derived = {k: mal_from_positions(pos[kmax], k) for k in range(kmax + 1)}
+    c = choose_k(derived, {k: v * 1e-6 for k, v in us.items()})
+    print(json.dumps({
+        "metric": f"verify step vs k, {w.description}",
+        "unit": "verified tokens/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "config": {"workload": w.name, "k": list(range(kmax + 1))},
+        "us_per_step": [round(us[k], 2) for k in range(kmax + 1)],
+        "tokens_per_step": [round(derived[k], 4) for k in range(kmax + 1)],   # per sequence
+        "tokens_per_step_measured_at_k": [round(mal[k], 4) for k in range(kmax + 1)],
+        "verified_tokens_per_s": [round(w.batch * c.tokens_per_second[k], 1) for k in range(kmax + 1)],
+        "acceptance_per_position_at_kmax": pos[kmax],
+        "best_k": c.best_k, "plateau_k": c.plateau_k}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -276,6 +440,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sweep-k", type=int, default=None, metavar="KMAX",
+                    help="time the workload's verify step at k = 0..KMAX drafts and print the "
+                         "tokens-per-step curve, throughput per k and the chosen k (one JSON line)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy 10 times (the reference kernel that "
                          "scales rocprofv3 FETCH_SIZE / WRITE_SIZE counters to bytes)")
@@ -308,114 +475,16 @@ def main():
     torch.cuda.set_device(device)
     w = WORKLOADS[args.workload]
     B, k, K1, V, H = w.batch, w.k, w.k1, w.vocab, w.hidden
-    R = B * K1
-
-    log(f"[bench] preparing input sets for {w.name}")
-    inp = prepare(w, device, torch, sv, gen, noise_sigma)
-    nsets = inp["nsets"]
-    lib = _lib.load()
-    stream = torch.cuda.current_stream(device)
-    sptr = ctypes.c_void_p(stream.cuda_stream) if stream.cuda_stream else None
-    nsteps = args.warmup + args.steps
-    U = torch.from_numpy(np.stack([gen.uniforms(w, step=1000 + s) for s in range(nsteps)])).to(device)
-    # the drafter samples its drafts anew every step: d ~ q of that step's input set, drawn by
-    # the accept call with k = 0 (plain sampling) before timing
-    Ud = torch.from_numpy(gen.rng(w, gen.STREAM_DRAFT, 0).random((nsteps, B * k, 1),
-                                                                 dtype=np.float32)).to(device)
-    drafts = torch.empty((nsteps, B, k), dtype=torch.int32, device=device)
-    for i in range(nsteps):
-        qs = inp["sets"][i % nsets]["qd"]
-        _, tok = sv.accept(None, None, qs.view(B * k, 1, V), Ud[i])
-        drafts[i].copy_(tok[:, 0].view(B, k))
-    torch.cuda.synchronize(device)
-    n_out = torch.empty((nsteps, B), dtype=torch.int32, device=device)
-    tok_out = torch.empty((nsteps, B, K1), dtype=torch.int32, device=device)
-    attn_out = [torch.empty((B, K1, L.hq, L.head_dim), dtype=torch.float32, device=device)
-                for L in w.layers]
-    probs = torch.empty((R, V), dtype=torch.float32, device=device)
-    ws_attn = torch.empty(max(sv.verify_attn_workspace_bytes(B, K1, L.hq, L.hkv, L.head_dim,
-                                                             inp["max_pages"], L.window)
-                              for L in w.layers), dtype=torch.uint8, device=device)
-    ws_lm = torch.empty(sv.lm_head_workspace_bytes(R, H, V), dtype=torch.uint8, device=device)
-    ws_acc = torch.empty(sv.accept_workspace_bytes(B, k, V), dtype=torch.uint8, device=device)
-    dt = sv.SPEC_BF16 if w.dtype == "bf16" else sv.SPEC_F32
-
-    # argument tuples of the C calls for every input set (pointers only)
-    calls = []
-    for s in inp["sets"]:
-        attn = []
-        for li, L in enumerate(w.layers):
-            kp, vp = inp["pools"][li]
-            attn.append((s["q"][li].data_ptr(), kp.data_ptr(), vp.data_ptr(), s["table"].data_ptr(),
-                         s["ctx"].data_ptr(), attn_out[li].data_ptr(), B, K1, L.hq, L.hkv,
-                         L.head_dim, w.page_size, inp["P"], inp["max_pages"], L.window,
-                         1.0 / math.sqrt(L.head_dim), dt, ws_attn.data_ptr(), ws_attn.numel(),
-                         sptr))
-        m = (s["x"].data_ptr(), inp["W"].data_ptr(), inp["temps"].data_ptr(), None,
-             probs.data_ptr(), R, H, V, dt, ws_lm.data_ptr(), ws_lm.numel(), sptr)
-        calls.append((attn, m, s["qd"].data_ptr()))
-
-    def step(i, ev=None, evi=0):
-        attn, m, q_ptr = calls[i % nsets]
-        for a in attn:
-            rc = lib.spec_verify_attn(*a)
-            if rc:
-                _lib.check("spec_verify_attn", rc)
-        if ev is not None:
-            lib.spec_profile_lm_head(ev.ev[evi], ev.ev[evi + 1])
-        rc = lib.spec_lm_head(*m)
-        if rc:
-            _lib.check("spec_lm_head", rc)
-        rc = lib.spec_accept(drafts[i].data_ptr(), q_ptr, probs.data_ptr(), U[i].data_ptr(),
-                             n_out[i].data_ptr(), tok_out[i].data_ptr(), B, k, V,
-                             ws_acc.data_ptr(), ws_acc.numel(), sptr)
-        if rc:
-            _lib.check("spec_accept", rc)
-
-    log(f"[bench] warmup {args.warmup} steps ({nsets} input sets)")
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize(device)
-
+    if args.sweep_k is not None:
+        sweep_k(w, args.sweep_k, args.steps, args.warmup, device)
+        return
+    r = measure(w, args.steps, args.warmup, device)
+    inp, lib, sptr, dt, ws_attn, n_out = r["inp"], r["lib"], r["sptr"], r["dt"], r["ws_attn"], r["n_out"]
+    value, ms_per_step, lm_avg_ms, achieved = r["value"], r["ms_per_step"], r["lm_avg_ms"], r["achieved"]
+    traffic, traffic_bytes, step_gbs = r["traffic"], r["traffic_bytes"], r["step_gbs"]
+    step_bytes, table_bytes, gpu_total_ms, stats = r["step_bytes"], r["table_bytes"], r["gpu_total_ms"], r["stats"]
+    nsamp, nsets = r["nsamp"], r["nsets"]
     K = args.steps
-    nsamp = (K + SAMPLE_EVERY - 1) // SAMPLE_EVERY
-    ev_lm = HipEvents(2 * nsamp)
-    ev_tot = HipEvents(2)
-    log(f"[bench] timing {K} steps (contraction bracketed on every {SAMPLE_EVERY}th step)")
-    torch.cuda.synchronize(device)
-    t0 = time.perf_counter()
-    ev_tot.record(0, sptr)
-    for j in range(K):
-        if j % SAMPLE_EVERY == 0:
-            step(args.warmup + j, ev_lm, 2 * (j // SAMPLE_EVERY))
-        else:
-            step(args.warmup + j)
-    ev_tot.record(1, sptr)
-    torch.cuda.synchronize(device)
-    t1 = time.perf_counter()
-    wall = t1 - t0
-
-    lm_ms = np.array([ev_lm.ms(2 * i, 2 * i + 1) for i in range(nsamp)])
-    gpu_total_ms = ev_tot.ms(0, 1)
-    ev_lm.close()
-    ev_tot.close()
-    n_all = n_out[args.warmup:].cpu().numpy()
-    tok_all = tok_out[args.warmup:].cpu().numpy()
-    assert ((tok_all >= -1) & (tok_all < V)).all()
-    emitted = int(np.sum(n_all + 1))
-    stats = accept_stats(n_all, k)
-    value = emitted / wall
-    kv_bytes, table_bytes = algorithmic_bytes(w, inp["ctx"])
-    step_bytes = kv_bytes + table_bytes
-    ms_per_step = wall * 1e3 / K
-    lm_avg_ms = float(lm_ms.mean())
-    achieved = table_bytes / (lm_avg_ms * 1e-3) / 1e9
-    traffic_bytes = profiled_traffic(w.name)
-    traffic = None if traffic_bytes is None else round(traffic_bytes / (lm_avg_ms * 1e-3) / 1e9, 1)
-    step_gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
-    log(f"[bench] gpu {gpu_total_ms * 1e3 / K:.1f} us/step; lm-head contraction "
-        f"{lm_avg_ms * 1e3:.1f} us = {achieved:.0f} GB/s; wall {ms_per_step * 1e3:.1f} us/step; "
-        f"acceptance pos {stats.per_position}")
 
     adjacent = adjacent_calls(w, inp, lib, sv, gen, torch, device, sptr, dt, ws_attn, n_out,
                               args.warmup)

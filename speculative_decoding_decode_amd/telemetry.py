@@ -11,6 +11,10 @@ measurements of section 2):
                         (unconditional); pos0 about 47%, pos1 about 24%; pos1 below 15% while
                         pos0 is normal means k should drop to 1
   net TPOT/ITL gain     measured outside this module
+
+k tuning (the guide's operating loop: raise k while the tokens per step still grow, and the
+G4 result that k = 2 was optimal with k >= 3 wasted, section 2): choose_k combines the
+tokens-per-step curve with the measured verify-step time at every k.
 """
 from __future__ import annotations
 
@@ -59,3 +63,37 @@ def expected_tokens_per_step(per_position_acceptance: float, k: int) -> float:
     previous ones): 1 + a + ... + a^k."""
     a = float(per_position_acceptance)
     return float(sum(a ** i for i in range(k + 1)))
+
+
+def mal_from_positions(per_position, k: int) -> float:
+    """Tokens per verify step at k drafts from unconditional per-position acceptance rates
+    P(n > i) measured with at least k drafts: 1 + sum over i < k.  (Whether position i is
+    accepted does not depend on the drafts after it, so rates measured at a larger k hold.)"""
+    if k > len(per_position):
+        raise ValueError(f"rates for {len(per_position)} positions, k = {k}")
+    return 1.0 + float(sum(per_position[:k]))
+
+
+@dataclass
+class KChoice:
+    best_k: int                   # highest verified tokens per second
+    plateau_k: int                # smallest k after which one more draft adds < min_gain tokens
+    tokens_per_step: dict
+    tokens_per_second: dict
+
+
+def choose_k(tokens_per_step: dict, step_seconds: dict, min_gain: float = 0.05) -> KChoice:
+    """Pick k from the tokens-per-step curve and the verify-step time at each k (both keyed
+    by k; k = 0 is plain decoding).  best_k maximises tokens per second (ties: smaller k);
+    plateau_k is the first k whose next draft adds less than min_gain tokens per step."""
+    ks = sorted(set(tokens_per_step) & set(step_seconds))
+    if not ks:
+        raise ValueError("no k with both a tokens-per-step value and a step time")
+    tps = {k: tokens_per_step[k] / step_seconds[k] for k in ks}
+    best = max(ks, key=lambda k: (tps[k], -k))
+    plateau = ks[-1]
+    for a, b in zip(ks, ks[1:]):
+        if tokens_per_step[b] - tokens_per_step[a] < min_gain:
+            plateau = a
+            break
+    return KChoice(best, plateau, {k: tokens_per_step[k] for k in ks}, tps)
