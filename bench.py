@@ -220,8 +220,9 @@ def adjacent_calls(w, inp, lib, sv, gen, torch, device, sptr, dt, ws_attn, n_out
                    iters=200):
     """The calls on either side of the verify step, timed after it with HIP events on the
     same stream and pools: KV append of the K1 verified positions for every layer plus the
-    commit, and the drafter's cross-attention (one query per sequence and draft step, K1 = 1,
-    over the committed context of the same pools), k draft steps per verify step."""
+    commit, the drafter's cross-attention (one query per sequence and draft step, K1 = 1, over
+    the committed context of the same pools), k draft steps per verify step, and the accept
+    step with its uniforms read from an array or drawn in the kernels."""
     from speculative_decoding_decode_amd import _lib
     B, k, K1 = w.batch, w.k, w.k1
     esz = 2 if w.dtype == "bf16" else 4
@@ -261,10 +262,38 @@ def adjacent_calls(w, inp, lib, sv, gen, torch, device, sptr, dt, ws_attn, n_out
                 if rc:
                     _lib.check("spec_verify_attn", rc)
     ev.record(2, sptr)
+    # the accept step with uniforms read from an array vs drawn in the kernels (Philox)
+    probs = torch.empty((B * K1, w.vocab), dtype=torch.float32, device=device)
+    _, probs = sv.lm_head(s0["x"], inp["W"], inp["temps"], probs=probs)
+    pk = probs.view(B, K1, w.vocab)
+    qd = s0["qd"] if k else None
+    dr0 = torch.zeros((B, k), dtype=torch.int32, device=device)
+    u0 = torch.from_numpy(gen.uniforms(w, step=0)).to(device)
+    ws_acc = torch.empty(sv.accept_workspace_bytes(B, k, w.vocab), dtype=torch.uint8, device=device)
+    n_acc = torch.empty((B,), dtype=torch.int32, device=device)
+    tok = torch.empty((B, K1), dtype=torch.int32, device=device)
+    torch.cuda.synchronize(device)
+    a_args = (dr0.data_ptr() if k else None, qd.data_ptr() if k else None, pk.data_ptr())
+    a_tail = (n_acc.data_ptr(), tok.data_ptr(), B, k, w.vocab, ws_acc.data_ptr(), ws_acc.numel(),
+              sptr)
+    ev2 = HipEvents(3)
+    ev2.record(0, sptr)
+    for it in range(iters):
+        rc = lib.spec_accept(*a_args, u0.data_ptr(), *a_tail)
+        if rc:
+            _lib.check("spec_accept", rc)
+    ev2.record(1, sptr)
+    for it in range(iters):
+        rc = lib.spec_accept_philox(*a_args, 0x5EED, it, None, *a_tail)
+        if rc:
+            _lib.check("spec_accept_philox", rc)
+    ev2.record(2, sptr)
     torch.cuda.synchronize(device)
     kv_us = ev.ms(0, 1) * 1e3 / iters
     dr_us = ev.ms(1, 2) * 1e3 / (iters * max(k, 1))
+    acc_us, acc_ph_us = ev2.ms(0, 1) * 1e3 / iters, ev2.ms(1, 2) * 1e3 / iters
     ev.close()
+    ev2.close()
     # algorithmic bytes: append reads and writes K1 rows of K and V per layer and sequence
     app_bytes = sum(2 * 2 * B * K1 * L.hkv * L.head_dim * esz for L in w.layers)
     ctx_committed = [int(c) - K1 for c in inp["ctx"]]
@@ -275,6 +304,8 @@ def adjacent_calls(w, inp, lib, sv, gen, torch, device, sptr, dt, ws_attn, n_out
             "drafter_xattn_us_per_draft_step": round(dr_us, 2),
             "drafter_xattn_kv_bytes_per_draft_step": dr_bytes,
             "drafter_xattn_gbs": round(dr_bytes / (dr_us * 1e-6) / 1e9, 1),
+            "accept_array_uniforms_us": round(acc_us, 2),
+            "accept_philox_uniforms_us": round(acc_ph_us, 2),
             "iterations": iters}
 
 

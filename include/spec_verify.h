@@ -150,6 +150,25 @@ int spec_accept(const int32_t *draft, const float *q, const float *p, const floa
                 void *workspace, size_t workspace_bytes, void *stream);
 
 /* ------------------------------------------------------------------------------------------
+ * (iii) with the uniforms drawn on the GPU: the same accept / reject and draw as spec_accept,
+ * with u[b][i] generated in the kernels by the counter-based generator Philox4x32-10 (Salmon,
+ * Moraes, Dror, Shaw, "Parallel Random Numbers: As Easy as 1, 2, 3", SC'11) instead of read
+ * from an array, so a decode loop needs no host-side random numbers:
+ *
+ *   u[b][i] = (word (i mod 4) of Philox4x32-10 at counter (i div 4, b, offset mod 2^32,
+ *              offset div 2^32) with key (seed mod 2^32, seed div 2^32)) >> 8, times 2^-24.
+ *
+ * A caller advances `offset` (e.g. by one per verify step) to get fresh draws under one seed.
+ * uniforms_out [B, K1] fp32, if not NULL, receives the values used; given those values
+ * spec_accept returns the same n_accepted and tokens.  Other arguments, workspace (the size
+ * spec_accept_workspace returns) and errors as for spec_accept.
+ * ---------------------------------------------------------------------------------------- */
+int spec_accept_philox(const int32_t *draft, const float *q, const float *p, uint64_t seed,
+                       uint64_t offset, float *uniforms_out, int32_t *n_accepted,
+                       int32_t *tokens, int B, int k, int V, void *workspace,
+                       size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------------------------------
  * KV-cache bookkeeping around the verify step.  Drafts from the first rejected one on are
  * discarded and the target generates the token there (butteryoon "Gemma 4 MTP 서빙 가이드
  * 해설", section 4 accept/reject step; llm-wiki "Gemma 4 MTP ...", section "투기적 디코딩의

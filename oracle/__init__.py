@@ -31,3 +31,4 @@ from .attention import verify_attention, visible_range  # noqa: F401
 from .lm_head import logits, probabilities  # noqa: F401
 from .accept import (accept_mask, first_rejection, integer_weights, sample_index,  # noqa: F401
                      verify_accept, FIXED_BITS, UNIFORM_BITS)
+from .philox import philox4x32_10, uniforms as philox_uniforms  # noqa: F401

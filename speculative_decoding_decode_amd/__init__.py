@@ -7,6 +7,7 @@ torch only provides device memory and the current stream:
     verify_attn(q, k_pool, v_pool, page_table, ctx_lens, window, ...)   -> out [B, K1, Hq, D]
     lm_head(hidden, weight, temperature, ...)                            -> (logits | None, p)
     accept(draft, q, p, uniforms, ...)                                   -> (n_accepted, tokens)
+    accept_philox(draft, q, p, seed, offset, ...)                        -> (n_accepted, tokens, u)
 
 Workspaces are allocated once per device and size class and reused (calls on one stream are
 ordered, so reuse is safe; concurrent streams should pass their own `workspace`).
@@ -188,6 +189,38 @@ def accept(draft, q, p, uniforms, n_accepted=None, tokens=None, workspace=None, 
         ws.data_ptr(), ws.numel(), _stream_ptr(dev, stream))
     _lib.check("spec_accept", rc)
     return n_accepted, tokens
+
+
+def accept_philox(draft, q, p, seed: int, offset: int, return_uniforms: bool = False,
+                  n_accepted=None, tokens=None, workspace=None, stream=None):
+    """accept() with the uniforms drawn on the GPU by Philox4x32-10 (seed, offset); returns
+    (n_accepted [B], tokens [B, k+1], uniforms [B, k+1] or None)."""
+    torch = _torch()
+    dev = p.device
+    _need(p, "p", torch.float32, dev)
+    B, K1, V = p.shape
+    k = K1 - 1
+    if k > 0:
+        _need(draft, "draft", torch.int32, dev)
+        _need(q, "q", torch.float32, dev)
+        if tuple(draft.shape) != (B, k) or tuple(q.shape) != (B, k, V):
+            raise ValueError("draft must be [B, k] and q [B, k, V] with p [B, k+1, V]")
+    if not (0 <= seed < 2 ** 64 and 0 <= offset < 2 ** 64):
+        raise ValueError("seed and offset are unsigned 64-bit integers")
+    if n_accepted is None:
+        n_accepted = torch.empty((B,), dtype=torch.int32, device=dev)
+    if tokens is None:
+        tokens = torch.empty((B, K1), dtype=torch.int32, device=dev)
+    _need(n_accepted, "n_accepted", torch.int32, dev)
+    _need(tokens, "tokens", torch.int32, dev)
+    u = torch.empty((B, K1), dtype=torch.float32, device=dev) if return_uniforms else None
+    ws = _workspace("accept", dev, accept_workspace_bytes(B, k, V), workspace)
+    rc = _lib.load().spec_accept_philox(
+        draft.data_ptr() if k > 0 else None, q.data_ptr() if k > 0 else None, p.data_ptr(),
+        int(seed), int(offset), u.data_ptr() if u is not None else None, n_accepted.data_ptr(),
+        tokens.data_ptr(), B, k, V, ws.data_ptr(), ws.numel(), _stream_ptr(dev, stream))
+    _lib.check("spec_accept_philox", rc)
+    return n_accepted, tokens, u
 
 
 def kv_append(k_new, v_new, k_pool, v_pool, page_table, ctx_lens, stream=None):

@@ -11,7 +11,7 @@ import os
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libspecverify.so")
 
 c_int, c_float, c_size_t, c_void_p = ctypes.c_int, ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p
-c_char_p = ctypes.c_char_p
+c_char_p, c_uint64 = ctypes.c_char_p, ctypes.c_uint64
 
 # name -> (restype, argtypes), in the order of include/spec_verify.h
 SIGNATURES = {
@@ -25,6 +25,8 @@ SIGNATURES = {
     "spec_profile_lm_head": (c_int, [c_void_p, c_void_p]),
     "spec_accept_workspace": (c_size_t, [c_int] * 3),
     "spec_accept": (c_int, [c_void_p] * 6 + [c_int] * 3 + [c_void_p, c_size_t, c_void_p]),
+    "spec_accept_philox": (c_int, [c_void_p] * 3 + [c_uint64, c_uint64] + [c_void_p] * 3
+                           + [c_int] * 3 + [c_void_p, c_size_t, c_void_p]),
     "spec_kv_append": (c_int, [c_void_p] * 6 + [c_int] * 7 + [c_int, c_void_p]),
     "spec_kv_commit": (c_int, [c_void_p, c_void_p, c_int, c_int, c_void_p]),
 }

@@ -38,17 +38,51 @@ __device__ __forceinline__ uint64_t fixed_weight(float x) {
 }
 
 // Number of accepted drafts of sequence b.  Must be called by a whole wave (lanes 0..63).
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As Easy as 1, 2, 3",
+// SC'11): ten rounds of two 32 x 32 -> 64-bit products with the published multipliers, the
+// new counter (hi(p2) ^ c1 ^ k0, lo(p2), hi(p0) ^ c3 ^ k1, lo(p0)), and the key bumped by the
+// published Weyl constants between rounds.
+__device__ __forceinline__ void philox4x32_10(uint32_t (&c)[4], uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r) { k0 += 0x9E3779B9u; k1 += 0xBB67AE85u; }
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c[0];
+    const uint64_t p2 = (uint64_t)0xCD9E8D57u * c[2];
+    const uint32_t n0 = (uint32_t)(p2 >> 32) ^ c[1] ^ k0, n1 = (uint32_t)p2;
+    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c[3] ^ k1, n3 = (uint32_t)p0;
+    c[0] = n0; c[1] = n1; c[2] = n2; c[3] = n3;
+  }
+}
+
+// The verify step's u[b][i]: word i mod 4 of Philox4x32-10 at counter (i div 4, b, offset) and
+// key seed, top 24 bits, as a multiple of 2^-24.
+__device__ __forceinline__ float philox_uniform(uint64_t seed, uint64_t offset, int b, int i) {
+  uint32_t c[4] = {(uint32_t)(i >> 2), (uint32_t)b, (uint32_t)offset, (uint32_t)(offset >> 32)};
+  philox4x32_10(c, (uint32_t)seed, (uint32_t)(seed >> 32));
+  const uint32_t w = (i & 3) == 0 ? c[0] : (i & 3) == 1 ? c[1] : (i & 3) == 2 ? c[2] : c[3];
+  return (float)(w >> 8) * (1.0f / 16777216.0f);
+}
+
+// Where a kernel takes u[b][i] from: the caller's array, or the generator.
+struct UniformSource {
+  const float *u;          // [B, K1], or null: Philox with seed / offset
+  uint64_t seed, offset;
+  __device__ __forceinline__ float operator()(int b, int K1, int i) const {
+    return u != nullptr ? u[(size_t)b * K1 + i] : philox_uniform(seed, offset, b, i);
+  }
+};
+
+// ul: this lane's uniform (lane i < k tests draft i).
 __device__ int accepted_count(const int32_t *__restrict__ draft, const float *__restrict__ q,
-                              const float *__restrict__ p, const float *__restrict__ u,
-                              int b, int k, int V, int lane) {
+                              const float *__restrict__ p, float ul, int b, int k, int V,
+                              int lane) {
   bool ok = false;
   if (lane < k) {
     const int d = draft[(size_t)b * k + lane];
     if (d >= 0 && d < V) {
       const double qd = q[((size_t)b * k + lane) * V + d];
       const double pd = p[((size_t)b * (k + 1) + lane) * V + d];
-      const double ud = u[(size_t)b * (k + 1) + lane];
-      ok = ud * qd < pd;
+      ok = (double)ul * qd < pd;
     }
   }
   const uint64_t acc = __ballot(ok);
@@ -105,13 +139,14 @@ __device__ __forceinline__ uint64_t residual(uint64_t P, uint64_t Q) { return P 
 template <int E>
 __global__ __launch_bounds__(kThreads) void accept_chunks(
     const int32_t *__restrict__ draft, const float *__restrict__ q, const float *__restrict__ p,
-    const float *__restrict__ u, uint64_t *__restrict__ wsum, uint64_t *__restrict__ psum,
+    UniformSource us, uint64_t *__restrict__ wsum, uint64_t *__restrict__ psum,
     int32_t *__restrict__ nbuf, int k, int V, int nchunks) {
   __shared__ int n_sh;
   __shared__ uint64_t red[kThreads];
   const int b = blockIdx.y, c = blockIdx.x, tid = threadIdx.x;
   if (tid < spec::kWave) {
-    const int n = accepted_count(draft, q, p, u, b, k, V, tid);
+    const float ul = tid < k ? us(b, k + 1, tid) : 0.f;
+    const int n = accepted_count(draft, q, p, ul, b, k, V, tid);
     if (tid == 0) n_sh = n;
   }
   __syncthreads();
@@ -142,9 +177,10 @@ __global__ __launch_bounds__(kThreads) void accept_chunks(
 template <int E>
 __global__ __launch_bounds__(kThreads) void accept_draw(
     const int32_t *__restrict__ draft, const float *__restrict__ q, const float *__restrict__ p,
-    const float *__restrict__ u, const uint64_t *__restrict__ wsum,
+    UniformSource us, const uint64_t *__restrict__ wsum,
     const uint64_t *__restrict__ psum, const int32_t *__restrict__ nbuf,
-    int32_t *__restrict__ n_out, int32_t *__restrict__ tokens, int k, int V, int nchunks) {
+    int32_t *__restrict__ n_out, int32_t *__restrict__ tokens, float *__restrict__ u_out, int k,
+    int V, int nchunks) {
   __shared__ uint64_t sh[kThreads];
   __shared__ int found_sh;
   __shared__ uint64_t base_sh;
@@ -154,7 +190,8 @@ __global__ __launch_bounds__(kThreads) void accept_draw(
   const int n = nbuf[b];
   const uint64_t cw = tid < nchunks ? wsum[(size_t)b * nchunks + tid] : 0ull;
   const uint64_t cp = tid < nchunks ? psum[(size_t)b * nchunks + tid] : 0ull;
-  const float uk = u[(size_t)b * K1 + k];
+  const float uk = us(b, K1, k);
+  if (u_out != nullptr && tid < K1) u_out[(size_t)b * K1 + tid] = us(b, K1, tid);
   const int dtok = tid < k ? draft[(size_t)b * k + tid] : -1;
 
   const uint64_t wtot = block_sum(cw, sh);
@@ -244,15 +281,46 @@ AcceptPlan plan(int B, int V) {
 
 template <int E>
 int launch(const AcceptPlan &pl, const int32_t *draft, const float *q, const float *p,
-           const float *uniforms, int32_t *n_accepted, int32_t *tokens, int B, int k, int V,
-           uint64_t *wsum, uint64_t *psum, int32_t *nbuf, hipStream_t st) {
+           UniformSource us, float *u_out, int32_t *n_accepted, int32_t *tokens, int B, int k,
+           int V, uint64_t *wsum, uint64_t *psum, int32_t *nbuf, hipStream_t st) {
   hipLaunchKernelGGL((accept_chunks<E>), dim3(pl.nchunks, B), dim3(kThreads), 0, st, draft, q,
-                     p, uniforms, wsum, psum, nbuf, k, V, pl.nchunks);
+                     p, us, wsum, psum, nbuf, k, V, pl.nchunks);
   int rc = spec::launched("accept_chunks");
   if (rc != SPEC_OK) return rc;
-  hipLaunchKernelGGL((accept_draw<E>), dim3(B), dim3(kThreads), 0, st, draft, q, p, uniforms,
-                     wsum, psum, nbuf, n_accepted, tokens, k, V, pl.nchunks);
+  hipLaunchKernelGGL((accept_draw<E>), dim3(B), dim3(kThreads), 0, st, draft, q, p, us,
+                     wsum, psum, nbuf, n_accepted, tokens, u_out, k, V, pl.nchunks);
   return spec::launched("accept_draw");
+}
+
+// Shared by spec_accept and spec_accept_philox: checks, workspace, launch.
+int accept_run(const char *who, const int32_t *draft, const float *q, const float *p,
+               UniformSource us, float *u_out, int32_t *n_accepted, int32_t *tokens, int B,
+               int k, int V, void *workspace, size_t workspace_bytes, void *stream) {
+  SPEC_REQUIRE(B > 0 && V > 0 && k >= 0, SPEC_EINVAL, "%s: B=%d k=%d V=%d out of range", who, B,
+               k, V);
+  SPEC_REQUIRE(k <= kMaxK, SPEC_EUNSUPPORTED, "%s: k=%d exceeds %d (one wave per sequence)", who,
+               k, kMaxK);
+  SPEC_REQUIRE((long)V <= (long)kMaxE * kThreads * kThreads, SPEC_EUNSUPPORTED,
+               "%s: V=%d exceeds %ld", who, V, (long)kMaxE * kThreads * kThreads);
+  SPEC_REQUIRE(p && n_accepted && tokens && (k == 0 || (draft && q)), SPEC_EINVAL,
+               "%s: null pointer argument", who);
+  const AcceptPlan pl = plan(B, V);
+  SPEC_REQUIRE(workspace != nullptr && workspace_bytes >= pl.bytes, SPEC_EWORKSPACE,
+               "%s: workspace of %zu bytes needed, %zu given", who, pl.bytes, workspace_bytes);
+  char *ws = static_cast<char *>(workspace);
+  uint64_t *wsum = reinterpret_cast<uint64_t *>(ws + pl.off_w);
+  uint64_t *psum = reinterpret_cast<uint64_t *>(ws + pl.off_p);
+  int32_t *nbuf = reinterpret_cast<int32_t *>(ws + pl.off_n);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  switch (pl.E) {
+    case 1: return launch<1>(pl, draft, q, p, us, u_out, n_accepted, tokens, B, k, V, wsum, psum, nbuf, st);
+    case 2: return launch<2>(pl, draft, q, p, us, u_out, n_accepted, tokens, B, k, V, wsum, psum, nbuf, st);
+    case 4: return launch<4>(pl, draft, q, p, us, u_out, n_accepted, tokens, B, k, V, wsum, psum, nbuf, st);
+    case 8: return launch<8>(pl, draft, q, p, us, u_out, n_accepted, tokens, B, k, V, wsum, psum, nbuf, st);
+    case 16: return launch<16>(pl, draft, q, p, us, u_out, n_accepted, tokens, B, k, V, wsum, psum, nbuf, st);
+    case 32: return launch<32>(pl, draft, q, p, us, u_out, n_accepted, tokens, B, k, V, wsum, psum, nbuf, st);
+    default: return launch<64>(pl, draft, q, p, us, u_out, n_accepted, tokens, B, k, V, wsum, psum, nbuf, st);
+  }
 }
 
 }  // namespace
@@ -269,29 +337,17 @@ extern "C" int spec_accept(const int32_t *draft, const float *q, const float *p,
                            const float *uniforms, int32_t *n_accepted, int32_t *tokens, int B,
                            int k, int V, void *workspace, size_t workspace_bytes, void *stream) {
   spec::clear_error();
-  SPEC_REQUIRE(B > 0 && V > 0 && k >= 0, SPEC_EINVAL,
-               "spec_accept: B=%d k=%d V=%d out of range", B, k, V);
-  SPEC_REQUIRE(k <= kMaxK, SPEC_EUNSUPPORTED, "spec_accept: k=%d exceeds %d (one wave per sequence)",
-               k, kMaxK);
-  SPEC_REQUIRE((long)V <= (long)kMaxE * kThreads * kThreads, SPEC_EUNSUPPORTED,
-               "spec_accept: V=%d exceeds %ld", V, (long)kMaxE * kThreads * kThreads);
-  SPEC_REQUIRE(p && uniforms && n_accepted && tokens && (k == 0 || (draft && q)), SPEC_EINVAL,
-               "spec_accept: null pointer argument");
-  const AcceptPlan pl = plan(B, V);
-  SPEC_REQUIRE(workspace != nullptr && workspace_bytes >= pl.bytes, SPEC_EWORKSPACE,
-               "spec_accept: workspace of %zu bytes needed, %zu given", pl.bytes, workspace_bytes);
-  char *ws = static_cast<char *>(workspace);
-  uint64_t *wsum = reinterpret_cast<uint64_t *>(ws + pl.off_w);
-  uint64_t *psum = reinterpret_cast<uint64_t *>(ws + pl.off_p);
-  int32_t *nbuf = reinterpret_cast<int32_t *>(ws + pl.off_n);
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  switch (pl.E) {
-    case 1: return launch<1>(pl, draft, q, p, uniforms, n_accepted, tokens, B, k, V, wsum, psum, nbuf, st);
-    case 2: return launch<2>(pl, draft, q, p, uniforms, n_accepted, tokens, B, k, V, wsum, psum, nbuf, st);
-    case 4: return launch<4>(pl, draft, q, p, uniforms, n_accepted, tokens, B, k, V, wsum, psum, nbuf, st);
-    case 8: return launch<8>(pl, draft, q, p, uniforms, n_accepted, tokens, B, k, V, wsum, psum, nbuf, st);
-    case 16: return launch<16>(pl, draft, q, p, uniforms, n_accepted, tokens, B, k, V, wsum, psum, nbuf, st);
-    case 32: return launch<32>(pl, draft, q, p, uniforms, n_accepted, tokens, B, k, V, wsum, psum, nbuf, st);
-    default: return launch<64>(pl, draft, q, p, uniforms, n_accepted, tokens, B, k, V, wsum, psum, nbuf, st);
-  }
+  SPEC_REQUIRE(uniforms != nullptr, SPEC_EINVAL, "spec_accept: null pointer argument");
+  return accept_run("spec_accept", draft, q, p, UniformSource{uniforms, 0, 0}, nullptr,
+                    n_accepted, tokens, B, k, V, workspace, workspace_bytes, stream);
+}
+
+extern "C" int spec_accept_philox(const int32_t *draft, const float *q, const float *p,
+                                  uint64_t seed, uint64_t offset, float *uniforms_out,
+                                  int32_t *n_accepted, int32_t *tokens, int B, int k, int V,
+                                  void *workspace, size_t workspace_bytes, void *stream) {
+  spec::clear_error();
+  return accept_run("spec_accept_philox", draft, q, p, UniformSource{nullptr, seed, offset},
+                    uniforms_out, n_accepted, tokens, B, k, V, workspace, workspace_bytes,
+                    stream);
 }
