@@ -19,8 +19,8 @@
 // MFMAs (keys x rows tile), the online softmax runs in registers with wavefront shuffles, and
 // the value update is a second MFMA per 16 columns of the head dim.  For every unit it touches
 // the workgroup writes one partial (max, sum, unnormalised output); a second kernel merges the
-// partials of each output row with log-sum-exp weights, one wave per row.  All exponentials
-// are base 2 with log2(e) folded into the query scale.
+// partials of each output row with log-sum-exp weights, one workgroup per row.  All
+// exponentials are base 2 with log2(e) folded into the query scale.
 #include <math.h>
 
 #include "common.hpp"

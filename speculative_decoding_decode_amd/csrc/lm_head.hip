@@ -7,21 +7,23 @@
 // from memory (same guide, introduction).  At R = 3..96 rows the kernel is a stream over the
 // V x H table: every table element is read once from HBM and used R times.
 //
-// Design (gfx950).  Two contraction kernels share one softmax finalize:
-//  * R <= 8 rows (batch-1 verification): a bandwidth-bound GEMV.  Each wave owns 64 table rows
-//    and streams them in order as a flat sequence of (row pair, 1 KB column chunk) items: every
-//    load instruction of the wave reads 1 KB of contiguous table with a nontemporal load (the
-//    table is used once per call), items are prefetched one tile ahead, the hidden rows sit in
-//    LDS and one LDS read of them serves two table rows; products accumulate in fp32 with
-//    v_dot2_f32_bf16 (fp32 tables: FMAs) and a wave reduction gives each row's logits.
-//    Measured on MI355X this streams the table at about 6.9 TB/s, against 4.8 TB/s for the
-//    MFMA tiling below (whose loads touch 16 rows x 64 B each).
-//  * R > 8 rows: MFMA.  One workgroup = 4 waves = 256 vocab rows; each wave owns 4 tiles of 16
-//    vocab rows and NT tiles of 16 hidden rows; table fragments are the A operand of
+// Design (gfx950).  Three contraction kernels share one softmax finalize:
+//  * R <= 3 rows over rows of at most 5 KB (batch-1 verification): a bandwidth-bound GEMV
+//    with the hidden rows in registers.  Each wave owns 64 table rows and streams them two at
+//    a time; every load instruction reads 1 KB of contiguous table with a nontemporal load (the
+//    table is used once per call) and products accumulate in fp32 with v_dot2_f32_bf16 (fp32
+//    tables: FMAs); a wave reduction gives each row's logit.
+//  * other R <= 8: the same stream as (row pair, 1 KB column chunk) items with the hidden rows
+//    in LDS (one LDS read serves two table rows); when the hidden rows fill LDS the loads run a
+//    tile ahead of the compute.  On MI355X these GEMVs stream the table at about 6.5 TB/s in the
+//    verify step, against about 4.8 TB/s for the MFMA tiling below (whose loads touch 16 rows x
+//    64 B each).
+//  * R > 8 rows: MFMA.  One workgroup = 16 waves = 256 vocab rows; each wave owns one tile of
+//    16 vocab rows and NT tiles of 16 hidden rows; table fragments are the A operand of
 //    v_mfma_f32_16x16x32_bf16 (fp32: four v_mfma_f32_16x16x4_f32), hidden rows are staged per
 //    chunk of the hidden dimension in LDS.
-//  * Both epilogues turn a 256-row vocab block into per-block softmax statistics (max, sum of
-//    exp, first argmax) and write exp(logit - block max) into p; lm_head_finalize merges the
+//  * Every epilogue turns a 256-row vocab block into per-block softmax statistics (max, sum of
+//    exp, first argmax) and writes exp(logit - block max) into p; lm_head_finalize merges the
 //    statistics of all blocks and rescales p in place (or writes the greedy one-hot rows).
 #include <math.h>
 
