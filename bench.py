@@ -409,6 +409,26 @@ def measure(w, steps, warmup, device):
     gpu_total_ms = ev_tot.ms(0, 1)
     ev_lm.close()
     ev_tot.close()
+
+    # distribution of single-step times: a separate pass with every step between two HIP
+    # events, less the median time of an empty event pair (the events' own cost)
+    P = min(200, steps)
+    ev_d = HipEvents(2 * P + 2 * 32)
+    for j in range(32):
+        ev_d.record(2 * P + 2 * j, sptr)
+        ev_d.record(2 * P + 2 * j + 1, sptr)
+    for j in range(P):
+        ev_d.record(2 * j, sptr)
+        step(warmup + j)
+        ev_d.record(2 * j + 1, sptr)
+    torch.cuda.synchronize(device)
+    floor_ms = float(np.median([ev_d.ms(2 * P + 2 * j, 2 * P + 2 * j + 1) for j in range(32)]))
+    step_us = np.array([ev_d.ms(2 * j, 2 * j + 1) - floor_ms for j in range(P)]) * 1e3
+    ev_d.close()
+    pct = {"p10": round(float(np.percentile(step_us, 10)), 2),
+           "p50": round(float(np.percentile(step_us, 50)), 2),
+           "p90": round(float(np.percentile(step_us, 90)), 2),
+           "steps": P, "event_pair_floor_us": round(floor_ms * 1e3, 2)}
     n_all = n_out[warmup:].cpu().numpy()
     tok_all = tok_out[warmup:].cpu().numpy()
     assert ((tok_all >= -1) & (tok_all < V)).all()
@@ -431,7 +451,7 @@ def measure(w, steps, warmup, device):
                 value=value, ms_per_step=ms_per_step, lm_avg_ms=lm_avg_ms, achieved=achieved,
                 traffic=traffic, traffic_bytes=traffic_bytes, step_gbs=step_gbs,
                 step_bytes=step_bytes, table_bytes=table_bytes, gpu_total_ms=gpu_total_ms,
-                stats=stats, nsamp=nsamp, nsets=nsets)
+                stats=stats, nsamp=nsamp, nsets=nsets, step_us_percentiles=pct)
 
 
 def sweep_k(w, kmax, steps, warmup, device):
@@ -514,7 +534,7 @@ def main():
     value, ms_per_step, lm_avg_ms, achieved = r["value"], r["ms_per_step"], r["lm_avg_ms"], r["achieved"]
     traffic, traffic_bytes, step_gbs = r["traffic"], r["traffic_bytes"], r["step_gbs"]
     step_bytes, table_bytes, gpu_total_ms, stats = r["step_bytes"], r["table_bytes"], r["gpu_total_ms"], r["stats"]
-    nsamp, nsets = r["nsamp"], r["nsets"]
+    nsamp, nsets, pct = r["nsamp"], r["nsets"], r["step_us_percentiles"]
     K = args.steps
 
     adjacent = adjacent_calls(w, inp, lib, sv, gen, torch, device, sptr, dt, ws_attn, n_out,
@@ -551,6 +571,7 @@ def main():
         "step_frac_peak": round(step_gbs / HBM_PEAK_GBS, 4),
         "step_algorithmic_bytes": step_bytes,
         "gpu_event_ms_per_step": round(gpu_total_ms / K, 5),
+        "step_us_percentiles": pct,
         "tokens_per_step": round(stats.mean_accepted_length, 4),
         "acceptance_per_position": [round(a, 4) for a in stats.per_position],
         "closed_form_acceptance_per_position": [round(a, 4) for a in inp["alpha_pos"]],
