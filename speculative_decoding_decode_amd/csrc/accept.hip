@@ -90,29 +90,45 @@ __device__ int accepted_count(const int32_t *__restrict__ draft, const float *__
   return min(k, __builtin_ctzll(~acc));
 }
 
-template <typename U>
-__device__ U block_sum(U v, U *sh) {
-  const int tid = threadIdx.x;
-  sh[tid] = v;
-  __syncthreads();
-  for (int s = kThreads / 2; s > 0; s >>= 1) {
-    if (tid < s) sh[tid] += sh[tid + s];
-    __syncthreads();
-  }
-  const U r = sh[0];
-  __syncthreads();
-  return r;
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
+  const uint32_t lo = __shfl_xor((uint32_t)v, m), hi = __shfl_xor((uint32_t)(v >> 32), m);
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ uint64_t shfl_up_u64(uint64_t v, int d) {
+  const uint32_t lo = __shfl_up((uint32_t)v, d), hi = __shfl_up((uint32_t)(v >> 32), d);
+  return ((uint64_t)hi << 32) | lo;
 }
 
-// In-place inclusive scan of sh[0..kThreads) (uint64), Hillis-Steele.
-__device__ void block_inclusive_scan(uint64_t *sh) {
-  const int tid = threadIdx.x;
-  for (int off = 1; off < kThreads; off <<= 1) {
-    const uint64_t add = tid >= off ? sh[tid - off] : 0ull;
-    __syncthreads();
-    sh[tid] += add;
-    __syncthreads();
+// Sum over the workgroup (integers: exact in any order); sh holds kThreads / 64 entries.
+__device__ __forceinline__ uint64_t wg_sum(uint64_t v, uint64_t *sh) {
+  const int lane = threadIdx.x & (spec::kWave - 1), wave = threadIdx.x / spec::kWave;
+#pragma unroll
+  for (int m = spec::kWave / 2; m > 0; m >>= 1) v += shfl_xor_u64(v, m);
+  if (lane == 0) sh[wave] = v;
+  __syncthreads();
+  uint64_t t = 0;
+#pragma unroll
+  for (int x = 0; x < kThreads / spec::kWave; ++x) t += sh[x];
+  __syncthreads();
+  return t;
+}
+
+// Inclusive prefix sum over the workgroup in thread order; sh holds kThreads / 64 entries.
+__device__ __forceinline__ uint64_t wg_inclusive_scan(uint64_t v, uint64_t *sh) {
+  const int lane = threadIdx.x & (spec::kWave - 1), wave = threadIdx.x / spec::kWave;
+#pragma unroll
+  for (int d = 1; d < spec::kWave; d <<= 1) {
+    const uint64_t o = shfl_up_u64(v, d);
+    if (lane >= d) v += o;
   }
+  if (lane == spec::kWave - 1) sh[wave] = v;
+  __syncthreads();
+  uint64_t base = 0;
+#pragma unroll
+  for (int x = 0; x < kThreads / spec::kWave; ++x)
+    if (x < wave) base += sh[x];
+  __syncthreads();
+  return v + base;
 }
 
 // Chunk c of a sequence's row: elements [c * chunk, (c + 1) * chunk), chunk = kThreads * E;
@@ -135,26 +151,27 @@ __device__ __forceinline__ void load_run(const float *__restrict__ row, int j0, 
 __device__ __forceinline__ uint64_t residual(uint64_t P, uint64_t Q) { return P > Q ? P - Q : 0ull; }
 
 // Grid: (nchunks, B).  Round trips: drafts, then p/q at the drafts (n), then the chunk of the
-// row the draw uses.
+// row the draw uses.  (Loading every row's chunk with the drafts, to pick row n from registers,
+// measured slower at batch 1: the extra bytes cost more than the round trip.)
 template <int E>
 __global__ __launch_bounds__(kThreads) void accept_chunks(
     const int32_t *__restrict__ draft, const float *__restrict__ q, const float *__restrict__ p,
     UniformSource us, uint64_t *__restrict__ wsum, uint64_t *__restrict__ psum,
     int32_t *__restrict__ nbuf, int k, int V, int nchunks) {
   __shared__ int n_sh;
-  __shared__ uint64_t red[kThreads];
+  __shared__ uint64_t red[kThreads / spec::kWave];
   const int b = blockIdx.y, c = blockIdx.x, tid = threadIdx.x;
+  const int K1 = k + 1;
   if (tid < spec::kWave) {
-    const float ul = tid < k ? us(b, k + 1, tid) : 0.f;
+    const float ul = tid < k ? us(b, K1, tid) : 0.f;
     const int n = accepted_count(draft, q, p, ul, b, k, V, tid);
     if (tid == 0) n_sh = n;
   }
   __syncthreads();
   const int n = n_sh;
-  const float *prow = p + ((size_t)b * (k + 1) + n) * V;
   const int j0 = c * kThreads * E + tid * E;
   float pv[E], qv[E];
-  load_run<E>(prow, j0, V, pv);
+  load_run<E>(p + ((size_t)b * K1 + n) * V, j0, V, pv);
   const bool corr = n < k;
   if (corr) load_run<E>(q + ((size_t)b * k + n) * V, j0, V, qv);
   uint64_t sp = 0, sw = 0;
@@ -164,8 +181,8 @@ __global__ __launch_bounds__(kThreads) void accept_chunks(
     sp += P;
     if (corr) sw += residual(P, fixed_weight(qv[e]));
   }
-  sp = block_sum(sp, red);
-  if (corr) sw = block_sum(sw, red);
+  sp = wg_sum(sp, red);
+  if (corr) sw = wg_sum(sw, red);
   if (tid == 0) {
     wsum[(size_t)b * nchunks + c] = corr ? sw : sp;
     psum[(size_t)b * nchunks + c] = sp;
@@ -181,11 +198,12 @@ __global__ __launch_bounds__(kThreads) void accept_draw(
     const uint64_t *__restrict__ psum, const int32_t *__restrict__ nbuf,
     int32_t *__restrict__ n_out, int32_t *__restrict__ tokens, float *__restrict__ u_out, int k,
     int V, int nchunks) {
-  __shared__ uint64_t sh[kThreads];
+  __shared__ uint64_t red[kThreads / spec::kWave];
   __shared__ int found_sh;
   __shared__ uint64_t base_sh;
   const int b = blockIdx.x, tid = threadIdx.x;
   const int K1 = k + 1;
+  if (tid == 0) found_sh = 0;   // ordered before the scans by the barriers inside wg_sum
   // everything independent of n at once (nchunks <= kThreads)
   const int n = nbuf[b];
   const uint64_t cw = tid < nchunks ? wsum[(size_t)b * nchunks + tid] : 0ull;
@@ -194,10 +212,10 @@ __global__ __launch_bounds__(kThreads) void accept_draw(
   if (u_out != nullptr && tid < K1) u_out[(size_t)b * K1 + tid] = us(b, K1, tid);
   const int dtok = tid < k ? draft[(size_t)b * k + tid] : -1;
 
-  const uint64_t wtot = block_sum(cw, sh);
+  const uint64_t wtot = wg_sum(cw, red);
   const bool fallback = n < k && wtot == 0ull;   // every correction weight 0: draw from p
   const uint64_t mine = fallback ? cp : cw;
-  const uint64_t total = fallback ? block_sum(cp, sh) : wtot;
+  const uint64_t total = fallback ? wg_sum(cp, red) : wtot;
 
   int y = 0;
   if (total > 0ull) {
@@ -207,13 +225,8 @@ __global__ __launch_bounds__(kThreads) void accept_draw(
     const uint64_t t = (m * total) >> kUniformBits;   // m < 2^24, total < 2^40
 
     // 1) the chunk whose running sum first exceeds t (one chunk per thread)
-    sh[tid] = mine;
-    __syncthreads();
-    block_inclusive_scan(sh);
-    if (tid == 0) found_sh = -1;
-    __syncthreads();
     {
-      const uint64_t incl = sh[tid], excl = incl - mine;
+      const uint64_t incl = wg_inclusive_scan(mine, red), excl = incl - mine;
       if (excl <= t && t < incl) { found_sh = tid; base_sh = excl; }
     }
     __syncthreads();
@@ -233,14 +246,8 @@ __global__ __launch_bounds__(kThreads) void accept_draw(
       w[e] = corr ? residual(P, fixed_weight(qv[e])) : P;
       wsum_t += w[e];
     }
-    __syncthreads();
-    sh[tid] = wsum_t;
-    __syncthreads();
-    block_inclusive_scan(sh);
-    if (tid == 0) found_sh = -1;
-    __syncthreads();
     {
-      const uint64_t incl = sh[tid], excl = incl - wsum_t;
+      const uint64_t incl = wg_inclusive_scan(wsum_t, red), excl = incl - wsum_t;
       if (excl <= t2 && t2 < incl) {
         uint64_t run = excl;
 #pragma unroll
