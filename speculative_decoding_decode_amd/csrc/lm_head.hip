@@ -16,12 +16,11 @@
 //  * other R <= 8: the same stream as (row pair, 1 KB column chunk) items with the hidden rows
 //    in LDS (one LDS read serves two table rows); when the hidden rows fill LDS the loads run a
 //    tile ahead of the compute.  On MI355X these GEMVs stream the table at about 6.5 TB/s in the
-//    verify step, against about 4.8 TB/s for the MFMA tiling below (whose loads touch 16 rows x
-//    64 B each).
-//  * R > 8 rows: MFMA.  One workgroup = 16 waves = 256 vocab rows; each wave owns one tile of
-//    16 vocab rows and NT tiles of 16 hidden rows; table fragments are the A operand of
-//    v_mfma_f32_16x16x32_bf16 (fp32: four v_mfma_f32_16x16x4_f32), hidden rows are staged per
-//    chunk of the hidden dimension in LDS.
+//    verify step.
+//  * R > 8 rows: MFMA (v_mfma_f32_16x16x32_bf16; fp32 tables: four v_mfma_f32_16x16x4_f32).
+//    One workgroup = 256 vocab rows against up to 96 hidden rows; chunks of 128 bytes of
+//    every row are loaded with 128-byte contiguous runs per row, transposed into MFMA fragments
+//    through bank-conflict-free LDS tiles, with a ring of four chunks in flight.
 //  * Every epilogue turns a 256-row vocab block into per-block softmax statistics (max, sum of
 //    exp, first argmax) and writes exp(logit - block max) into p; lm_head_finalize merges the
 //    statistics of all blocks and rescales p in place (or writes the greedy one-hot rows).
@@ -35,11 +34,11 @@ namespace {
 using spec::kWave;
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));   // one 16-byte slot
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;          // 4
 constexpr int kBlockRows = 256;                   // vocab rows per statistics block
-constexpr int kDepth = 4;                         // K-steps per load batch
 constexpr int kFinChunk = 4096;                   // vocab entries per finalize workgroup
 constexpr long kFinWideWGs = 2048;                // above this many, 4x larger chunks
 constexpr size_t kGemvMaxLds = 128 * 1024;        // hidden rows resident in LDS (GEMV path)
@@ -50,7 +49,7 @@ template <typename T> struct Mma;
 template <> struct Mma<uint16_t> {  // bf16 table: one 16x16x32 MFMA per 16-byte fragment
   static constexpr int kEPL = 8;             // elements per lane per fragment
   static constexpr int kStep = 4 * kEPL;     // hidden elements per K-step (4 lane groups)
-  __device__ static __forceinline__ f32x4_t run(uint4 a, uint4 b, f32x4_t c) {
+  __device__ static __forceinline__ f32x4_t run(u32x4_t a, u32x4_t b, f32x4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                    __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
   }
@@ -58,212 +57,273 @@ template <> struct Mma<uint16_t> {  // bf16 table: one 16x16x32 MFMA per 16-byte
 template <> struct Mma<float> {  // fp32 table: four 16x16x4 MFMAs, one per fragment element
   static constexpr int kEPL = 4;
   static constexpr int kStep = 4 * kEPL;
-  __device__ static __forceinline__ f32x4_t run(uint4 a, uint4 b, f32x4_t c) {
-    c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.x), __uint_as_float(b.x), c, 0, 0, 0);
-    c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.y), __uint_as_float(b.y), c, 0, 0, 0);
-    c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.z), __uint_as_float(b.z), c, 0, 0, 0);
-    c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.w), __uint_as_float(b.w), c, 0, 0, 0);
+  __device__ static __forceinline__ f32x4_t run(u32x4_t a, u32x4_t b, f32x4_t c) {
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[0]), __uint_as_float(b[0]), c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[1]), __uint_as_float(b[1]), c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[2]), __uint_as_float(b[2]), c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[3]), __uint_as_float(b[3]), c, 0, 0, 0);
     return c;
   }
 };
+
+__device__ __forceinline__ u32x4_t load_stream(const void *p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
+}
 
 __device__ __forceinline__ bool better(float m, int a, float om, int oa) {
   return om > m || (om == m && oa < a);
 }
 
 // Contraction + per-block statistics for R > 8 rows.  Grid: (ceil(V / 256), ceil(R / (16 NT))),
-// 1024 threads: 16 waves, each owning one 16-row vocab tile of the 256-row block and all NT
-// tiles of 16 hidden rows.  MFMA operand roles: A = 16 vocab rows x K of the table (straight
-// from HBM into registers, one batch of kDepth K-steps ahead), B = K x 16 hidden rows from an
-// LDS chunk of kChunkSteps K-steps; chunks are double-buffered and the next chunk's global
-// loads are issued a whole chunk ahead, so neither the table stream nor the chunk staging ever
-// drains the other.  Accumulator lane l holds logits of vocab rows 4*(l/16) + e (e = 0..3) of
-// the wave's tile for hidden row n*16 + l % 16.
-constexpr int kMmaThreads = 1024;
-constexpr int kMmaWaves = kMmaThreads / kWave;     // 16
-constexpr int kChunkSteps = 2 * kDepth;           // K-steps per staged hidden-row chunk
-constexpr int kMaxNT = 6;                         // hidden-row tiles per pass
+// NT = 2 NH tiles of 16 hidden rows per pass; 512 threads, two waves per SIMD.  The workgroup
+// walks the hidden dimension in chunks of 128 bytes of every row; wave w multiplies vocab rows
+// blk * 256 + 64 (w % 4) + [0, 64) (four MFMA tiles, the A operand) by hidden-row tiles
+// NH (w / 4) + [0, NH) (the B operand).
+//  * Loads: 8 consecutive lanes read the 128 bytes of one row, so each instruction takes 128
+//    contiguous bytes from each of 8 rows (table loads nontemporal: it is read once per call).
+//    MFMA fragments need one row per lane instead, so every chunk (256 table rows and NT * 16
+//    hidden rows) passes through LDS: rows 128 bytes apart with the 16-byte slots
+//    XOR-swizzled by row pair, so neither the writes nor the fragment reads conflict on a bank.
+//  * Pipeline: the loads of kMmaRing chunks are in flight in a ring of registers (about 176 KB
+//    per CU, which the loaded memory latency needs).  Per chunk: one workgroup barrier, the
+//    multiplies of chunk c out of one LDS buffer, then chunk c + 1 (the oldest in the ring) is
+//    written to the other buffer and its ring slot refilled with chunk c + 1 + kMmaRing.
+//    Fetches past the last chunk read one shared address; slots past H are zeroed on both
+//    operands when they are written to LDS.
+// Accumulator lane l of tile (vt, n) holds the logits of vocab rows 16 vt + 4 (l / 16) + e
+// (e = 0..3) of the wave's 64 for hidden row 16 (NH (w / 4) + n) + l % 16.
+constexpr int kMmaThreads = 512;
+constexpr int kMmaWaves = kMmaThreads / kWave;                // 8
+constexpr int kMmaRowsW = 64;                                 // vocab rows per wave
+constexpr int kMmaVT = kMmaRowsW / 16;                        // 4 vocab tiles per wave
+constexpr int kMmaSlots = 8;                                  // 16-byte slots per row per chunk
+constexpr int kMmaWL = kBlockRows * kMmaSlots / kMmaThreads;  // 4 table loads per thread per chunk
+constexpr int kMmaWBuf = kBlockRows * kMmaSlots * 16;         // 32 KB: one chunk of the table
+constexpr int kMmaRing = 4;                                   // chunks in flight
+constexpr int kMaxNH = 3;                                     // hidden-row tiles per wave
+constexpr int kMaxNT = 2 * kMaxNH;                            // hidden-row tiles per pass
+constexpr int kMmaXBuf = kMaxNT * 16 * kMmaSlots * 16;        // 12 KB: one chunk of hidden rows
+constexpr size_t kMmaLds = 2 * (size_t)(kMmaWBuf + kMmaXBuf);
 
-template <typename T, int NT>
-__global__ __launch_bounds__(kMmaThreads) void lm_head_mfma(
+__device__ __forceinline__ u32x4_t mask16(u32x4_t v, bool keep) {
+  const uint32_t m = keep ? 0xffffffffu : 0u;
+  return u32x4_t{v[0] & m, v[1] & m, v[2] & m, v[3] & m};
+}
+
+// Byte offset of 16-byte slot `slot` of row `row` in a [rows][8 slots] LDS tile.
+__device__ __forceinline__ int swz(int row, int slot) { return row * 128 + ((slot ^ (row >> 1)) & 7) * 16; }
+
+template <typename T, int NH>
+__global__ __launch_bounds__(kMmaThreads, 1) void lm_head_mfma(
     const T *__restrict__ X, const T *__restrict__ W, const float *__restrict__ temp,
     float *__restrict__ logits, float *__restrict__ probs, float2 *__restrict__ stats,
     int *__restrict__ amax, int R, int H, int V) {
   using M = Mma<T>;
-  constexpr int KC = kChunkSteps * M::kStep;             // elements per chunk
-  constexpr int XSTR = KC + M::kEPL;                     // LDS row stride, 16-byte pad
-  constexpr int GPRC = KC / M::kEPL;                     // 16-byte groups per row per chunk
-  constexpr int XPT = (NT * 16 * GPRC + kMmaThreads - 1) / kMmaThreads;
+  constexpr int NT = 2 * NH;
+  constexpr int EPL = M::kEPL;                    // elements per 16-byte slot
+  constexpr int KC = kMmaSlots * EPL;             // elements per chunk (two MFMA K-steps)
+  constexpr int XS = NT * 16 * kMmaSlots;         // hidden-row slots per chunk
+  constexpr int XL = (XS + kMmaThreads - 1) / kMmaThreads;   // of them per thread
   extern __shared__ __align__(16) unsigned char smem[];
-  T *xs = reinterpret_cast<T *>(smem);                   // [2][NT*16][XSTR]
+  __shared__ float red_m[kMmaWaves][kMaxNH * 16], red_s[kMmaWaves][kMaxNH * 16];
+  __shared__ int red_i[kMmaWaves][kMaxNH * 16];
 
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-  const int lr = lane & 15, lq = lane >> 4;
+  const int vq = wave & 3, rh = wave >> 2;      // vocab quarter / hidden-row half
+  const int lr = lane & 15, lq = lane >> 4;     // fragment row / K group
+  const int ls = tid & 7;                       // load slot
   const int blk = blockIdx.x;
   const int r0 = blockIdx.y * NT * 16;
-  const int nrows = min(NT * 16, R - r0);
-  const int vrow0 = blk * kBlockRows + wave * 16;
-  const T *wrow = W + (size_t)min(vrow0 + lr, V - 1) * H + lq * M::kEPL;   // tail rows discarded
-  const int nks = (H + M::kStep - 1) / M::kStep;
-  const int nchunks = (nks + kChunkSteps - 1) / kChunkSteps;
+  const int vb = blk * kBlockRows;
+  const int vw = vb + vq * kMmaRowsW;
+  const int nch = (H + KC - 1) / KC;
+  unsigned char *wl = smem;                             // [2][256 rows][128 B]
+  unsigned char *xl = smem + 2 * (size_t)kMmaWBuf;      // [2][NT * 16 rows][128 B]
 
-  uint4 xr[XPT];
-  auto xload = [&](int c) {
+  struct Chunk {
+    u32x4_t w[kMmaWL];
+    u32x4_t x[XL];
+  };
+  auto fetch = [&](Chunk &ch, int c) __attribute__((always_inline)) {
+    const size_t live = c < nch ? ~(size_t)0 : 0;   // uniform; past the end: offset 0
+    const int kk = min(c * KC + ls * EPL, H - EPL);
 #pragma unroll
-    for (int x = 0; x < XPT; ++x) {
-      const int e = tid + x * kMmaThreads;
-      const int r = e / GPRC, g = e - r * GPRC;
-      const int k = c * KC + g * M::kEPL;
-      xr[x] = (r < nrows && k < H) ? *reinterpret_cast<const uint4 *>(X + (size_t)(r0 + r) * H + k)
-                                   : uint4{0u, 0u, 0u, 0u};
+    for (int i = 0; i < kMmaWL; ++i) {
+      const size_t off = (size_t)min(vb + (tid + i * kMmaThreads) / kMmaSlots, V - 1) * H + kk;
+      ch.w[i] = load_stream(W + (off & live));
+    }
+#pragma unroll
+    for (int j = 0; j < XL; ++j) {
+      const int e = min(tid + j * kMmaThreads, XS - 1);
+      const int row = min(r0 + e / kMmaSlots, R - 1);
+      const size_t off = (size_t)row * H + min(c * KC + (e % kMmaSlots) * EPL, H - EPL);
+      ch.x[j] = *reinterpret_cast<const u32x4_t *>(X + (off & live));
     }
   };
-  auto xstore = [&](int buf) {
-#pragma unroll
-    for (int x = 0; x < XPT; ++x) {
-      const int e = tid + x * kMmaThreads;
-      const int r = e / GPRC, g = e - r * GPRC;
-      if (r < NT * 16) *reinterpret_cast<uint4 *>(xs + (buf * NT * 16 + r) * XSTR + g * M::kEPL) = xr[x];
-    }
-  };
-  auto wload = [&](uint4(&a)[kDepth], int batch) {      // global batch index
-#pragma unroll
-    for (int d = 0; d < kDepth; ++d) {
-      const int ks = batch * kDepth + d;
-      const bool ok = ks < nks && ks * M::kStep + lq * M::kEPL < H;
-      a[d] = ok ? *reinterpret_cast<const uint4 *>(wrow + (size_t)ks * M::kStep) : uint4{0u, 0u, 0u, 0u};
-    }
-  };
-  f32x4_t acc[NT];
-#pragma unroll
-  for (int n = 0; n < NT; ++n) acc[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  auto compute = [&](const uint4(&a)[kDepth], int buf, int step0) {   // step0: local K-step
-#pragma unroll
-    for (int d = 0; d < kDepth; ++d) {
-      const int kl = (step0 + d) * M::kStep + lq * M::kEPL;
-#pragma unroll
-      for (int n = 0; n < NT; ++n) {
-        const int r = n * 16 + lr;
-        uint4 bv = {0u, 0u, 0u, 0u};
-        if (r < nrows) bv = *reinterpret_cast<const uint4 *>(xs + (buf * NT * 16 + r) * XSTR + kl);
-        acc[n] = M::run(a[d], bv, acc[n]);
-      }
-    }
-  };
-
-  xload(0);
-  xstore(0);
-  __syncthreads();
-  if (nchunks > 1) xload(1);
-  uint4 a0[kDepth], a1[kDepth];
-  wload(a0, 0);
-  for (int c = 0; c < nchunks; ++c) {
+  // chunk c (the oldest in the ring) into LDS buffer c & 1; slots past H become zero
+  auto stage = [&](const Chunk &ch, int c) __attribute__((always_inline)) {
     const int buf = c & 1;
-    wload(a1, 2 * c + 1);
-    compute(a0, buf, 0);
-    if (c + 1 < nchunks) wload(a0, 2 * c + 2);
-    compute(a1, buf, kDepth);
-    if (c + 1 < nchunks) {
-      xstore(buf ^ 1);
-      __syncthreads();
-      if (c + 2 < nchunks) xload(c + 2);
+    const bool in = c * KC + ls * EPL < H;
+#pragma unroll
+    for (int i = 0; i < kMmaWL; ++i)
+      *reinterpret_cast<u32x4_t *>(wl + buf * kMmaWBuf + swz((tid + i * kMmaThreads) / kMmaSlots, ls)) =
+          mask16(ch.w[i], in);
+#pragma unroll
+    for (int j = 0; j < XL; ++j) {
+      const int e = min(tid + j * kMmaThreads, XS - 1);   // duplicates write the same bytes
+      *reinterpret_cast<u32x4_t *>(xl + buf * kMmaXBuf + swz(e / kMmaSlots, e % kMmaSlots)) =
+          mask16(ch.x[j], c * KC + (e % kMmaSlots) * EPL < H);
+    }
+  };
+  f32x4_t acc[kMmaVT][NH];
+#pragma unroll
+  for (int vt = 0; vt < kMmaVT; ++vt)
+#pragma unroll
+    for (int n = 0; n < NH; ++n) acc[vt][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](int c) __attribute__((always_inline)) {
+    const int buf = c & 1;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      u32x4_t a[kMmaVT], bx[NH];
+#pragma unroll
+      for (int vt = 0; vt < kMmaVT; ++vt)
+        a[vt] = *reinterpret_cast<const u32x4_t *>(
+            wl + buf * kMmaWBuf + swz(vq * kMmaRowsW + vt * 16 + lr, s * 4 + lq));
+#pragma unroll
+      for (int n = 0; n < NH; ++n)
+        bx[n] = *reinterpret_cast<const u32x4_t *>(
+            xl + buf * kMmaXBuf + swz((rh * NH + n) * 16 + lr, s * 4 + lq));
+#pragma unroll
+      for (int vt = 0; vt < kMmaVT; ++vt)
+#pragma unroll
+        for (int n = 0; n < NH; ++n) acc[vt][n] = M::run(a[vt], bx[n], acc[vt][n]);
+    }
+  };
+
+  Chunk ring[kMmaRing];
+#pragma unroll
+  for (int q = 0; q < kMmaRing; ++q) fetch(ring[q], q);
+  stage(ring[0], 0);
+  fetch(ring[0], kMmaRing);
+  // Scheduling barriers keep each phase where it is written, so every wait leaves the younger
+  // chunks in flight.  Chunk counts that are not a multiple of kMmaRing end with multiplies of
+  // zeros (chunks past H are zero on both operands).
+  for (int c0 = 0; c0 < nch; c0 += kMmaRing) {
+#pragma unroll
+    for (int q = 0; q < kMmaRing; ++q) {
+      const int c = c0 + q;
+      __syncthreads();          // chunk c is in LDS; every wave is done with chunk c - 1
+      __builtin_amdgcn_sched_barrier(0);
+      compute(c);
+      __builtin_amdgcn_sched_barrier(0);
+      stage(ring[(q + 1) % kMmaRing], c + 1);
+      fetch(ring[(q + 1) % kMmaRing], c + 1 + kMmaRing);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 
-  // ---- epilogue: block max / first argmax, then sum of exp, per hidden row (LDS reuses xs)
-  __syncthreads();
-  float *red_m = reinterpret_cast<float *>(smem);               // [16 waves][NT*16]
-  float *red_s = red_m + kMmaWaves * NT * 16;
-  int *red_i = reinterpret_cast<int *>(red_s + kMmaWaves * NT * 16);
+  // ---- epilogue: block max / first argmax, then sum of exp, per hidden row.  Hidden row
+  // slot c = n * 16 + lr of the wave is row r0 + 16 (NH rh + n) + lr; the four vocab quarters
+  // (waves rh * 4 + q) are merged in quarter order.
 #pragma unroll
-  for (int n = 0; n < NT; ++n) {
+  for (int n = 0; n < NH; ++n) {
     float mx = -INFINITY;
     int ax = 0x7fffffff;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int v = vrow0 + lq * 4 + e;
-      const float z = acc[n][e];
-      if (v < V && z > mx) { mx = z; ax = v; }
-    }
+    for (int vt = 0; vt < kMmaVT; ++vt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {   // increasing v within the lane: the first maximum stays
+        const int v = vw + vt * 16 + lq * 4 + e;
+        const float z = acc[vt][n][e];
+        if (v < V && z > mx) { mx = z; ax = v; }
+      }
 #pragma unroll
     for (int off = 16; off < kWave; off <<= 1) {
       const float om = __shfl_xor(mx, off);
       const int oa = __shfl_xor(ax, off);
       if (better(mx, ax, om, oa)) { mx = om; ax = oa; }
     }
-    if (lq == 0) { red_m[wave * NT * 16 + n * 16 + lr] = mx; red_i[wave * NT * 16 + n * 16 + lr] = ax; }
+    if (lq == 0) { red_m[wave][n * 16 + lr] = mx; red_i[wave][n * 16 + lr] = ax; }
   }
   __syncthreads();
-  float cexp[NT];
-  bool live[NT];
+  float cexp[NH];
+  bool live[NH];
 #pragma unroll
-  for (int n = 0; n < NT; ++n) {
+  for (int n = 0; n < NH; ++n) {
     const int c = n * 16 + lr;
-    float m = red_m[c];
-    for (int w = 1; w < kMmaWaves; ++w) m = fmaxf(m, red_m[w * NT * 16 + c]);
-    const int r = r0 + c;
+    float m = red_m[rh * 4][c];
+#pragma unroll
+    for (int q = 1; q < 4; ++q) m = fmaxf(m, red_m[rh * 4 + q][c]);
+    const int r = r0 + (rh * NH + n) * 16 + lr;
     live[n] = r < R;
     const float tr = live[n] ? temp[r] : 1.f;
     cexp[n] = tr > 0.f ? kLog2e / tr : 0.f;   // 0: greedy row, p is written by the finalize
-    const int v0 = vrow0 + lq * 4;
-    if (live[n] && logits != nullptr) {
-      float *dst = logits + (size_t)r * V + v0;
-      if (v0 + 3 < V && (V & 3) == 0) {
-        *reinterpret_cast<float4 *>(dst) = make_float4(acc[n][0], acc[n][1], acc[n][2], acc[n][3]);
-      } else {
-        for (int e = 0; e < 4; ++e)
-          if (v0 + e < V) dst[e] = acc[n][e];
-      }
-    }
     float sacc = 0.f;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float ex = (v0 + e < V) ? exp2f((acc[n][e] - m) * cexp[n]) : 0.f;
-      acc[n][e] = ex;
-      sacc += ex;
+    for (int vt = 0; vt < kMmaVT; ++vt) {
+      const int v0 = vw + vt * 16 + lq * 4;
+      if (live[n] && logits != nullptr) {
+        float *dst = logits + (size_t)r * V + v0;
+        if (v0 + 3 < V && (V & 3) == 0) {
+          *reinterpret_cast<float4 *>(dst) =
+              make_float4(acc[vt][n][0], acc[vt][n][1], acc[vt][n][2], acc[vt][n][3]);
+        } else {
+          for (int e = 0; e < 4; ++e)
+            if (v0 + e < V) dst[e] = acc[vt][n][e];
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float ex = (v0 + e < V) ? exp2f((acc[vt][n][e] - m) * cexp[n]) : 0.f;
+        acc[vt][n][e] = ex;
+        sacc += ex;
+      }
     }
 #pragma unroll
     for (int off = 16; off < kWave; off <<= 1) sacc += __shfl_xor(sacc, off);
-    if (lq == 0) red_s[wave * NT * 16 + c] = sacc;
+    if (lq == 0) red_s[wave][c] = sacc;
   }
   __syncthreads();
-  if (wave == 0 && lq == 0) {
+  if (vq == 0 && lq == 0) {
 #pragma unroll
-    for (int n = 0; n < NT; ++n) {
-      const int c = n * 16 + lr, r = r0 + c;
+    for (int n = 0; n < NH; ++n) {
+      const int c = n * 16 + lr, r = r0 + (rh * NH + n) * 16 + lr;
       if (r >= R) continue;
-      float m = red_m[c];
-      int a = red_i[c];
-      float sum = red_s[c];
-      for (int w = 1; w < kMmaWaves; ++w) {
-        if (better(m, a, red_m[w * NT * 16 + c], red_i[w * NT * 16 + c])) {
-          m = red_m[w * NT * 16 + c];
-          a = red_i[w * NT * 16 + c];
+      float m = red_m[rh * 4][c];
+      int a = red_i[rh * 4][c];
+#pragma unroll
+      for (int q = 1; q < 4; ++q)
+        if (better(m, a, red_m[rh * 4 + q][c], red_i[rh * 4 + q][c])) {
+          m = red_m[rh * 4 + q][c];
+          a = red_i[rh * 4 + q][c];
         }
-        sum += red_s[w * NT * 16 + c];
-      }
+      const float sum = ((red_s[rh * 4][c] + red_s[rh * 4 + 1][c]) + red_s[rh * 4 + 2][c]) +
+                        red_s[rh * 4 + 3][c];
       stats[(size_t)blk * R + r] = make_float2(m, sum);
       amax[(size_t)blk * R + r] = a;
     }
   }
 #pragma unroll
-  for (int n = 0; n < NT; ++n) {
-    const int r = r0 + n * 16 + lr;
+  for (int n = 0; n < NH; ++n) {
+    const int r = r0 + (rh * NH + n) * 16 + lr;
     if (!live[n] || cexp[n] == 0.f) continue;
-    const int v0 = vrow0 + lq * 4;
-    float *dst = probs + (size_t)r * V + v0;
-    if (v0 + 3 < V && (V & 3) == 0) {
-      *reinterpret_cast<float4 *>(dst) = make_float4(acc[n][0], acc[n][1], acc[n][2], acc[n][3]);
-    } else {
-      for (int e = 0; e < 4; ++e)
-        if (v0 + e < V) dst[e] = acc[n][e];
+#pragma unroll
+    for (int vt = 0; vt < kMmaVT; ++vt) {
+      const int v0 = vw + vt * 16 + lq * 4;
+      float *dst = probs + (size_t)r * V + v0;
+      if (v0 + 3 < V && (V & 3) == 0) {
+        *reinterpret_cast<float4 *>(dst) =
+            make_float4(acc[vt][n][0], acc[vt][n][1], acc[vt][n][2], acc[vt][n][3]);
+      } else {
+        for (int e = 0; e < 4; ++e)
+          if (v0 + e < V) dst[e] = acc[vt][n][e];
+      }
     }
   }
 }
 
 // ------------------------------------------------------------------------- small-R GEMV path
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kGemvMaxR = 8;
 constexpr int kRowsPerWave = 64;     // one table row per lane in the epilogue
@@ -290,10 +350,6 @@ template <> struct Dot<float> {
     return s;
   }
 };
-
-__device__ __forceinline__ u32x4_t load_stream(const void *p) {
-  return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
-}
 
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
@@ -696,39 +752,30 @@ __global__ __launch_bounds__(kThreads) void lm_head_finalize(
   }
 }
 
-template <typename T, int NT>
-int launch_nt(const void *X, const void *W, const float *temp, float *logits, float *probs,
+template <typename T, int NH>
+int launch_nh(const void *X, const void *W, const float *temp, float *logits, float *probs,
               float2 *stats, int *amax, int R, int H, int V, hipStream_t st) {
-  using M = Mma<T>;
-  constexpr int KC = kChunkSteps * M::kStep;
-  const size_t xs_bytes = 2ull * NT * 16 * (KC + M::kEPL) * sizeof(T);
-  const size_t red_bytes = 3ull * kMmaWaves * NT * 16 * 4;
-  const size_t lds = xs_bytes > red_bytes ? xs_bytes : red_bytes;
   static bool attr_set = false;
-  if (!attr_set && lds > 64 * 1024) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void *>(&lm_head_mfma<T, NT>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
-      return spec::fail(SPEC_EHIP, "spec_lm_head: cannot reserve %zu bytes of LDS", lds);
+  if (!attr_set) {
+    if (hipFuncSetAttribute(reinterpret_cast<const void *>(&lm_head_mfma<T, NH>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMmaLds) != hipSuccess)
+      return spec::fail(SPEC_EHIP, "spec_lm_head: cannot reserve %zu bytes of LDS", kMmaLds);
     attr_set = true;
   }
-  const int nblk = spec::ceil_div(V, kBlockRows);
-  dim3 grid(nblk, spec::ceil_div(R, NT * 16));
-  hipLaunchKernelGGL((lm_head_mfma<T, NT>), grid, dim3(kMmaThreads), lds, st,
+  dim3 grid(spec::ceil_div(V, kBlockRows), spec::ceil_div(R, 2 * NH * 16));
+  hipLaunchKernelGGL((lm_head_mfma<T, NH>), grid, dim3(kMmaThreads), kMmaLds, st,
                      static_cast<const T *>(X), static_cast<const T *>(W), temp, logits, probs,
                      stats, amax, R, H, V);
   return spec::launched("lm_head_mfma");
 }
 
 template <typename T>
-int launch(int NT, const void *X, const void *W, const float *temp, float *logits, float *probs,
+int launch(int NH, const void *X, const void *W, const float *temp, float *logits, float *probs,
            float2 *stats, int *amax, int R, int H, int V, hipStream_t st) {
-  switch (NT) {
-    case 1: return launch_nt<T, 1>(X, W, temp, logits, probs, stats, amax, R, H, V, st);
-    case 2: return launch_nt<T, 2>(X, W, temp, logits, probs, stats, amax, R, H, V, st);
-    case 3: return launch_nt<T, 3>(X, W, temp, logits, probs, stats, amax, R, H, V, st);
-    case 4: return launch_nt<T, 4>(X, W, temp, logits, probs, stats, amax, R, H, V, st);
-    case 5: return launch_nt<T, 5>(X, W, temp, logits, probs, stats, amax, R, H, V, st);
-    default: return launch_nt<T, 6>(X, W, temp, logits, probs, stats, amax, R, H, V, st);
+  switch (NH) {
+    case 1: return launch_nh<T, 1>(X, W, temp, logits, probs, stats, amax, R, H, V, st);
+    case 2: return launch_nh<T, 2>(X, W, temp, logits, probs, stats, amax, R, H, V, st);
+    default: return launch_nh<T, 3>(X, W, temp, logits, probs, stats, amax, R, H, V, st);
   }
 }
 
@@ -785,9 +832,10 @@ int lm_head_check(const void *hidden, const void *weight, const float *temperatu
 int lm_head_contract(const void *hidden, const void *weight, const float *temperature,
                      float *logits, float *probs, float2 *stats, int *amax, int R, int H, int V,
                      spec_dtype dtype, hipStream_t st) {
-  // MFMA path: up to 6 tiles of 16 hidden rows per pass over the table (128 VGPRs per lane at
-  // 1024 threads); more rows take further passes.
-  const int NT = min(kMaxNT, spec::ceil_div(R, 16));
+  // MFMA path: 2 NH tiles of 16 hidden rows per pass over the table, NH <= 3 (each wave's
+  // accumulators and the ring of chunks in flight fill half a SIMD's registers); more rows
+  // take further passes.
+  const int NH = min(kMaxNH, spec::ceil_div(R, 32));
   hipEvent_t ev0 = g_prof_start, ev1 = g_prof_stop;
   g_prof_start = g_prof_stop = nullptr;
   if (ev0 != nullptr && hipEventRecord(ev0, st) != hipSuccess)
@@ -806,8 +854,8 @@ int lm_head_contract(const void *hidden, const void *weight, const float *temper
              : launch_gemv_r<float>(R, hidden, weight, temperature, logits, probs, stats, amax, H, V, st);
   else
     rc = dtype == SPEC_BF16
-             ? launch<uint16_t>(NT, hidden, weight, temperature, logits, probs, stats, amax, R, H, V, st)
-             : launch<float>(NT, hidden, weight, temperature, logits, probs, stats, amax, R, H, V, st);
+             ? launch<uint16_t>(NH, hidden, weight, temperature, logits, probs, stats, amax, R, H, V, st)
+             : launch<float>(NH, hidden, weight, temperature, logits, probs, stats, amax, R, H, V, st);
   if (rc != SPEC_OK) return rc;
   if (ev1 != nullptr && hipEventRecord(ev1, st) != hipSuccess)
     return spec::fail(SPEC_EHIP, "spec_lm_head: hipEventRecord(stop) failed");
