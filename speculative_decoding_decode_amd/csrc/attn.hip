@@ -67,14 +67,23 @@ struct AttnShape {
   static constexpr int kQPT = (kRowsWG * kGPR + kThreads - 1) / kThreads;
   static constexpr int kDT = D / 16;                     // 16-wide tiles of the head dim
   static constexpr int kDTW = kDT / kWaves;              // of them per wave
-  static constexpr size_t kLds = (size_t)(kRowsWG + 2 * kPage) * kStr * sizeof(T);
+  static constexpr size_t kTiles = (size_t)(kRowsWG + 2 * kPage) * kStr * sizeof(T);
   // Waves per SIMD the register budget is set for (one wave of each workgroup per SIMD): as
   // many workgroups as a CU's 160 KB of LDS holds, capped where the page buffers and output
   // tiles (growing with D * RT * element size) would no longer fit the registers.
-  static constexpr int kLdsWGs = (int)((160u * 1024u) / kLds);
   static constexpr int kRowBytes = D * RT * (int)sizeof(T);
   static constexpr int kRegCap = kRowBytes <= 512 ? 4 : kRowBytes <= 1024 ? 3 : kRowBytes <= 2048 ? 2 : 1;
-  static constexpr int kWavesPerEU = kLdsWGs < kRegCap ? kLdsWGs : kRegCap;
+  // Split scores: at D >= 256 each wave computes the scores over its quarter of the head dim
+  // and the four partial tiles are summed through LDS (kSplitBytes of scratch) instead of
+  // every wave computing the whole dot product, wherever the scratch costs no workgroup slot.
+  static constexpr size_t kSplitBytes = (size_t)kWaves * RT * 64 * 16;
+  static constexpr int kWGs(size_t lds) {
+    const int n = (int)((160u * 1024u) / lds);
+    return n < kRegCap ? n : kRegCap;
+  }
+  static constexpr bool kSplit = D >= 256 && kWGs(kTiles + kSplitBytes) >= kWGs(kTiles);
+  static constexpr size_t kLds = kTiles + (kSplit ? kSplitBytes : 0);
+  static constexpr int kWavesPerEU = kWGs(kLds);
 };
 
 // MFMA helpers: QK^T per K-step, PV per page.  16x16 accumulator layout: lane l holds rows
@@ -229,8 +238,10 @@ __device__ __forceinline__ long long pages_before(const int32_t *__restrict__ ct
 // buffers alternate, so while page i is processed pages i + 1 and i + 2 are in flight.  Every
 // fetch is unconditional (an invalid page id re-reads page 0 of the pool, whose data is never
 // used; a fetch past the piece reads a 16-byte location every lane shares), which keeps the
-// wait before each LDS write at "all but the newest page".  Per page, every wave computes the
-// whole 16-key x (16 * RT)-row score tile with MFMAs (so scores never go through LDS), runs
+// wait before each LDS write at "all but the newest page".  Per page, every wave gets the
+// whole 16-key x (16 * RT)-row score tile in MFMA accumulator layout: at small head dims by
+// computing all of it, at D >= 256 (kSplit) by computing its quarter of the head dim and
+// summing the four quarters from LDS in wave order (the same bits in every wave).  It runs
 // the online softmax in registers (4 keys per lane, two cross-lane shuffles for the row max
 // and sum), and accumulates its quarter of the head dim with MFMAs whose B operand is the
 // probability tile as the score MFMA left it.
@@ -247,6 +258,7 @@ __global__ __launch_bounds__(kThreads, (AttnShape<D, T, RT>::kWavesPerEU)) void 
   T *qs = reinterpret_cast<T *>(smem);                             // [kRowsWG][kStr]
   T *ks = qs + kRowsWG * S::kStr;                                  // [16][kStr]
   T *vs = ks + kPage * S::kStr;                                    // [16][kStr]
+  f32x4_t *sred = reinterpret_cast<f32x4_t *>(smem + S::kTiles);   // [kWaves][RT][64] partial scores
   __shared__ int pid_sh[kMaxPagesPerPiece];
 
   const int tid = threadIdx.x, lane = tid & (spec::kWave - 1), wave = tid / spec::kWave;
@@ -377,14 +389,44 @@ __global__ __launch_bounds__(kThreads, (AttnShape<D, T, RT>::kWavesPerEU)) void 
     auto page = [&](int i) __attribute__((always_inline)) {
       if (pid_sh[i] < 0) return;       // uniform: an invalid page id hides its keys
       const int pg = pg_begin + i;
+      // scores S^T[key 4*lq + e][row rt*16 + lr]
+      f32x4_t scs[RT];
+      if constexpr (S::kSplit) {
+        // this wave's quarter of the head dim, then the four quarters summed in wave order
+        constexpr int DQ = D / kWaves;
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          f32x4_t part = {0.f, 0.f, 0.f, 0.f};
+          if (rt == 0 || two_tiles) {
+#pragma unroll
+            for (int d0 = 0; d0 < DQ; d0 += M::kStepQK)
+              part = M::qk(ks + lr * S::kStr + wave * DQ + d0,
+                           qs + (rt * 16 + lr) * S::kStr + wave * DQ + d0, lq, part);
+          }
+          sred[(wave * RT + rt) * 64 + lane] = part;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          f32x4_t t = sred[rt * 64 + lane];
+#pragma unroll
+          for (int w2 = 1; w2 < kWaves; ++w2) t += sred[(w2 * RT + rt) * 64 + lane];
+          scs[rt] = t;
+        }
+      } else {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          scs[rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          if (rt == 1 && !two_tiles) break;
+#pragma unroll
+          for (int d0 = 0; d0 < D; d0 += M::kStepQK)
+            scs[rt] = M::qk(ks + lr * S::kStr + d0, qs + (rt * 16 + lr) * S::kStr + d0, lq, scs[rt]);
+        }
+      }
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
         if (rt == 1 && !two_tiles) break;
-        // scores S^T[key 4*lq + e][row rt*16 + lr]
-        f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int d0 = 0; d0 < D; d0 += M::kStepQK)
-          sc = M::qk(ks + lr * S::kStr + d0, qs + (rt * 16 + lr) * S::kStr + d0, lq, sc);
+        const f32x4_t sc = scs[rt];
         float sv[4];
         float mx = -INFINITY;
 #pragma unroll
