@@ -57,8 +57,8 @@ METRIC = "verified tokens/sec and verify-step HBM GB/s (% peak), batch 1, k=2, 8
 PROFILED_TRAFFIC = {
     "workload": DEFAULT_WORKLOAD,
     "source": "speculative_decoding_decode_amd/csrc/lm_head.hip",
-    "sha256": "b2f7fb52cc7b18f9a022b9d3b21d95a6313fd8d481bb9049c06c11b946a90004",
-    "bytes_per_launch": 1345616209,
+    "sha256": "d96870f72aaff89998abecc4f6818090d751973058b7e262035da965a479b46c",
+    "bytes_per_launch": 1345616191,
 }
 
 
