@@ -18,9 +18,9 @@
 //    tile ahead of the compute.  On MI355X these GEMVs stream the table at about 6.5 TB/s in the
 //    verify step.
 //  * R > 8 rows: MFMA (v_mfma_f32_16x16x32_bf16; fp32 tables: four v_mfma_f32_16x16x4_f32).
-//    One workgroup = 256 vocab rows against up to 96 hidden rows; chunks of 128 bytes of
-//    every row are loaded with 128-byte contiguous runs per row, transposed into MFMA fragments
-//    through bank-conflict-free LDS tiles, with a ring of four chunks in flight.
+//    One workgroup = 512 vocab rows against up to 64 hidden rows, or 256 against up to 96;
+//    chunks of 128 bytes of every row are loaded as 128-byte contiguous runs per row and
+//    transposed into MFMA fragments through bank-conflict-free LDS tiles.
 //  * Every epilogue turns a 256-row vocab block into per-block softmax statistics (max, sum of
 //    exp, first argmax) and writes exp(logit - block max) into p; lm_head_finalize merges the
 //    statistics of all blocks and rescales p in place (or writes the greedy one-hot rows).
@@ -74,36 +74,45 @@ __device__ __forceinline__ bool better(float m, int a, float om, int oa) {
   return om > m || (om == m && oa < a);
 }
 
-// Contraction + per-block statistics for R > 8 rows.  Grid: (ceil(V / 256), ceil(R / (16 NT))),
-// NT = 2 NH tiles of 16 hidden rows per pass; 512 threads, two waves per SIMD.  The workgroup
-// walks the hidden dimension in chunks of 128 bytes of every row; wave w multiplies vocab rows
-// blk * 256 + 64 (w % 4) + [0, 64) (four MFMA tiles, the A operand) by hidden-row tiles
-// NH (w / 4) + [0, NH) (the B operand).
+// Contraction + per-block statistics for R > 8 rows.  512 threads, two waves per SIMD; a
+// workgroup owns 512 / RH vocab rows (RH = 1: two statistics blocks, RH = 2: one) and
+// NT = NH * RH tiles of 16 hidden rows.  Grid: (ceil(V / (512 / RH)), ceil(R / (16 NT))).
+// Wave w multiplies its 64 vocab rows, vocab slice w % (8 / RH) (four MFMA tiles, the A
+// operand), by the hidden-row tiles NH (w / (8 / RH)) + [0, NH) (the B operand).  RH = 1
+// (R <= 64) halves the hidden-row traffic per table byte; RH = 2 (R up to 96 per pass) keeps
+// the accumulators within two waves per SIMD.  The workgroup walks the hidden dimension in
+// chunks of 128 bytes of every row.
 //  * Loads: 8 consecutive lanes read the 128 bytes of one row, so each instruction takes 128
 //    contiguous bytes from each of 8 rows (table loads nontemporal: it is read once per call).
-//    MFMA fragments need one row per lane instead, so every chunk (256 table rows and NT * 16
+//    MFMA fragments need one row per lane instead, so every chunk (the table rows and NT * 16
 //    hidden rows) passes through LDS: rows 128 bytes apart with the 16-byte slots
 //    XOR-swizzled by row pair, so neither the writes nor the fragment reads conflict on a bank.
-//  * Pipeline: the loads of kMmaRing chunks are in flight in a ring of registers (about 176 KB
-//    per CU, which the loaded memory latency needs).  Per chunk: one workgroup barrier, the
-//    multiplies of chunk c out of one LDS buffer, then chunk c + 1 (the oldest in the ring) is
-//    written to the other buffer and its ring slot refilled with chunk c + 1 + kMmaRing.
-//    Fetches past the last chunk read one shared address; slots past H are zeroed on both
-//    operands when they are written to LDS.
+//  * Pipeline: per chunk, one workgroup barrier, the multiplies of chunk c out of one LDS
+//    buffer, then chunk c + 1 (loaded into registers a chunk earlier) is written to the other
+//    buffer and its registers refilled with chunk c + 1 + kMmaRing.  Fetches past the last
+//    chunk read one shared address; slots past H are zeroed on both operands when they are
+//    written to LDS.
 // Accumulator lane l of tile (vt, n) holds the logits of vocab rows 16 vt + 4 (l / 16) + e
-// (e = 0..3) of the wave's 64 for hidden row 16 (NH (w / 4) + n) + l % 16.
+// (e = 0..3) of the wave's 64 for hidden row 16 (NH rh + n) + l % 16.
 constexpr int kMmaThreads = 512;
 constexpr int kMmaWaves = kMmaThreads / kWave;                // 8
 constexpr int kMmaRowsW = 64;                                 // vocab rows per wave
 constexpr int kMmaVT = kMmaRowsW / 16;                        // 4 vocab tiles per wave
 constexpr int kMmaSlots = 8;                                  // 16-byte slots per row per chunk
-constexpr int kMmaWL = kBlockRows * kMmaSlots / kMmaThreads;  // 4 table loads per thread per chunk
-constexpr int kMmaWBuf = kBlockRows * kMmaSlots * 16;         // 32 KB: one chunk of the table
-constexpr int kMmaRing = 4;                                   // chunks in flight
-constexpr int kMaxNH = 3;                                     // hidden-row tiles per wave
-constexpr int kMaxNT = 2 * kMaxNH;                            // hidden-row tiles per pass
-constexpr int kMmaXBuf = kMaxNT * 16 * kMmaSlots * 16;        // 12 KB: one chunk of hidden rows
-constexpr size_t kMmaLds = 2 * (size_t)(kMmaWBuf + kMmaXBuf);
+constexpr int kMmaRing = 2;                                   // chunks in registers
+constexpr int kMaxNH = 4;                                     // hidden-row tiles per wave
+
+template <int NH, int RH>
+struct MmaShape {
+  static constexpr int kRows = kMmaWaves / RH * kMmaRowsW;    // vocab rows per workgroup
+  static constexpr int kVQ = kMmaWaves / RH;                  // vocab slices
+  static constexpr int kNT = NH * RH;                         // hidden-row tiles per pass
+  static constexpr int kWL = kRows * kMmaSlots / kMmaThreads; // table loads per thread per chunk
+  static constexpr int kWBuf = kRows * kMmaSlots * 16;        // one chunk of the table rows
+  static constexpr int kXBuf = kNT * 16 * kMmaSlots * 16;     // one chunk of the hidden rows
+  static constexpr size_t kLds = 2 * (size_t)(kWBuf + kXBuf);
+  static_assert(kRows % kBlockRows == 0 && NH <= kMaxNH, "workgroup = whole statistics blocks");
+};
 
 __device__ __forceinline__ u32x4_t mask16(u32x4_t v, bool keep) {
   const uint32_t m = keep ? 0xffffffffu : 0u;
@@ -113,13 +122,14 @@ __device__ __forceinline__ u32x4_t mask16(u32x4_t v, bool keep) {
 // Byte offset of 16-byte slot `slot` of row `row` in a [rows][8 slots] LDS tile.
 __device__ __forceinline__ int swz(int row, int slot) { return row * 128 + ((slot ^ (row >> 1)) & 7) * 16; }
 
-template <typename T, int NH>
+template <typename T, int NH, int RH>
 __global__ __launch_bounds__(kMmaThreads, 1) void lm_head_mfma(
     const T *__restrict__ X, const T *__restrict__ W, const float *__restrict__ temp,
     float *__restrict__ logits, float *__restrict__ probs, float2 *__restrict__ stats,
     int *__restrict__ amax, int R, int H, int V) {
   using M = Mma<T>;
-  constexpr int NT = 2 * NH;
+  using S = MmaShape<NH, RH>;
+  constexpr int NT = S::kNT;
   constexpr int EPL = M::kEPL;                    // elements per 16-byte slot
   constexpr int KC = kMmaSlots * EPL;             // elements per chunk (two MFMA K-steps)
   constexpr int XS = NT * 16 * kMmaSlots;         // hidden-row slots per chunk
@@ -129,26 +139,26 @@ __global__ __launch_bounds__(kMmaThreads, 1) void lm_head_mfma(
   __shared__ int red_i[kMmaWaves][kMaxNH * 16];
 
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-  const int vq = wave & 3, rh = wave >> 2;      // vocab quarter / hidden-row half
-  const int lr = lane & 15, lq = lane >> 4;     // fragment row / K group
-  const int ls = tid & 7;                       // load slot
+  const int vq = wave % S::kVQ, rh = wave / S::kVQ;   // vocab slice / hidden-row part
+  const int lr = lane & 15, lq = lane >> 4;           // fragment row / K group
+  const int ls = tid & 7;                             // load slot
   const int blk = blockIdx.x;
   const int r0 = blockIdx.y * NT * 16;
-  const int vb = blk * kBlockRows;
+  const int vb = blk * S::kRows;
   const int vw = vb + vq * kMmaRowsW;
   const int nch = (H + KC - 1) / KC;
-  unsigned char *wl = smem;                             // [2][256 rows][128 B]
-  unsigned char *xl = smem + 2 * (size_t)kMmaWBuf;      // [2][NT * 16 rows][128 B]
+  unsigned char *wl = smem;                             // [2][kRows][128 B]
+  unsigned char *xl = smem + 2 * (size_t)S::kWBuf;      // [2][NT * 16 rows][128 B]
 
   struct Chunk {
-    u32x4_t w[kMmaWL];
+    u32x4_t w[S::kWL];
     u32x4_t x[XL];
   };
   auto fetch = [&](Chunk &ch, int c) __attribute__((always_inline)) {
     const size_t live = c < nch ? ~(size_t)0 : 0;   // uniform; past the end: offset 0
     const int kk = min(c * KC + ls * EPL, H - EPL);
 #pragma unroll
-    for (int i = 0; i < kMmaWL; ++i) {
+    for (int i = 0; i < S::kWL; ++i) {
       const size_t off = (size_t)min(vb + (tid + i * kMmaThreads) / kMmaSlots, V - 1) * H + kk;
       ch.w[i] = load_stream(W + (off & live));
     }
@@ -165,13 +175,13 @@ __global__ __launch_bounds__(kMmaThreads, 1) void lm_head_mfma(
     const int buf = c & 1;
     const bool in = c * KC + ls * EPL < H;
 #pragma unroll
-    for (int i = 0; i < kMmaWL; ++i)
-      *reinterpret_cast<u32x4_t *>(wl + buf * kMmaWBuf + swz((tid + i * kMmaThreads) / kMmaSlots, ls)) =
+    for (int i = 0; i < S::kWL; ++i)
+      *reinterpret_cast<u32x4_t *>(wl + buf * S::kWBuf + swz((tid + i * kMmaThreads) / kMmaSlots, ls)) =
           mask16(ch.w[i], in);
 #pragma unroll
     for (int j = 0; j < XL; ++j) {
       const int e = min(tid + j * kMmaThreads, XS - 1);   // duplicates write the same bytes
-      *reinterpret_cast<u32x4_t *>(xl + buf * kMmaXBuf + swz(e / kMmaSlots, e % kMmaSlots)) =
+      *reinterpret_cast<u32x4_t *>(xl + buf * S::kXBuf + swz(e / kMmaSlots, e % kMmaSlots)) =
           mask16(ch.x[j], c * KC + (e % kMmaSlots) * EPL < H);
     }
   };
@@ -188,11 +198,11 @@ __global__ __launch_bounds__(kMmaThreads, 1) void lm_head_mfma(
 #pragma unroll
       for (int vt = 0; vt < kMmaVT; ++vt)
         a[vt] = *reinterpret_cast<const u32x4_t *>(
-            wl + buf * kMmaWBuf + swz(vq * kMmaRowsW + vt * 16 + lr, s * 4 + lq));
+            wl + buf * S::kWBuf + swz(vq * kMmaRowsW + vt * 16 + lr, s * 4 + lq));
 #pragma unroll
       for (int n = 0; n < NH; ++n)
         bx[n] = *reinterpret_cast<const u32x4_t *>(
-            xl + buf * kMmaXBuf + swz((rh * NH + n) * 16 + lr, s * 4 + lq));
+            xl + buf * S::kXBuf + swz((rh * NH + n) * 16 + lr, s * 4 + lq));
 #pragma unroll
       for (int vt = 0; vt < kMmaVT; ++vt)
 #pragma unroll
@@ -223,8 +233,10 @@ __global__ __launch_bounds__(kMmaThreads, 1) void lm_head_mfma(
   }
 
   // ---- epilogue: block max / first argmax, then sum of exp, per hidden row.  Hidden row
-  // slot c = n * 16 + lr of the wave is row r0 + 16 (NH rh + n) + lr; the four vocab quarters
-  // (waves rh * 4 + q) are merged in quarter order.
+  // slot c = n * 16 + lr of the wave is row r0 + 16 (NH rh + n) + lr; the four 64-row slices
+  // of a statistics block (waves g0 + q) are merged in slice order.
+  const int g0 = rh * S::kVQ + (vq & ~3);       // first wave of this wave's block and part
+  const int sb = vb / kBlockRows + vq / 4;      // statistics block
 #pragma unroll
   for (int n = 0; n < NH; ++n) {
     float mx = -INFINITY;
@@ -251,9 +263,9 @@ __global__ __launch_bounds__(kMmaThreads, 1) void lm_head_mfma(
 #pragma unroll
   for (int n = 0; n < NH; ++n) {
     const int c = n * 16 + lr;
-    float m = red_m[rh * 4][c];
+    float m = red_m[g0][c];
 #pragma unroll
-    for (int q = 1; q < 4; ++q) m = fmaxf(m, red_m[rh * 4 + q][c]);
+    for (int q = 1; q < 4; ++q) m = fmaxf(m, red_m[g0 + q][c]);
     const int r = r0 + (rh * NH + n) * 16 + lr;
     live[n] = r < R;
     const float tr = live[n] ? temp[r] : 1.f;
@@ -284,23 +296,23 @@ __global__ __launch_bounds__(kMmaThreads, 1) void lm_head_mfma(
     if (lq == 0) red_s[wave][c] = sacc;
   }
   __syncthreads();
-  if (vq == 0 && lq == 0) {
+  if ((vq & 3) == 0 && lq == 0 && sb * kBlockRows < V) {
 #pragma unroll
     for (int n = 0; n < NH; ++n) {
       const int c = n * 16 + lr, r = r0 + (rh * NH + n) * 16 + lr;
       if (r >= R) continue;
-      float m = red_m[rh * 4][c];
-      int a = red_i[rh * 4][c];
+      float m = red_m[g0][c];
+      int a = red_i[g0][c];
 #pragma unroll
       for (int q = 1; q < 4; ++q)
-        if (better(m, a, red_m[rh * 4 + q][c], red_i[rh * 4 + q][c])) {
-          m = red_m[rh * 4 + q][c];
-          a = red_i[rh * 4 + q][c];
+        if (better(m, a, red_m[g0 + q][c], red_i[g0 + q][c])) {
+          m = red_m[g0 + q][c];
+          a = red_i[g0 + q][c];
         }
-      const float sum = ((red_s[rh * 4][c] + red_s[rh * 4 + 1][c]) + red_s[rh * 4 + 2][c]) +
-                        red_s[rh * 4 + 3][c];
-      stats[(size_t)blk * R + r] = make_float2(m, sum);
-      amax[(size_t)blk * R + r] = a;
+      const float sum = ((red_s[g0][c] + red_s[g0 + 1][c]) + red_s[g0 + 2][c]) +
+                        red_s[g0 + 3][c];
+      stats[(size_t)sb * R + r] = make_float2(m, sum);
+      amax[(size_t)sb * R + r] = a;
     }
   }
 #pragma unroll
@@ -752,30 +764,35 @@ __global__ __launch_bounds__(kThreads) void lm_head_finalize(
   }
 }
 
-template <typename T, int NH>
+template <typename T, int NH, int RH>
 int launch_nh(const void *X, const void *W, const float *temp, float *logits, float *probs,
               float2 *stats, int *amax, int R, int H, int V, hipStream_t st) {
+  using S = MmaShape<NH, RH>;
   static bool attr_set = false;
   if (!attr_set) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void *>(&lm_head_mfma<T, NH>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMmaLds) != hipSuccess)
-      return spec::fail(SPEC_EHIP, "spec_lm_head: cannot reserve %zu bytes of LDS", kMmaLds);
+    if (hipFuncSetAttribute(reinterpret_cast<const void *>(&lm_head_mfma<T, NH, RH>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)S::kLds) != hipSuccess)
+      return spec::fail(SPEC_EHIP, "spec_lm_head: cannot reserve %zu bytes of LDS", S::kLds);
     attr_set = true;
   }
-  dim3 grid(spec::ceil_div(V, kBlockRows), spec::ceil_div(R, 2 * NH * 16));
-  hipLaunchKernelGGL((lm_head_mfma<T, NH>), grid, dim3(kMmaThreads), kMmaLds, st,
+  dim3 grid(spec::ceil_div(V, S::kRows), spec::ceil_div(R, S::kNT * 16));
+  hipLaunchKernelGGL((lm_head_mfma<T, NH, RH>), grid, dim3(kMmaThreads), S::kLds, st,
                      static_cast<const T *>(X), static_cast<const T *>(W), temp, logits, probs,
                      stats, amax, R, H, V);
   return spec::launched("lm_head_mfma");
 }
 
+// R <= 64: one 16-row tile per NH, whole workgroup on all rows (RH = 1); larger R: the rows
+// split between two halves of the workgroup, 96 rows per pass (RH = 2, NH = 3).
 template <typename T>
-int launch(int NH, const void *X, const void *W, const float *temp, float *logits, float *probs,
-           float2 *stats, int *amax, int R, int H, int V, hipStream_t st) {
-  switch (NH) {
-    case 1: return launch_nh<T, 1>(X, W, temp, logits, probs, stats, amax, R, H, V, st);
-    case 2: return launch_nh<T, 2>(X, W, temp, logits, probs, stats, amax, R, H, V, st);
-    default: return launch_nh<T, 3>(X, W, temp, logits, probs, stats, amax, R, H, V, st);
+int launch(int R, const void *X, const void *W, const float *temp, float *logits, float *probs,
+           float2 *stats, int *amax, int H, int V, hipStream_t st) {
+  switch (spec::ceil_div(R, 16)) {
+    case 1: return launch_nh<T, 1, 1>(X, W, temp, logits, probs, stats, amax, R, H, V, st);
+    case 2: return launch_nh<T, 2, 1>(X, W, temp, logits, probs, stats, amax, R, H, V, st);
+    case 3: return launch_nh<T, 3, 1>(X, W, temp, logits, probs, stats, amax, R, H, V, st);
+    case 4: return launch_nh<T, 4, 1>(X, W, temp, logits, probs, stats, amax, R, H, V, st);
+    default: return launch_nh<T, 3, 2>(X, W, temp, logits, probs, stats, amax, R, H, V, st);
   }
 }
 
@@ -832,10 +849,7 @@ int lm_head_check(const void *hidden, const void *weight, const float *temperatu
 int lm_head_contract(const void *hidden, const void *weight, const float *temperature,
                      float *logits, float *probs, float2 *stats, int *amax, int R, int H, int V,
                      spec_dtype dtype, hipStream_t st) {
-  // MFMA path: 2 NH tiles of 16 hidden rows per pass over the table, NH <= 3 (each wave's
-  // accumulators and the ring of chunks in flight fill half a SIMD's registers); more rows
-  // take further passes.
-  const int NH = min(kMaxNH, spec::ceil_div(R, 32));
+
   hipEvent_t ev0 = g_prof_start, ev1 = g_prof_stop;
   g_prof_start = g_prof_stop = nullptr;
   if (ev0 != nullptr && hipEventRecord(ev0, st) != hipSuccess)
@@ -854,8 +868,8 @@ int lm_head_contract(const void *hidden, const void *weight, const float *temper
              : launch_gemv_r<float>(R, hidden, weight, temperature, logits, probs, stats, amax, H, V, st);
   else
     rc = dtype == SPEC_BF16
-             ? launch<uint16_t>(NH, hidden, weight, temperature, logits, probs, stats, amax, R, H, V, st)
-             : launch<float>(NH, hidden, weight, temperature, logits, probs, stats, amax, R, H, V, st);
+             ? launch<uint16_t>(R, hidden, weight, temperature, logits, probs, stats, amax, H, V, st)
+             : launch<float>(R, hidden, weight, temperature, logits, probs, stats, amax, H, V, st);
   if (rc != SPEC_OK) return rc;
   if (ev1 != nullptr && hipEventRecord(ev1, st) != hipSuccess)
     return spec::fail(SPEC_EHIP, "spec_lm_head: hipEventRecord(stop) failed");
