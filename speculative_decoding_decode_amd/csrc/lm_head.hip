@@ -18,9 +18,9 @@
 //    tile ahead of the compute.  On MI355X these GEMVs stream the table at about 6.5 TB/s in the
 //    verify step.
 //  * R > 8 rows: MFMA (v_mfma_f32_16x16x32_bf16; fp32 tables: four v_mfma_f32_16x16x4_f32).
-//    One workgroup = 512 vocab rows against up to 64 hidden rows, or 256 against up to 96;
-//    chunks of 128 bytes of every row are loaded as 128-byte contiguous runs per row and
-//    transposed into MFMA fragments through bank-conflict-free LDS tiles.
+//    One workgroup = 512 vocab rows against up to 96 hidden rows per pass; chunks of 128 bytes
+//    of every row are loaded as 128-byte contiguous runs per row and transposed into MFMA
+//    fragments through bank-conflict-free LDS tiles.
 //  * Every epilogue turns a 256-row vocab block into per-block softmax statistics (max, sum of
 //    exp, first argmax) and writes exp(logit - block max) into p; lm_head_finalize merges the
 //    statistics of all blocks and rescales p in place (or writes the greedy one-hot rows).
@@ -75,43 +75,40 @@ __device__ __forceinline__ bool better(float m, int a, float om, int oa) {
 }
 
 // Contraction + per-block statistics for R > 8 rows.  512 threads, two waves per SIMD; a
-// workgroup owns 512 / RH vocab rows (RH = 1: two statistics blocks, RH = 2: one) and
-// NT = NH * RH tiles of 16 hidden rows.  Grid: (ceil(V / (512 / RH)), ceil(R / (16 NT))).
-// Wave w multiplies its 64 vocab rows, vocab slice w % (8 / RH) (four MFMA tiles, the A
-// operand), by the hidden-row tiles NH (w / (8 / RH)) + [0, NH) (the B operand).  RH = 1
-// (R <= 64) halves the hidden-row traffic per table byte; RH = 2 (R up to 96 per pass) keeps
-// the accumulators within two waves per SIMD.  The workgroup walks the hidden dimension in
-// chunks of 128 bytes of every row.
+// workgroup owns 512 vocab rows (two statistics blocks) and NH <= 6 tiles of 16 hidden rows.
+// Grid: (ceil(V / 512), ceil(R / (16 NH))).  Wave w multiplies vocab rows 64 w + [0, 64) of the
+// workgroup (four MFMA tiles, the A operand) by all NH hidden-row tiles (the B operand).  The
+// workgroup walks the hidden dimension in chunks of 128 bytes of every row.
 //  * Loads: 8 consecutive lanes read the 128 bytes of one row, so each instruction takes 128
 //    contiguous bytes from each of 8 rows (table loads nontemporal: it is read once per call).
-//    MFMA fragments need one row per lane instead, so every chunk (the table rows and NT * 16
-//    hidden rows) passes through LDS: rows 128 bytes apart with the 16-byte slots
-//    XOR-swizzled by row pair, so neither the writes nor the fragment reads conflict on a bank.
+//    MFMA fragments need one row per lane instead, so every chunk (512 table rows and 16 NH
+//    hidden rows) passes through LDS: rows 128 bytes apart with the 16-byte slots XOR-swizzled
+//    by row pair, so neither the writes nor the fragment reads conflict on a bank.  The hidden
+//    rows are re-read for every chunk by every workgroup, so the workgroup is made as tall as
+//    the LDS allows (their bytes per table byte are 16 NH / 512).
 //  * Pipeline: per chunk, one workgroup barrier, the multiplies of chunk c out of one LDS
-//    buffer, then chunk c + 1 (loaded into registers a chunk earlier) is written to the other
-//    buffer and its registers refilled with chunk c + 1 + kMmaRing.  Fetches past the last
-//    chunk read one shared address; slots past H are zeroed on both operands when they are
-//    written to LDS.
+//    buffer, then chunk c + 1 (loaded into registers earlier) is written to the other buffer
+//    and its registers refilled with the next chunk; up to NH = 4 two chunks are in registers,
+//    above that one (the accumulators take the rest).  Fetches past the last chunk read one
+//    shared address; slots past H are zeroed on both operands when they are written to LDS.
 // Accumulator lane l of tile (vt, n) holds the logits of vocab rows 16 vt + 4 (l / 16) + e
-// (e = 0..3) of the wave's 64 for hidden row 16 (NH rh + n) + l % 16.
+// (e = 0..3) of the wave's 64 for hidden row 16 n + l % 16.
 constexpr int kMmaThreads = 512;
 constexpr int kMmaWaves = kMmaThreads / kWave;                // 8
 constexpr int kMmaRowsW = 64;                                 // vocab rows per wave
 constexpr int kMmaVT = kMmaRowsW / 16;                        // 4 vocab tiles per wave
+constexpr int kMmaRows = kMmaWaves * kMmaRowsW;               // 512 vocab rows per workgroup
 constexpr int kMmaSlots = 8;                                  // 16-byte slots per row per chunk
-constexpr int kMmaRing = 2;                                   // chunks in registers
-constexpr int kMaxNH = 4;                                     // hidden-row tiles per wave
+constexpr int kMmaWL = kMmaRows * kMmaSlots / kMmaThreads;    // 8 table loads per thread per chunk
+constexpr int kMmaWBuf = kMmaRows * kMmaSlots * 16;           // 64 KB: one chunk of the table rows
+constexpr int kMaxNH = 6;                                     // hidden-row tiles per pass
 
-template <int NH, int RH>
+template <int NH>
 struct MmaShape {
-  static constexpr int kRows = kMmaWaves / RH * kMmaRowsW;    // vocab rows per workgroup
-  static constexpr int kVQ = kMmaWaves / RH;                  // vocab slices
-  static constexpr int kNT = NH * RH;                         // hidden-row tiles per pass
-  static constexpr int kWL = kRows * kMmaSlots / kMmaThreads; // table loads per thread per chunk
-  static constexpr int kWBuf = kRows * kMmaSlots * 16;        // one chunk of the table rows
-  static constexpr int kXBuf = kNT * 16 * kMmaSlots * 16;     // one chunk of the hidden rows
-  static constexpr size_t kLds = 2 * (size_t)(kWBuf + kXBuf);
-  static_assert(kRows % kBlockRows == 0 && NH <= kMaxNH, "workgroup = whole statistics blocks");
+  static constexpr int kXBuf = NH * 16 * kMmaSlots * 16;      // one chunk of the hidden rows
+  static constexpr size_t kLds = 2 * (size_t)(kMmaWBuf + kXBuf);
+  static constexpr int kRing = NH > 4 ? 1 : 2;                // chunks in registers
+  static_assert(kMmaRows % kBlockRows == 0 && NH <= kMaxNH, "workgroup = whole statistics blocks");
 };
 
 __device__ __forceinline__ u32x4_t mask16(u32x4_t v, bool keep) {
@@ -122,43 +119,40 @@ __device__ __forceinline__ u32x4_t mask16(u32x4_t v, bool keep) {
 // Byte offset of 16-byte slot `slot` of row `row` in a [rows][8 slots] LDS tile.
 __device__ __forceinline__ int swz(int row, int slot) { return row * 128 + ((slot ^ (row >> 1)) & 7) * 16; }
 
-template <typename T, int NH, int RH>
+template <typename T, int NH>
 __global__ __launch_bounds__(kMmaThreads, 1) void lm_head_mfma(
     const T *__restrict__ X, const T *__restrict__ W, const float *__restrict__ temp,
     float *__restrict__ logits, float *__restrict__ probs, float2 *__restrict__ stats,
     int *__restrict__ amax, int R, int H, int V) {
   using M = Mma<T>;
-  using S = MmaShape<NH, RH>;
-  constexpr int NT = S::kNT;
+  using S = MmaShape<NH>;
+  constexpr int NT = NH;
   constexpr int EPL = M::kEPL;                    // elements per 16-byte slot
   constexpr int KC = kMmaSlots * EPL;             // elements per chunk (two MFMA K-steps)
   constexpr int XS = NT * 16 * kMmaSlots;         // hidden-row slots per chunk
   constexpr int XL = (XS + kMmaThreads - 1) / kMmaThreads;   // of them per thread
   extern __shared__ __align__(16) unsigned char smem[];
-  __shared__ float red_m[kMmaWaves][kMaxNH * 16], red_s[kMmaWaves][kMaxNH * 16];
-  __shared__ int red_i[kMmaWaves][kMaxNH * 16];
 
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-  const int vq = wave % S::kVQ, rh = wave / S::kVQ;   // vocab slice / hidden-row part
   const int lr = lane & 15, lq = lane >> 4;           // fragment row / K group
   const int ls = tid & 7;                             // load slot
   const int blk = blockIdx.x;
   const int r0 = blockIdx.y * NT * 16;
-  const int vb = blk * S::kRows;
-  const int vw = vb + vq * kMmaRowsW;
+  const int vb = blk * kMmaRows;
+  const int vw = vb + wave * kMmaRowsW;
   const int nch = (H + KC - 1) / KC;
-  unsigned char *wl = smem;                             // [2][kRows][128 B]
-  unsigned char *xl = smem + 2 * (size_t)S::kWBuf;      // [2][NT * 16 rows][128 B]
+  unsigned char *wl = smem;                             // [2][512 rows][128 B]
+  unsigned char *xl = smem + 2 * (size_t)kMmaWBuf;      // [2][NH * 16 rows][128 B]
 
   struct Chunk {
-    u32x4_t w[S::kWL];
+    u32x4_t w[kMmaWL];
     u32x4_t x[XL];
   };
   auto fetch = [&](Chunk &ch, int c) __attribute__((always_inline)) {
     const size_t live = c < nch ? ~(size_t)0 : 0;   // uniform; past the end: offset 0
     const int kk = min(c * KC + ls * EPL, H - EPL);
 #pragma unroll
-    for (int i = 0; i < S::kWL; ++i) {
+    for (int i = 0; i < kMmaWL; ++i) {
       const size_t off = (size_t)min(vb + (tid + i * kMmaThreads) / kMmaSlots, V - 1) * H + kk;
       ch.w[i] = load_stream(W + (off & live));
     }
@@ -175,8 +169,8 @@ __global__ __launch_bounds__(kMmaThreads, 1) void lm_head_mfma(
     const int buf = c & 1;
     const bool in = c * KC + ls * EPL < H;
 #pragma unroll
-    for (int i = 0; i < S::kWL; ++i)
-      *reinterpret_cast<u32x4_t *>(wl + buf * S::kWBuf + swz((tid + i * kMmaThreads) / kMmaSlots, ls)) =
+    for (int i = 0; i < kMmaWL; ++i)
+      *reinterpret_cast<u32x4_t *>(wl + buf * kMmaWBuf + swz((tid + i * kMmaThreads) / kMmaSlots, ls)) =
           mask16(ch.w[i], in);
 #pragma unroll
     for (int j = 0; j < XL; ++j) {
@@ -198,11 +192,11 @@ __global__ __launch_bounds__(kMmaThreads, 1) void lm_head_mfma(
 #pragma unroll
       for (int vt = 0; vt < kMmaVT; ++vt)
         a[vt] = *reinterpret_cast<const u32x4_t *>(
-            wl + buf * S::kWBuf + swz(vq * kMmaRowsW + vt * 16 + lr, s * 4 + lq));
+            wl + buf * kMmaWBuf + swz(wave * kMmaRowsW + vt * 16 + lr, s * 4 + lq));
 #pragma unroll
       for (int n = 0; n < NH; ++n)
         bx[n] = *reinterpret_cast<const u32x4_t *>(
-            xl + buf * S::kXBuf + swz((rh * NH + n) * 16 + lr, s * 4 + lq));
+            xl + buf * S::kXBuf + swz(n * 16 + lr, s * 4 + lq));
 #pragma unroll
       for (int vt = 0; vt < kMmaVT; ++vt)
 #pragma unroll
@@ -210,33 +204,40 @@ __global__ __launch_bounds__(kMmaThreads, 1) void lm_head_mfma(
     }
   };
 
-  Chunk ring[kMmaRing];
+  constexpr int RING = S::kRing;
+  Chunk ring[RING];
 #pragma unroll
-  for (int q = 0; q < kMmaRing; ++q) fetch(ring[q], q);
+  for (int q = 0; q < RING; ++q) fetch(ring[q], q);
   stage(ring[0], 0);
-  fetch(ring[0], kMmaRing);
+  fetch(ring[0], RING);
   // Scheduling barriers keep each phase where it is written, so every wait leaves the younger
-  // chunks in flight.  Chunk counts that are not a multiple of kMmaRing end with multiplies of
+  // chunks in flight.  Chunk counts that are not a multiple of RING end with multiplies of
   // zeros (chunks past H are zero on both operands).
-  for (int c0 = 0; c0 < nch; c0 += kMmaRing) {
+  for (int c0 = 0; c0 < nch; c0 += RING) {
 #pragma unroll
-    for (int q = 0; q < kMmaRing; ++q) {
+    for (int q = 0; q < RING; ++q) {
       const int c = c0 + q;
       __syncthreads();          // chunk c is in LDS; every wave is done with chunk c - 1
       __builtin_amdgcn_sched_barrier(0);
       compute(c);
       __builtin_amdgcn_sched_barrier(0);
-      stage(ring[(q + 1) % kMmaRing], c + 1);
-      fetch(ring[(q + 1) % kMmaRing], c + 1 + kMmaRing);
+      stage(ring[(q + 1) % RING], c + 1);
+      fetch(ring[(q + 1) % RING], c + 1 + RING);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
 
   // ---- epilogue: block max / first argmax, then sum of exp, per hidden row.  Hidden row
-  // slot c = n * 16 + lr of the wave is row r0 + 16 (NH rh + n) + lr; the four 64-row slices
+  // slot c = n * 16 + lr of the wave is row r0 + 16 n + lr; the four 64-row slices
   // of a statistics block (waves g0 + q) are merged in slice order.
-  const int g0 = rh * S::kVQ + (vq & ~3);       // first wave of this wave's block and part
-  const int sb = vb / kBlockRows + vq / 4;      // statistics block
+  const int g0 = wave & ~3;                     // first wave of this wave's block
+  __syncthreads();   // the chunk buffers are free: they hold the reduction arrays now
+  typedef float RowF[kMaxNH * 16];
+  typedef int RowI[kMaxNH * 16];
+  RowF *red_m = reinterpret_cast<RowF *>(smem);
+  RowF *red_s = red_m + kMmaWaves;
+  RowI *red_i = reinterpret_cast<RowI *>(red_s + kMmaWaves);
+  const int sb = vb / kBlockRows + wave / 4;    // statistics block
 #pragma unroll
   for (int n = 0; n < NH; ++n) {
     float mx = -INFINITY;
@@ -266,7 +267,7 @@ __global__ __launch_bounds__(kMmaThreads, 1) void lm_head_mfma(
     float m = red_m[g0][c];
 #pragma unroll
     for (int q = 1; q < 4; ++q) m = fmaxf(m, red_m[g0 + q][c]);
-    const int r = r0 + (rh * NH + n) * 16 + lr;
+    const int r = r0 + n * 16 + lr;
     live[n] = r < R;
     const float tr = live[n] ? temp[r] : 1.f;
     cexp[n] = tr > 0.f ? kLog2e / tr : 0.f;   // 0: greedy row, p is written by the finalize
@@ -296,10 +297,10 @@ __global__ __launch_bounds__(kMmaThreads, 1) void lm_head_mfma(
     if (lq == 0) red_s[wave][c] = sacc;
   }
   __syncthreads();
-  if ((vq & 3) == 0 && lq == 0 && sb * kBlockRows < V) {
+  if ((wave & 3) == 0 && lq == 0 && sb * kBlockRows < V) {
 #pragma unroll
     for (int n = 0; n < NH; ++n) {
-      const int c = n * 16 + lr, r = r0 + (rh * NH + n) * 16 + lr;
+      const int c = n * 16 + lr, r = r0 + n * 16 + lr;
       if (r >= R) continue;
       float m = red_m[g0][c];
       int a = red_i[g0][c];
@@ -317,7 +318,7 @@ __global__ __launch_bounds__(kMmaThreads, 1) void lm_head_mfma(
   }
 #pragma unroll
   for (int n = 0; n < NH; ++n) {
-    const int r = r0 + (rh * NH + n) * 16 + lr;
+    const int r = r0 + n * 16 + lr;
     if (!live[n] || cexp[n] == 0.f) continue;
 #pragma unroll
     for (int vt = 0; vt < kMmaVT; ++vt) {
@@ -764,35 +765,35 @@ __global__ __launch_bounds__(kThreads) void lm_head_finalize(
   }
 }
 
-template <typename T, int NH, int RH>
+template <typename T, int NH>
 int launch_nh(const void *X, const void *W, const float *temp, float *logits, float *probs,
               float2 *stats, int *amax, int R, int H, int V, hipStream_t st) {
-  using S = MmaShape<NH, RH>;
+  using S = MmaShape<NH>;
   static bool attr_set = false;
   if (!attr_set) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void *>(&lm_head_mfma<T, NH, RH>),
+    if (hipFuncSetAttribute(reinterpret_cast<const void *>(&lm_head_mfma<T, NH>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)S::kLds) != hipSuccess)
       return spec::fail(SPEC_EHIP, "spec_lm_head: cannot reserve %zu bytes of LDS", S::kLds);
     attr_set = true;
   }
-  dim3 grid(spec::ceil_div(V, S::kRows), spec::ceil_div(R, S::kNT * 16));
-  hipLaunchKernelGGL((lm_head_mfma<T, NH, RH>), grid, dim3(kMmaThreads), S::kLds, st,
+  dim3 grid(spec::ceil_div(V, kMmaRows), spec::ceil_div(R, NH * 16));
+  hipLaunchKernelGGL((lm_head_mfma<T, NH>), grid, dim3(kMmaThreads), S::kLds, st,
                      static_cast<const T *>(X), static_cast<const T *>(W), temp, logits, probs,
                      stats, amax, R, H, V);
   return spec::launched("lm_head_mfma");
 }
 
-// R <= 64: one 16-row tile per NH, whole workgroup on all rows (RH = 1); larger R: the rows
-// split between two halves of the workgroup, 96 rows per pass (RH = 2, NH = 3).
+// One pass over the table covers up to 96 hidden rows; more rows take further passes.
 template <typename T>
 int launch(int R, const void *X, const void *W, const float *temp, float *logits, float *probs,
            float2 *stats, int *amax, int H, int V, hipStream_t st) {
-  switch (spec::ceil_div(R, 16)) {
-    case 1: return launch_nh<T, 1, 1>(X, W, temp, logits, probs, stats, amax, R, H, V, st);
-    case 2: return launch_nh<T, 2, 1>(X, W, temp, logits, probs, stats, amax, R, H, V, st);
-    case 3: return launch_nh<T, 3, 1>(X, W, temp, logits, probs, stats, amax, R, H, V, st);
-    case 4: return launch_nh<T, 4, 1>(X, W, temp, logits, probs, stats, amax, R, H, V, st);
-    default: return launch_nh<T, 3, 2>(X, W, temp, logits, probs, stats, amax, R, H, V, st);
+  switch (min(kMaxNH, spec::ceil_div(R, 16))) {
+    case 1: return launch_nh<T, 1>(X, W, temp, logits, probs, stats, amax, R, H, V, st);
+    case 2: return launch_nh<T, 2>(X, W, temp, logits, probs, stats, amax, R, H, V, st);
+    case 3: return launch_nh<T, 3>(X, W, temp, logits, probs, stats, amax, R, H, V, st);
+    case 4: return launch_nh<T, 4>(X, W, temp, logits, probs, stats, amax, R, H, V, st);
+    case 5: return launch_nh<T, 5>(X, W, temp, logits, probs, stats, amax, R, H, V, st);
+    default: return launch_nh<T, 6>(X, W, temp, logits, probs, stats, amax, R, H, V, st);
   }
 }
 
