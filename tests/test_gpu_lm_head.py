@@ -47,7 +47,9 @@ def test_tiny_fp32_workload():
 
 @pytest.mark.parametrize("R,H,V,dtype", [(19, 264, 5003, "bf16"), (5, 8, 17, "f32"),
                                           (130, 64, 1000, "bf16"), (1, 512, 4100, "f32"),
-                                          (33, 2568, 2048, "bf16"), (20, 200, 777, "f32")])
+                                          (33, 2568, 2048, "bf16"), (20, 200, 777, "f32"),
+                                          (97, 136, 700, "bf16"), (40, 64, 100, "bf16"),
+                                          (96, 72, 1536, "f32")])
 def test_ragged_shapes(R, H, V, dtype):
     torch.manual_seed(R * 7 + V)
     td = torch.float32 if dtype == "f32" else torch.bfloat16
