@@ -57,8 +57,8 @@ METRIC = "verified tokens/sec and verify-step HBM GB/s (% peak), batch 1, k=2, 8
 PROFILED_TRAFFIC = {
     "workload": DEFAULT_WORKLOAD,
     "source": "speculative_decoding_decode_amd/csrc/lm_head.hip",
-    "sha256": "d96870f72aaff89998abecc4f6818090d751973058b7e262035da965a479b46c",
-    "bytes_per_launch": 1345616191,
+    "sha256": "757d78cd076e07c420d4c131a701dce14a872a7a55bb7e18f94985d01008a93a",
+    "bytes_per_launch": 1345616160,
 }
 
 
