@@ -506,23 +506,26 @@ __global__ __launch_bounds__(kThreads, (AttnShape<D, T, RT>::kWavesPerEU)) void 
   }
 }
 
-// Grid: B * K1 * Hq workgroups of kCombWaves waves, one per output row (b, i, h).  Every
-// wave finds the row's pieces (the same plan as the partial kernel) and their common maximum;
-// wave v then sums the weighted partial outputs of pieces v, v + kCombWaves, ..., D / 64
-// columns per lane, with the loads of up to kBatch pieces issued together, and one LDS
-// exchange adds the waves' sums.
-constexpr int kCombWaves = 8;
+// Grid: B * K1 * Hq workgroups of CW waves, one per output row (b, i, h).  Every wave finds
+// the row's pieces (the same plan as the partial kernel) and their common maximum; wave v then
+// sums the weighted partial outputs of pieces v, v + CW, ..., D / 64 columns per lane, with
+// the loads of up to kBatch pieces issued together, and one LDS exchange adds the waves' sums.
+// CW = 8 when units have many pieces (few long sequences), 2 when they have a handful (many
+// sequences), so that all rows' workgroups are resident at once.
+// Pieces per unit (about nwg / units, plus the two boundary pieces) up to which two waves
+// merge a row.
+constexpr int kCombFewPieces = 16;
 
-template <int D>
-__global__ __launch_bounds__(kCombWaves * 64) void attn_combine(
+template <int D, int CW>
+__global__ __launch_bounds__(CW * 64) void attn_combine(
     const float2 *__restrict__ part_ml, const float *__restrict__ part_acc,
     const int32_t *__restrict__ ctx_lens, float *__restrict__ out, int B, int K1, int Hq, int Hkv,
     int max_pages, int window, int nwg, int c_floor, int GK1, int rows_wg) {
   constexpr int NC = D / spec::kWave;                 // columns per lane
   constexpr int kBatch = NC >= 8 ? 8 : 64 / NC > 16 ? 16 : 64 / NC;
   typedef float vecc_t __attribute__((ext_vector_type(NC)));
-  __shared__ __align__(16) float red_acc[kCombWaves - 1][D];
-  __shared__ float red_l[kCombWaves];
+  __shared__ __align__(16) float red_acc[CW - 1][D];
+  __shared__ float red_l[CW];
   const int tid = threadIdx.x, lane = tid & (spec::kWave - 1), wave = tid / spec::kWave;
   const long long row = blockIdx.x;
   const int h = (int)(row % Hq), i = (int)((row / Hq) % K1), b = (int)(row / ((long long)Hq * K1));
@@ -547,13 +550,13 @@ __global__ __launch_bounds__(kCombWaves * 64) void attn_combine(
   const float2 *mlp = part_ml + (size_t)piece0 * rstride + r;
   const float *ap = part_acc + ((size_t)piece0 * rstride + r) * D + lane * NC;
   const size_t astep = (size_t)rstride * D;
-  const int nmine = n > wave ? (n - wave + kCombWaves - 1) / kCombWaves : 0;   // pieces wave, wave + kCombWaves, ..
+  const int nmine = n > wave ? (n - wave + CW - 1) / CW : 0;   // pieces wave, wave + CW, ..
 
   // this wave's first batch of partial outputs is in flight while the maximum is reduced
   vecc_t v[kBatch];
 #pragma unroll
   for (int t = 0; t < kBatch; ++t)
-    v[t] = *reinterpret_cast<const vecc_t *>(ap + (size_t)min(wave + kCombWaves * t, n - 1) * astep);
+    v[t] = *reinterpret_cast<const vecc_t *>(ap + (size_t)min(wave + CW * t, n - 1) * astep);
   float mx = -INFINITY;
   for (int c0 = 0; c0 < n; c0 += spec::kWave) {
     const float2 x = mlp[(size_t)min(c0 + lane, n - 1) * rstride];
@@ -565,7 +568,7 @@ __global__ __launch_bounds__(kCombWaves * 64) void attn_combine(
   vecc_t a = vecc_t(0.f);
   float l = 0.f;
   for (int t0 = 0; t0 < nmine; t0 += spec::kWave) {
-    const int k = wave + kCombWaves * min(t0 + lane, nmine - 1);
+    const int k = wave + CW * min(t0 + lane, nmine - 1);
     const float2 x = mlp[(size_t)k * rstride];
     const float wk = (t0 + lane < nmine && x.x != -INFINITY) ? exp2f(x.x - m) : 0.f;
     l += wk * x.y;
@@ -575,7 +578,7 @@ __global__ __launch_bounds__(kCombWaves * 64) void attn_combine(
 #pragma unroll
         for (int t = 0; t < kBatch; ++t)
           v[t] = *reinterpret_cast<const vecc_t *>(
-              ap + (size_t)(wave + kCombWaves * min(t0 + u0 + t, nmine - 1)) * astep);
+              ap + (size_t)(wave + CW * min(t0 + u0 + t, nmine - 1)) * astep);
       }
 #pragma unroll
       for (int t = 0; t < kBatch; ++t) {
@@ -593,7 +596,7 @@ __global__ __launch_bounds__(kCombWaves * 64) void attn_combine(
   if (wave == 0) {
     float L = l;
 #pragma unroll
-    for (int x = 0; x < kCombWaves - 1; ++x) {
+    for (int x = 0; x < CW - 1; ++x) {
       a += *reinterpret_cast<const vecc_t *>(&red_acc[x][lane * NC]);
       L += red_l[x + 1];
     }
@@ -678,9 +681,16 @@ int launch(const void *q, const void *kp, const void *vp, const int32_t *table,
                                          max_pages, window, scale, pl, ml, acc, st);
   if (rc != SPEC_OK) return rc;
   const long long rows = (long long)B * K1 * Hq;
-  hipLaunchKernelGGL((attn_combine<D>), dim3((unsigned)rows),
-                     dim3(kCombWaves * 64), 0, st, ml, acc, ctx, out, B, K1, Hq, Hkv, max_pages,
-                     window, pl.nwg, pl.c_floor, pl.GK1, pl.rows_wg);
+  const long long units = (long long)B * Hkv * spec::ceil_div(pl.GK1, pl.rows_wg);
+  if (pl.nwg / units + 2 <= kCombFewPieces) {
+    hipLaunchKernelGGL((attn_combine<D, 2>), dim3((unsigned)rows), dim3(2 * 64), 0, st, ml, acc,
+                       ctx, out, B, K1, Hq, Hkv, max_pages, window, pl.nwg, pl.c_floor, pl.GK1,
+                       pl.rows_wg);
+  } else {
+    hipLaunchKernelGGL((attn_combine<D, 8>), dim3((unsigned)rows), dim3(8 * 64), 0, st, ml, acc,
+                       ctx, out, B, K1, Hq, Hkv, max_pages, window, pl.nwg, pl.c_floor, pl.GK1,
+                       pl.rows_wg);
+  }
   return spec::launched("attn_combine");
 }
 
