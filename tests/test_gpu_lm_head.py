@@ -59,15 +59,16 @@ def test_ragged_shapes(R, H, V, dtype):
     run_and_compare(x, W, temps, dtype, label="ragged")
 
 
-def test_greedy_ties_take_first_index():
+@pytest.mark.parametrize("R", [2, 20])        # GEMV and MFMA paths
+def test_greedy_ties_take_first_index(R):
     d = dev()
-    x = torch.ones(2, 16, dtype=torch.float32)
+    x = torch.ones(R, 16, dtype=torch.float32)
     W = torch.zeros(600, 16, dtype=torch.float32)
     W[[7, 300, 599]] = 1.0                         # three equal maxima across blocks
-    t = torch.zeros(2, device=d)
+    t = torch.zeros(R, device=d)
     _, p = sv.lm_head(x.to(d), W.to(d), t)
     pc = p.cpu()
-    assert pc[:, 7].tolist() == [1.0, 1.0] and float(pc.sum()) == 2.0
+    assert pc[:, 7].tolist() == [1.0] * R and float(pc.sum()) == float(R)
 
 
 @pytest.mark.parametrize("name", ["b1_k2_sliding256_8k", "b1_k4_global512_32k"])
