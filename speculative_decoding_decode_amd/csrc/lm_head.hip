@@ -7,17 +7,17 @@
 // from memory (same guide, introduction).  At R = 3..96 rows the kernel is a stream over the
 // V x H table: every table element is read once from HBM and used R times.
 //
-// Design (gfx950).  Three contraction kernels share one softmax finalize:
+// Design (gfx950).  Three contraction kernels share one softmax finalize; which one runs was
+// set by timing all three on MI355X at 1..8 rows:
 //  * R <= 3 rows over rows of at most 5 KB (batch-1 verification): a bandwidth-bound GEMV
 //    with the hidden rows in registers.  Each wave owns 64 table rows and streams them two at
 //    a time; every load instruction reads 1 KB of contiguous table with a nontemporal load (the
 //    table is used once per call) and products accumulate in fp32 with v_dot2_f32_bf16 (fp32
-//    tables: FMAs); a wave reduction gives each row's logit.
-//  * other R <= 8: the same stream as (row pair, 1 KB column chunk) items with the hidden rows
+//    tables: FMAs); a wave reduction gives each row's logit.  About 6.5 TB/s in the step.
+//  * other R <= 2: the same stream as (row pair, 1 KB column chunk) items with the hidden rows
 //    in LDS (one LDS read serves two table rows); when the hidden rows fill LDS the loads run a
-//    tile ahead of the compute.  On MI355X these GEMVs stream the table at about 6.5 TB/s in the
-//    verify step.
-//  * R > 8 rows: MFMA (v_mfma_f32_16x16x32_bf16; fp32 tables: four v_mfma_f32_16x16x4_f32).
+//    tile ahead of the compute.
+//  * every other R: MFMA (v_mfma_f32_16x16x32_bf16; fp32 tables: four v_mfma_f32_16x16x4_f32).
 //    One workgroup = 512 vocab rows against up to 96 hidden rows per pass; chunks of 128 bytes
 //    of every row are loaded as 128-byte contiguous runs per row and transposed into MFMA
 //    fragments through bank-conflict-free LDS tiles.
@@ -74,8 +74,9 @@ __device__ __forceinline__ bool better(float m, int a, float om, int oa) {
   return om > m || (om == m && oa < a);
 }
 
-// Contraction + per-block statistics for R > 8 rows.  512 threads, two waves per SIMD; a
-// workgroup owns 512 vocab rows (two statistics blocks) and NH <= 6 tiles of 16 hidden rows.
+// Contraction + per-block statistics for every R the GEMVs do not take.  512 threads, two
+// waves per SIMD; a workgroup owns 512 vocab rows (two statistics blocks) and NH <= 6 tiles of
+// 16 hidden rows.
 // Grid: (ceil(V / 512), ceil(R / (16 NH))).  Wave w multiplies vocab rows 64 w + [0, 64) of the
 // workgroup (four MFMA tiles, the A operand) by all NH hidden-row tiles (the B operand).  The
 // workgroup walks the hidden dimension in chunks of 128 bytes of every row.
@@ -338,7 +339,7 @@ __global__ __launch_bounds__(kMmaThreads, 1) void lm_head_mfma(
 // ------------------------------------------------------------------------- small-R GEMV path
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
-constexpr int kGemvMaxR = 8;
+constexpr int kGemvMaxR = 2;     // above this the MFMA contraction streams faster
 constexpr int kRowsPerWave = 64;     // one table row per lane in the epilogue
 constexpr int kTile = 2;             // items (row pair x 1 KB chunk) per prefetch tile
 
@@ -688,16 +689,8 @@ int launch_gemv(const void *X, const void *W, const float *temp, float *logits, 
 template <typename T>
 int launch_gemv_r(int R, const void *X, const void *W, const float *temp, float *logits,
                   float *probs, float2 *stats, int *amax, int H, int V, hipStream_t st) {
-  switch (R) {
-    case 1: return launch_gemv<T, 1>(X, W, temp, logits, probs, stats, amax, H, V, st);
-    case 2: return launch_gemv<T, 2>(X, W, temp, logits, probs, stats, amax, H, V, st);
-    case 3: return launch_gemv<T, 3>(X, W, temp, logits, probs, stats, amax, H, V, st);
-    case 4: return launch_gemv<T, 4>(X, W, temp, logits, probs, stats, amax, H, V, st);
-    case 5: return launch_gemv<T, 5>(X, W, temp, logits, probs, stats, amax, H, V, st);
-    case 6: return launch_gemv<T, 6>(X, W, temp, logits, probs, stats, amax, H, V, st);
-    case 7: return launch_gemv<T, 7>(X, W, temp, logits, probs, stats, amax, H, V, st);
-    default: return launch_gemv<T, 8>(X, W, temp, logits, probs, stats, amax, H, V, st);
-  }
+  return R == 1 ? launch_gemv<T, 1>(X, W, temp, logits, probs, stats, amax, H, V, st)
+                : launch_gemv<T, 2>(X, W, temp, logits, probs, stats, amax, H, V, st);
 }
 
 // Merge the block statistics of row blockIdx.y and normalise its chunk of p in place.

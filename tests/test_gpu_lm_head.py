@@ -49,7 +49,8 @@ def test_tiny_fp32_workload():
                                           (130, 64, 1000, "bf16"), (1, 512, 4100, "f32"),
                                           (33, 2568, 2048, "bf16"), (20, 200, 777, "f32"),
                                           (97, 136, 700, "bf16"), (40, 64, 100, "bf16"),
-                                          (96, 72, 1536, "f32")])
+                                          (96, 72, 1536, "f32"), (2, 2568, 3000, "bf16"),
+                                          (2, 5376, 1500, "bf16"), (4, 2560, 2000, "bf16")])
 def test_ragged_shapes(R, H, V, dtype):
     torch.manual_seed(R * 7 + V)
     td = torch.float32 if dtype == "f32" else torch.bfloat16
