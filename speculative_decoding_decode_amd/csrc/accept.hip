@@ -31,6 +31,7 @@ constexpr int kMaxK = 63;
 constexpr float kFixedScale = 274877906944.0f;   // 2^38
 constexpr int kUniformBits = 24;
 constexpr int kMaxE = 64;                        // elements per thread per chunk (V <= 4M)
+constexpr long kChunkWGs = 2048;                 // chunk workgroups worth one round on the GPU
 
 __device__ __forceinline__ uint64_t fixed_weight(float x) {
   const float s = x * kFixedScale;   // exact: power-of-two scaling
@@ -272,9 +273,13 @@ struct AcceptPlan {
 AcceptPlan plan(int B, int V) {
   AcceptPlan pl;
   // chunk = 256 * E elements, E a power of two chosen so that a row has at most 256 chunks
-  // (one chunk sum per thread of the draw kernel); V = 262144 gives 256 chunks of 1024.
+  // (one chunk sum per thread of the draw kernel; V = 262144 gives 256 chunks of 1024), and
+  // larger while the batch would need more than kChunkWGs workgroups (then every workgroup
+  // streams more of its row instead of the grid running in several rounds).  The chunking
+  // only groups exact integer sums, so it never changes a result.
   int E = 1;
   while (E < kMaxE && (long)kThreads * E * kThreads < V) E *= 2;
+  while (E < kMaxE && (long)B * spec::ceil_div(V, kThreads * E) > kChunkWGs) E *= 2;
   pl.E = E;
   pl.chunk = kThreads * E;
   pl.nchunks = spec::ceil_div(V, pl.chunk);
