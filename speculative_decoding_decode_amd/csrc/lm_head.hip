@@ -88,10 +88,10 @@ __device__ __forceinline__ bool better(float m, int a, float om, int oa) {
 //    rows are re-read for every chunk by every workgroup, so the workgroup is made as tall as
 //    the LDS allows (their bytes per table byte are 16 NH / 512).
 //  * Pipeline: per chunk, one workgroup barrier, the multiplies of chunk c out of one LDS
-//    buffer, then chunk c + 1 (loaded into registers earlier) is written to the other buffer
-//    and its registers refilled with the next chunk; up to NH = 4 two chunks are in registers,
-//    above that one (the accumulators take the rest).  Fetches past the last chunk read one
-//    shared address; slots past H are zeroed on both operands when they are written to LDS.
+//    buffer, then chunk c + 1 (loaded into registers during chunk c - 1) is written to the
+//    other buffer and the registers refilled with chunk c + 2.  (Two chunks in registers were
+//    measured 1-2% slower.)  Fetches past the last chunk read one shared address; slots past H
+//    are zeroed on both operands when they are written to LDS.
 // Accumulator lane l of tile (vt, n) holds the logits of vocab rows 16 vt + 4 (l / 16) + e
 // (e = 0..3) of the wave's 64 for hidden row 16 n + l % 16.
 constexpr int kMmaThreads = 512;
@@ -108,7 +108,6 @@ template <int NH>
 struct MmaShape {
   static constexpr int kXBuf = NH * 16 * kMmaSlots * 16;      // one chunk of the hidden rows
   static constexpr size_t kLds = 2 * (size_t)(kMmaWBuf + kXBuf);
-  static constexpr int kRing = NH > 4 ? 1 : 2;                // chunks in registers
   static_assert(kMmaRows % kBlockRows == 0 && NH <= kMaxNH, "workgroup = whole statistics blocks");
 };
 
@@ -205,27 +204,20 @@ __global__ __launch_bounds__(kMmaThreads, 1) void lm_head_mfma(
     }
   };
 
-  constexpr int RING = S::kRing;
-  Chunk ring[RING];
-#pragma unroll
-  for (int q = 0; q < RING; ++q) fetch(ring[q], q);
-  stage(ring[0], 0);
-  fetch(ring[0], RING);
-  // Scheduling barriers keep each phase where it is written, so every wait leaves the younger
-  // chunks in flight.  Chunk counts that are not a multiple of RING end with multiplies of
-  // zeros (chunks past H are zero on both operands).
-  for (int c0 = 0; c0 < nch; c0 += RING) {
-#pragma unroll
-    for (int q = 0; q < RING; ++q) {
-      const int c = c0 + q;
-      __syncthreads();          // chunk c is in LDS; every wave is done with chunk c - 1
-      __builtin_amdgcn_sched_barrier(0);
-      compute(c);
-      __builtin_amdgcn_sched_barrier(0);
-      stage(ring[(q + 1) % RING], c + 1);
-      fetch(ring[(q + 1) % RING], c + 1 + RING);
-      __builtin_amdgcn_sched_barrier(0);
-    }
+  Chunk ring;
+  fetch(ring, 0);
+  stage(ring, 0);
+  fetch(ring, 1);
+  // Scheduling barriers keep each phase where it is written, so the wait before a stage is
+  // for the chunk that stage writes and the next chunk's loads stay in flight.
+  for (int c = 0; c < nch; ++c) {
+    __syncthreads();          // chunk c is in LDS; every wave is done with chunk c - 1
+    __builtin_amdgcn_sched_barrier(0);
+    compute(c);
+    __builtin_amdgcn_sched_barrier(0);
+    stage(ring, c + 1);
+    fetch(ring, c + 2);
+    __builtin_amdgcn_sched_barrier(0);
   }
 
   // ---- epilogue: block max / first argmax, then sum of exp, per hidden row.  Hidden row
