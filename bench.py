@@ -57,8 +57,8 @@ METRIC = "verified tokens/sec and verify-step HBM GB/s (% peak), batch 1, k=2, 8
 PROFILED_TRAFFIC = {
     "workload": DEFAULT_WORKLOAD,
     "source": "speculative_decoding_decode_amd/csrc/lm_head.hip",
-    "sha256": "8b33548c145a50091360d78d7f6933424671955a637fdca122b5e629549f52e4",
-    "bytes_per_launch": 1345607010,
+    "sha256": "52580805c049975eb2276b93c678ea56742f4477eec73a85ca14359ed12aa27e",
+    "bytes_per_launch": 1345604470,
 }
 
 
