@@ -104,7 +104,8 @@ int spec_verify_attn(const void *q, const void *k_pool, const void *v_pool,
  *   temperature  [R] fp32 (device)
  *   logits       [R, V] fp32, or NULL when the raw logits are not wanted
  *   probs        [R, V] fp32  p, rows summing to 1
- *   H % 8 == 0 (16-byte rows for bf16).  Accumulation is fp32 (MFMA).
+ *   H % 8 == 0 (16-byte rows for bf16).  Accumulation is fp32 (dot products in the GEMVs that
+ *   serve one to three rows, MFMA otherwise).
  * ---------------------------------------------------------------------------------------- */
 size_t spec_lm_head_workspace(int R, int H, int V);
 
