@@ -133,8 +133,8 @@ __device__ __forceinline__ uint64_t wg_inclusive_scan(uint64_t v, uint64_t *sh) 
 }
 
 // Chunk c of a sequence's row: elements [c * chunk, (c + 1) * chunk), chunk = kThreads * E;
-// thread t owns the E contiguous elements starting at c * chunk + t * E (E is 4 in the common
-// case; a multiple of 4 is read as float4s).
+// thread t owns the E contiguous elements starting at c * chunk + t * E (E is 4 for one
+// sequence over a 256k vocabulary, larger for big batches; a multiple of 4 is read as float4s).
 template <int E>
 __device__ __forceinline__ void load_run(const float *__restrict__ row, int j0, int V, float (&x)[E]) {
   if (E % 4 == 0 && j0 + E <= V && (V & 3) == 0) {
