@@ -42,7 +42,6 @@ constexpr int kBlockRows = 256;                   // vocab rows per statistics b
 constexpr int kFinChunk = 4096;                   // vocab entries per finalize workgroup
 constexpr long kFinWideWGs = 2048;                // above this many, 4x larger chunks
 constexpr size_t kGemvMaxLds = 128 * 1024;        // hidden rows resident in LDS (GEMV path)
-constexpr bool kXrPrefetch = false;               // register GEMV: issue next rows before consuming
 constexpr float kLog2e = 1.4426950408889634f;
 
 template <typename T> struct Mma;
@@ -357,10 +356,53 @@ template <> struct Dot<float> {
   }
 };
 
+// DPP lane permutation within each 16-lane row (all lanes written).
+template <int Ctrl>
+__device__ __forceinline__ float dpp_perm(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), Ctrl,
+                                                               0xf, 0xf, false));
+}
+__device__ __forceinline__ float lane_value(float v, int l) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+}
+
+// Sum over the 64 lanes, the same total in every lane.  Inside each 16-lane row the partial
+// sums move by DPP permutations, which are plain VALU operands (no LDS round trip): the
+// neighbour in the quad, the other pair of the quad, the other quad of the half row (half-row
+// mirror), the other half of the row (row mirror).  The four row sums are then read out of
+// lanes 0, 16, 32, 48 and added in a fixed order.
 __device__ __forceinline__ float wave_sum(float v) {
+  v += dpp_perm<0xb1>(v);    // quad_perm [1, 0, 3, 2]
+  v += dpp_perm<0x4e>(v);    // quad_perm [2, 3, 0, 1]
+  v += dpp_perm<0x141>(v);   // row_half_mirror
+  v += dpp_perm<0x140>(v);   // row_mirror
+  return (lane_value(v, 0) + lane_value(v, 16)) + (lane_value(v, 32) + lane_value(v, 48));
+}
+
+template <int Ctrl>
+__device__ __forceinline__ void argmax_step(float &m, int &a) {
+  const float om = dpp_perm<Ctrl>(m);
+  const int oa = __builtin_amdgcn_update_dpp(0, a, Ctrl, 0xf, 0xf, false);
+  if (better(m, a, om, oa)) { m = om; a = oa; }
+}
+
+// Largest value over the 64 lanes and the lowest index holding it, in every lane: the DPP
+// steps of wave_sum inside each row, then the four row results in row order.
+__device__ __forceinline__ void wave_argmax(float &m, int &a) {
+  argmax_step<0xb1>(m, a);
+  argmax_step<0x4e>(m, a);
+  argmax_step<0x141>(m, a);
+  argmax_step<0x140>(m, a);
+  float bm = lane_value(m, 0);
+  int ba = __builtin_amdgcn_readlane(a, 0);
 #pragma unroll
-  for (int off = kWave / 2; off > 0; off >>= 1) v += __shfl_xor(v, off);
-  return v;
+  for (int q = 1; q < 4; ++q) {
+    const float om = lane_value(m, 16 * q);
+    const int oa = __builtin_amdgcn_readlane(a, 16 * q);
+    if (better(bm, ba, om, oa)) { bm = om; ba = oa; }
+  }
+  m = bm;
+  a = ba;
 }
 
 // GEMV epilogue: lane l holds the logits keep[r] of vocab row v0 + l.  Per 256-row block and
@@ -381,12 +423,7 @@ __device__ __forceinline__ void gemv_epilogue(const float (&keep)[RT], int v0, i
   for (int r = 0; r < RT; ++r) {
     float mx = vok ? keep[r] : -INFINITY;
     int ax = vok ? v : 0x7fffffff;
-#pragma unroll
-    for (int off = kWave / 2; off > 0; off >>= 1) {
-      const float om = __shfl_xor(mx, off);
-      const int oa = __shfl_xor(ax, off);
-      if (better(mx, ax, om, oa)) { mx = om; ax = oa; }
-    }
+    wave_argmax(mx, ax);
     if (lane == 0) { red_m[wave][r] = mx; red_i[wave][r] = ax; }
   }
   __syncthreads();
@@ -546,12 +583,13 @@ __global__ __launch_bounds__(kThreads) void lm_head_gemv(
 // Grid: ceil(V / 256).  Small R * H: the hidden rows live in registers (lane l holds columns
 // j * 512 + 8 l, j < NG, of every row; 1 KB of a table row per wave load), so the inner loop
 // is table loads and dot products only.  Each wave streams its 64 table rows kXrRows at a
-// time: all NG chunks of those rows are issued together and consumed in order (with PF the
-// next rows' loads are issued before the current rows are consumed).  A tail chunk past H is
-// masked to zero on both operands.
+// time: all NG chunks of those rows are issued together and consumed in order.  The first
+// rows' loads are issued before the hidden rows are read, so every wave's start overlaps the
+// hidden-row reads (the same R x H elements for every wave, served from cache) with HBM
+// latency.  A tail chunk past H is masked to zero on both operands.
 constexpr int kXrRows = 2;
 
-template <typename T, int RT, int NG, bool PF>
+template <typename T, int RT, int NG>
 __global__ __launch_bounds__(kThreads) void lm_head_gemv_xr(
     const T *__restrict__ X, const T *__restrict__ W, const float *__restrict__ temp,
     float *__restrict__ logits, float *__restrict__ probs, float2 *__restrict__ stats,
@@ -562,16 +600,9 @@ __global__ __launch_bounds__(kThreads) void lm_head_gemv_xr(
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int blk = blockIdx.x;
   const int v0 = blk * kBlockRows + wave * kRowsPerWave;
+  const bool tail_ok = (NG - 1) * CW + lane * EPL < H;   // this lane's part of the last chunk
 
   uint4 xr[RT][NG];
-#pragma unroll
-  for (int r = 0; r < RT; ++r)
-#pragma unroll
-    for (int j = 0; j < NG; ++j) {
-      const int col = j * CW + lane * EPL;
-      xr[r][j] = col < H ? *reinterpret_cast<const uint4 *>(X + (size_t)r * H + col) : uint4{0u, 0u, 0u, 0u};
-    }
-  const bool tail_ok = (NG - 1) * CW + lane * EPL < H;   // this lane's part of the last chunk
   float keep[RT];
 #pragma unroll
   for (int r = 0; r < RT; ++r) keep[r] = -INFINITY;
@@ -605,21 +636,21 @@ __global__ __launch_bounds__(kThreads) void lm_head_gemv_xr(
       }
     }
   };
-  if constexpr (PF) {
-    u32x4_t wa[kXrRows][NG], wb[kXrRows][NG];
-    load(wa, 0);
-    for (int rb = 0; rb < kRowsPerWave; rb += 2 * kXrRows) {
-      load(wb, rb + kXrRows);
-      consume(wa, rb);
-      load(wa, min(rb + 2 * kXrRows, kRowsPerWave - kXrRows));   // last one re-reads rows
-      consume(wb, rb + kXrRows);
+  u32x4_t w[kXrRows][NG];
+  load(w, 0);
+  __builtin_amdgcn_sched_barrier(0);   // the first table loads stay ahead of the hidden rows
+#pragma unroll
+  for (int r = 0; r < RT; ++r)
+#pragma unroll
+    for (int j = 0; j < NG; ++j) {
+      const int col = j * CW + lane * EPL;
+      const uint4 xv = *reinterpret_cast<const uint4 *>(X + (size_t)r * H + min(col, H - EPL));
+      xr[r][j] = col < H ? xv : uint4{0u, 0u, 0u, 0u};
     }
-  } else {
-    for (int rb = 0; rb < kRowsPerWave; rb += kXrRows) {
-      u32x4_t w[kXrRows][NG];
-      load(w, rb);
-      consume(w, rb);
-    }
+  consume(w, 0);
+  for (int rb = kXrRows; rb < kRowsPerWave; rb += kXrRows) {
+    load(w, rb);
+    consume(w, rb);
   }
   gemv_epilogue<RT>(keep, v0, lane, wave, blk, temp, logits, probs, stats, amax, V);
 }
@@ -627,7 +658,7 @@ __global__ __launch_bounds__(kThreads) void lm_head_gemv_xr(
 template <typename T, int RT, int NG>
 int launch_gemv_xr(const void *X, const void *W, const float *temp, float *logits, float *probs,
                    float2 *stats, int *amax, int H, int V, hipStream_t st) {
-  hipLaunchKernelGGL((lm_head_gemv_xr<T, RT, NG, kXrPrefetch>), dim3(spec::ceil_div(V, kBlockRows)),
+  hipLaunchKernelGGL((lm_head_gemv_xr<T, RT, NG>), dim3(spec::ceil_div(V, kBlockRows)),
                      dim3(kThreads), 0, st, static_cast<const T *>(X), static_cast<const T *>(W),
                      temp, logits, probs, stats, amax, H, V);
   return spec::launched("lm_head_gemv_xr");
