@@ -15,9 +15,10 @@
 // device from the context lengths (each workgroup and each merge wave derives the same
 // numbers).  Within a share a workgroup walks the pages of each (sequence, KV head, row chunk)
 // unit it touches: each 16-token page of K and of V is one contiguous 16*D block per head,
-// read with coalesced 16-byte loads two pages ahead and staged through LDS; scores come from
-// MFMAs (keys x rows tile), the online softmax runs in registers with wavefront shuffles, and
-// the value update is a second MFMA per 16 columns of the head dim.  For every unit it touches
+// read with coalesced, nontemporal 16-byte loads (each page is read once per call) two pages
+// ahead and staged through LDS; scores come from MFMAs (keys x rows tile), the online softmax
+// runs in registers with wavefront shuffles, and the value update is a second MFMA per 16
+// columns of the head dim.  For every unit it touches
 // the workgroup writes one partial (max, sum, unnormalised output); a second kernel merges the
 // partials of each output row with log-sum-exp weights, one workgroup per row.  All
 // exponentials are base 2 with log2(e) folded into the query scale.
@@ -343,8 +344,8 @@ __global__ __launch_bounds__(kThreads, (AttnShape<D, T, RT>::kWavesPerEU)) void 
 #pragma unroll
       for (int x = 0; x < S::kGPT; ++x) {
         const int e = real ? min(tid + x * kThreads, S::kTileG - 1) : 0;
-        kr[x] = *reinterpret_cast<const u32x4_t *>(kpool + off + e * S::kEPG);
-        vr[x] = *reinterpret_cast<const u32x4_t *>(vpool + off + e * S::kEPG);
+        kr[x] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(kpool + off + e * S::kEPG));
+        vr[x] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(vpool + off + e * S::kEPG));
       }
     };
     auto stage = [&](const u32x4_t(&kr)[S::kGPT], const u32x4_t(&vr)[S::kGPT]) __attribute__((always_inline)) {
