@@ -53,7 +53,6 @@ __device__ __host__ inline Span seq_span(int ctx, int K1, int window, int max_pa
 }
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));   // one 16-byte group
 
@@ -100,19 +99,24 @@ template <> struct AttnMma<uint16_t> {
                                                    __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
   }
   // O^T[d][row] += V^T[d][keys 4*lq + i] . P^T[keys 4*lq + i][row].  P is split into a bf16
-  // head and a bf16 tail (p = hi + lo to 2^-17 relative), two MFMAs, so the products keep
-  // fp32-level accuracy while V stays exact bf16.
+  // head and a bf16 tail (p = hi + lo to 2^-17 relative) so the products keep fp32-level
+  // accuracy while V stays exact bf16.  Both halves go through one 16x16x32 MFMA: the
+  // contraction index is only a label shared by the two operands, so this lane's 8 slots
+  // carry its 4 keys twice, (V, hi) in the first four and (V, lo) in the last four, and no
+  // lane needs another lane's probabilities.
   __device__ static __forceinline__ f32x4_t pv(const uint16_t *vs, int str, int dcol, int lq,
                                                const float (&p)[4], f32x4_t c) {
-    bf16x4_t a, hi, lo;
+    bf16x8_t a, b;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      a[i] = __builtin_bit_cast(__bf16, vs[(4 * lq + i) * str + dcol]);
-      hi[i] = static_cast<__bf16>(p[i]);
-      lo[i] = static_cast<__bf16>(p[i] - static_cast<float>(hi[i]));
+      const __bf16 v = __builtin_bit_cast(__bf16, vs[(4 * lq + i) * str + dcol]);
+      const __bf16 hi = static_cast<__bf16>(p[i]);
+      a[i] = v;
+      a[i + 4] = v;
+      b[i] = hi;
+      b[i + 4] = static_cast<__bf16>(p[i] - static_cast<float>(hi));
     }
-    c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, hi, c, 0, 0, 0);
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, lo, c, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
   }
 };
 template <> struct AttnMma<float> {
