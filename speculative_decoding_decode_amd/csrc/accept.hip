@@ -91,10 +91,6 @@ __device__ int accepted_count(const int32_t *__restrict__ draft, const float *__
   return min(k, __builtin_ctzll(~acc));
 }
 
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
-  const uint32_t lo = __shfl_xor((uint32_t)v, m), hi = __shfl_xor((uint32_t)(v >> 32), m);
-  return ((uint64_t)hi << 32) | lo;
-}
 __device__ __forceinline__ uint64_t shfl_up_u64(uint64_t v, int d) {
   const uint32_t lo = __shfl_up((uint32_t)v, d), hi = __shfl_up((uint32_t)(v >> 32), d);
   return ((uint64_t)hi << 32) | lo;
@@ -103,8 +99,7 @@ __device__ __forceinline__ uint64_t shfl_up_u64(uint64_t v, int d) {
 // Sum over the workgroup (integers: exact in any order); sh holds kThreads / 64 entries.
 __device__ __forceinline__ uint64_t wg_sum(uint64_t v, uint64_t *sh) {
   const int lane = threadIdx.x & (spec::kWave - 1), wave = threadIdx.x / spec::kWave;
-#pragma unroll
-  for (int m = spec::kWave / 2; m > 0; m >>= 1) v += shfl_xor_u64(v, m);
+  v = spec::wave_sum(v);
   if (lane == 0) sh[wave] = v;
   __syncthreads();
   uint64_t t = 0;

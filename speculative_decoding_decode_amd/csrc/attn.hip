@@ -147,26 +147,6 @@ template <> struct AttnMma<float> {
 // computes of unit u = b * U + j is stored at partial index w + u (consecutive pieces along
 // the list raise w, u or both, so the index is unique and below nwg + B * U).
 
-__device__ __forceinline__ int wave_sum_i(int v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
-}
-__device__ __forceinline__ int wave_max_i(int v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o));
-  return v;
-}
-__device__ __forceinline__ float wave_max_f(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
-}
-__device__ __forceinline__ float wave_sum_f(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
-}
 __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
@@ -232,7 +212,7 @@ __device__ __forceinline__ long long pages_before(const int32_t *__restrict__ ct
   long long Pb = __shfl(pl.incl0, spec::kWave - 1);
   for (int c0 = spec::kWave; c0 < b; c0 += spec::kWave) {
     const int bb = min(c0 + lane, b - 1);
-    Pb += wave_sum_i(c0 + lane < b ? seq_span(ctx_lens[bb], K1, window, max_pages).np : 0);
+    Pb += spec::wave_sum(c0 + lane < b ? seq_span(ctx_lens[bb], K1, window, max_pages).np : 0);
   }
   return uni64(Pb);
 }
@@ -567,7 +547,7 @@ __global__ __launch_bounds__(CW * 64) void attn_combine(
     const float2 x = mlp[(size_t)min(c0 + lane, n - 1) * rstride];
     if (c0 + lane < n) mx = fmaxf(mx, x.x);
   }
-  const float m = wave_max_f(mx);
+  const float m = spec::wave_max(mx);
 
   // weights of this wave's pieces: lane t of a round holds piece wave + 4 * (t0 + t)
   vecc_t a = vecc_t(0.f);
@@ -592,7 +572,7 @@ __global__ __launch_bounds__(CW * 64) void attn_combine(
       }
     }
   }
-  l = wave_sum_f(l);
+  l = spec::wave_sum(l);
   if (wave > 0) {
     *reinterpret_cast<vecc_t *>(&red_acc[wave - 1][lane * NC]) = a;
     if (lane == 0) red_l[wave] = l;

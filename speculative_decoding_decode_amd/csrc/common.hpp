@@ -47,6 +47,88 @@ __device__ __forceinline__ void unpack16(const uint4 &v, float (&f)[8], uint16_t
   f[4] = bf16_lo(v.z); f[5] = bf16_hi(v.z); f[6] = bf16_lo(v.w); f[7] = bf16_hi(v.w);
 }
 
+// ---------------------------------------------------------------- device: wave reductions
+// Reductions over the 64 lanes of a wave, the result in every lane.  Inside each 16-lane row
+// the values move by DPP permutations, which are plain VALU operands (no LDS round trip):
+// the neighbour in the quad, the other pair of the quad, the other quad of the half row
+// (half-row mirror), the other half of the row (row mirror).  The four row results are then
+// read from lanes 0, 16, 32 and 48 and combined as (r0 op r1) op (r2 op r3), so the result is
+// the same bits in every lane and on every call.  All 64 lanes must be active.
+template <int Ctrl>
+__device__ __forceinline__ int dpp_move(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, Ctrl, 0xf, 0xf, false);
+}
+template <int Ctrl>
+__device__ __forceinline__ float dpp_move(float v) {
+  return __builtin_bit_cast(float, dpp_move<Ctrl>(__builtin_bit_cast(int, v)));
+}
+template <int Ctrl>
+__device__ __forceinline__ uint64_t dpp_move(uint64_t v) {
+  const uint32_t lo = (uint32_t)dpp_move<Ctrl>((int)(uint32_t)v);
+  const uint32_t hi = (uint32_t)dpp_move<Ctrl>((int)(uint32_t)(v >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ int lane_value(int v, int l) { return __builtin_amdgcn_readlane(v, l); }
+__device__ __forceinline__ float lane_value(float v, int l) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+}
+__device__ __forceinline__ uint64_t lane_value(uint64_t v, int l) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+template <typename T, typename Op>
+__device__ __forceinline__ T wave_reduce(T v, Op op) {
+  v = op(v, dpp_move<0xb1>(v));    // quad_perm [1, 0, 3, 2]
+  v = op(v, dpp_move<0x4e>(v));    // quad_perm [2, 3, 0, 1]
+  v = op(v, dpp_move<0x141>(v));   // row_half_mirror
+  v = op(v, dpp_move<0x140>(v));   // row_mirror
+  return op(op(lane_value(v, 0), lane_value(v, 16)), op(lane_value(v, 32), lane_value(v, 48)));
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+  return wave_reduce(v, [](float x, float y) { return x + y; });
+}
+__device__ __forceinline__ int wave_sum(int v) {
+  return wave_reduce(v, [](int x, int y) { return x + y; });
+}
+__device__ __forceinline__ uint64_t wave_sum(uint64_t v) {
+  return wave_reduce(v, [](uint64_t x, uint64_t y) { return x + y; });
+}
+__device__ __forceinline__ float wave_max(float v) {
+  return wave_reduce(v, [](float x, float y) { return fmaxf(x, y); });
+}
+__device__ __forceinline__ int wave_max(int v) {
+  return wave_reduce(v, [](int x, int y) { return max(x, y); });
+}
+
+// (om, oa) beats (m, a): larger value, or the same value at a lower index.
+__device__ __forceinline__ bool first_max_better(float m, int a, float om, int oa) {
+  return om > m || (om == m && oa < a);
+}
+
+// Largest value over the wave and the lowest index holding it, in every lane.
+__device__ __forceinline__ void wave_argmax(float &m, int &a) {
+  auto step = [&](float om, int oa) {
+    if (first_max_better(m, a, om, oa)) { m = om; a = oa; }
+  };
+  step(dpp_move<0xb1>(m), dpp_move<0xb1>(a));
+  step(dpp_move<0x4e>(m), dpp_move<0x4e>(a));
+  step(dpp_move<0x141>(m), dpp_move<0x141>(a));
+  step(dpp_move<0x140>(m), dpp_move<0x140>(a));
+  float bm = lane_value(m, 0);
+  int ba = lane_value(a, 0);
+#pragma unroll
+  for (int q = 1; q < 4; ++q) {
+    const float om = lane_value(m, 16 * q);
+    const int oa = lane_value(a, 16 * q);
+    if (first_max_better(bm, ba, om, oa)) { bm = om; ba = oa; }
+  }
+  m = bm;
+  a = ba;
+}
+
 }  // namespace spec
 
 #define SPEC_REQUIRE(cond, code, ...)                 \

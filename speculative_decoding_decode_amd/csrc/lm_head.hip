@@ -32,6 +32,8 @@
 namespace {
 
 using spec::kWave;
+using spec::wave_argmax;
+using spec::wave_sum;
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));   // one 16-byte slot
@@ -70,7 +72,7 @@ __device__ __forceinline__ u32x4_t load_stream(const void *p) {
 }
 
 __device__ __forceinline__ bool better(float m, int a, float om, int oa) {
-  return om > m || (om == m && oa < a);
+  return spec::first_max_better(m, a, om, oa);
 }
 
 // Contraction + per-block statistics for every R the GEMVs do not take.  512 threads, two
@@ -355,55 +357,6 @@ template <> struct Dot<float> {
     return s;
   }
 };
-
-// DPP lane permutation within each 16-lane row (all lanes written).
-template <int Ctrl>
-__device__ __forceinline__ float dpp_perm(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), Ctrl,
-                                                               0xf, 0xf, false));
-}
-__device__ __forceinline__ float lane_value(float v, int l) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
-}
-
-// Sum over the 64 lanes, the same total in every lane.  Inside each 16-lane row the partial
-// sums move by DPP permutations, which are plain VALU operands (no LDS round trip): the
-// neighbour in the quad, the other pair of the quad, the other quad of the half row (half-row
-// mirror), the other half of the row (row mirror).  The four row sums are then read out of
-// lanes 0, 16, 32, 48 and added in a fixed order.
-__device__ __forceinline__ float wave_sum(float v) {
-  v += dpp_perm<0xb1>(v);    // quad_perm [1, 0, 3, 2]
-  v += dpp_perm<0x4e>(v);    // quad_perm [2, 3, 0, 1]
-  v += dpp_perm<0x141>(v);   // row_half_mirror
-  v += dpp_perm<0x140>(v);   // row_mirror
-  return (lane_value(v, 0) + lane_value(v, 16)) + (lane_value(v, 32) + lane_value(v, 48));
-}
-
-template <int Ctrl>
-__device__ __forceinline__ void argmax_step(float &m, int &a) {
-  const float om = dpp_perm<Ctrl>(m);
-  const int oa = __builtin_amdgcn_update_dpp(0, a, Ctrl, 0xf, 0xf, false);
-  if (better(m, a, om, oa)) { m = om; a = oa; }
-}
-
-// Largest value over the 64 lanes and the lowest index holding it, in every lane: the DPP
-// steps of wave_sum inside each row, then the four row results in row order.
-__device__ __forceinline__ void wave_argmax(float &m, int &a) {
-  argmax_step<0xb1>(m, a);
-  argmax_step<0x4e>(m, a);
-  argmax_step<0x141>(m, a);
-  argmax_step<0x140>(m, a);
-  float bm = lane_value(m, 0);
-  int ba = __builtin_amdgcn_readlane(a, 0);
-#pragma unroll
-  for (int q = 1; q < 4; ++q) {
-    const float om = lane_value(m, 16 * q);
-    const int oa = __builtin_amdgcn_readlane(a, 16 * q);
-    if (better(bm, ba, om, oa)) { bm = om; ba = oa; }
-  }
-  m = bm;
-  a = ba;
-}
 
 // GEMV epilogue: lane l holds the logits keep[r] of vocab row v0 + l.  Per 256-row block and
 // hidden row: (max, sum of exp) and the first argmax into stats / amax; exp((z - block max) / T)

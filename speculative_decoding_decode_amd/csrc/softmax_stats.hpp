@@ -11,8 +11,8 @@
 //
 // Reduction order (fixed, so every workgroup that reduces a row gets the same bits): thread t
 // merges blocks t, t + 256, t + 512, ... in that order; the 64 lanes of a wave are combined by
-// an xor butterfly (both partners of every step add the same two values, so all lanes end with
-// the same bits); the four waves' results are added in wave order.
+// the fixed DPP-and-readlane pattern of spec::wave_reduce (the same bits in every lane); the
+// four waves' results are added in wave order.
 #pragma once
 
 #include "common.hpp"
@@ -26,7 +26,7 @@ constexpr int kStatsPerThread = 4;     // blocks per thread and pass (V <= 26214
 constexpr float kStatLog2e = 1.4426950408889634f;
 
 __device__ __forceinline__ bool stat_better(float m, int a, float om, int oa) {
-  return om > m || (om == m && oa < a);
+  return first_max_better(m, a, om, oa);
 }
 
 // log2(e) / T, or 0 for a greedy row (T <= 0).
@@ -65,20 +65,6 @@ __device__ __forceinline__ RowPartial stat_partial(const float2 *__restrict__ st
   return w;
 }
 
-__device__ __forceinline__ void stat_wave_maxarg(float &m, int &a) {
-#pragma unroll
-  for (int off = kWave / 2; off > 0; off >>= 1) {
-    const float om = __shfl_xor(m, off);
-    const int oa = __shfl_xor(a, off);
-    if (stat_better(m, a, om, oa)) { m = om; a = oa; }
-  }
-}
-
-__device__ __forceinline__ float stat_wave_sum(float v) {
-#pragma unroll
-  for (int off = kWave / 2; off > 0; off >>= 1) v += __shfl_xor(v, off);
-  return v;
-}
 
 // Global (max, first argmax) and sum of row partials over the workgroup, for NR rows at once
 // (rows >= nrows are ignored).  sm / si / ss: LDS of kStatWaves * NR entries each.  Every
@@ -94,7 +80,7 @@ __device__ __forceinline__ void stat_reduce(const RowPartial (&w)[NR], float (&c
   for (int i = 0; i < NR; ++i) {
     m[i] = w[i].m;
     a[i] = w[i].a;
-    if (i < nrows) stat_wave_maxarg(m[i], a[i]);
+    if (i < nrows) wave_argmax(m[i], a[i]);
     if (lane == 0) { sm[wave * NR + i] = m[i]; si[wave * NR + i] = a[i]; }
   }
   __syncthreads();
@@ -108,7 +94,7 @@ __device__ __forceinline__ void stat_reduce(const RowPartial (&w)[NR], float (&c
     gmax[i] = gm;
     garg[i] = ga;
     float v = w[i].m == -INFINITY ? 0.f : w[i].s * exp2f((w[i].m - gm) * c[i]);
-    if (i < nrows) v = stat_wave_sum(v);
+    if (i < nrows) v = wave_sum(v);
     if (lane == 0) ss[wave * NR + i] = v;
   }
   __syncthreads();
