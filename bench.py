@@ -57,8 +57,8 @@ METRIC = "verified tokens/sec and verify-step HBM GB/s (% peak), batch 1, k=2, 8
 PROFILED_TRAFFIC = {
     "workload": DEFAULT_WORKLOAD,
     "source": "speculative_decoding_decode_amd/csrc/lm_head.hip",
-    "sha256": "f86be7073931d43e2cc5b99cb6bc10c14bb1d79e3f80206d8f2f2e4982fcc150",
-    "bytes_per_launch": 1345639389,
+    "sha256": "1b003ce544e3888b2b0d33cf798b4ffacc91bf096c4252d29c47e6939f1d1dec",
+    "bytes_per_launch": 1345637740,
 }
 
 
