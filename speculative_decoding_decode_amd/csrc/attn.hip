@@ -549,7 +549,7 @@ __global__ __launch_bounds__(CW * 64) void attn_combine(
   }
   const float m = spec::wave_max(mx);
 
-  // weights of this wave's pieces: lane t of a round holds piece wave + 4 * (t0 + t)
+  // weights of this wave's pieces: lane t of a round holds piece wave + CW * (t0 + t)
   vecc_t a = vecc_t(0.f);
   float l = 0.f;
   for (int t0 = 0; t0 < nmine; t0 += spec::kWave) {
