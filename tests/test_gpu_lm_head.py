@@ -72,6 +72,24 @@ def test_greedy_ties_take_first_index(R):
     assert pc[:, 7].tolist() == [1.0] * R and float(pc.sum()) == float(R)
 
 
+@pytest.mark.parametrize("R", [2, 3, 20])     # both GEMVs' epilogue and the MFMA path
+@pytest.mark.parametrize("ties", [[45, 13, 2, 3, 130], [50, 33, 17], [1, 0], [255, 64, 128, 192],
+                                  [63, 62, 61, 48, 47, 31, 16, 15]])
+def test_greedy_ties_within_a_wave(R, ties):
+    # equal maxima on lanes of one 64-row wave in different quads, half rows and rows of 16,
+    # and across the waves of one block: the lowest index wins every reduction step
+    d = dev()
+    x = torch.ones(R, 16, dtype=torch.float32)
+    W = torch.zeros(600, 16, dtype=torch.float32)
+    W[ties] = 1.0
+    W[400] = 0.5                                   # a smaller value elsewhere
+    t = torch.zeros(R, device=d)
+    _, p = sv.lm_head(x.to(d), W.to(d), t)
+    pc = p.cpu()
+    want = min(ties)
+    assert pc[:, want].tolist() == [1.0] * R and float(pc.sum()) == float(R)
+
+
 @pytest.mark.parametrize("name", ["b1_k2_sliding256_8k", "b1_k4_global512_32k"])
 def test_full_size_batch1(name):
     w = WORKLOADS[name]
