@@ -79,7 +79,8 @@ const char *spec_last_error(void);
  *   page_table  [B, max_pages_per_seq] int32  physical page ids
  *   ctx_lens    [B] int32                     tokens in each cache, the K1 new ones included
  *   out         [B, K1, Hq, D] fp32
- *   D in {64, 128, 256, 512}; page_size == 16; Hq % Hkv == 0; K1 in [1, 64].
+ *   D in {64, 128, 256, 512}; page_size == 16; Hq % Hkv == 0; K1 in [1, 64];
+ *   B * K1 * Hq < 2^31 (SPEC_EUNSUPPORTED otherwise).
  *
  * Device-data preconditions: K1 <= ctx_lens[b] <= max_pages_per_seq * page_size.  ctx_lens
  * beyond that bound are clamped to it; a page id outside [0, num_pages) hides the keys on
@@ -104,8 +105,8 @@ int spec_verify_attn(const void *q, const void *k_pool, const void *v_pool,
  *   temperature  [R] fp32 (device)
  *   logits       [R, V] fp32, or NULL when the raw logits are not wanted
  *   probs        [R, V] fp32  p, rows summing to 1
- *   H % 8 == 0 (16-byte rows for bf16).  Accumulation is fp32 (dot products in the GEMVs that
- *   serve one to three rows, MFMA otherwise).
+ *   H % 8 == 0 (16-byte rows for bf16); R <= 65535.  Accumulation is fp32 (dot products in
+ *   the GEMVs that serve one to three rows, MFMA otherwise).
  * ---------------------------------------------------------------------------------------- */
 size_t spec_lm_head_workspace(int R, int H, int V);
 
@@ -138,7 +139,7 @@ int spec_profile_lm_head(void *start_event, void *stop_event);
  *   uniforms    [B, K1]    fp32  in [0, 1): k acceptance tests, then the one draw
  *   n_accepted  [B] int32  (out) 0..k
  *   tokens      [B, K1] int32 (out) d_0 .. d_{n-1}, y, then -1 padding
- *   k in [0, 63].
+ *   k in [0, 63]; B <= 65535.
  *
  * Device-data preconditions: p and q rows are distributions (non-negative, summing to 1).  A
  * draft id outside [0, V) is rejected without being read.  A p row whose weights are all 0
@@ -180,7 +181,7 @@ int spec_accept_philox(const int32_t *draft, const float *q, const float *p, uin
  *                   ctx_lens[b] - K1 + i of each sequence's pages (ctx_lens already counts
  *                   them, as in spec_verify_attn).  Positions outside the page table or on a
  *                   page id outside [0, num_pages) are skipped.  D * element size must be a
- *                   multiple of 16 bytes.
+ *                   multiple of 16 bytes; B * K1 * Hkv < 2^31.
  *   spec_kv_commit  after spec_accept: ctx_lens[b] -= K1 - 1 - n_accepted[b] (n clamped to
  *                   [0, K1 - 1]), keeping the last committed token and the n accepted drafts;
  *                   the rejected slots are overwritten by the next append, and the correction

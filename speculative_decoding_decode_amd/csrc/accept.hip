@@ -305,6 +305,8 @@ int accept_run(const char *who, const int32_t *draft, const float *q, const floa
                int k, int V, void *workspace, size_t workspace_bytes, void *stream) {
   SPEC_REQUIRE(B > 0 && V > 0 && k >= 0, SPEC_EINVAL, "%s: B=%d k=%d V=%d out of range", who, B,
                k, V);
+  SPEC_REQUIRE(B <= 65535, SPEC_EUNSUPPORTED,
+               "%s: B=%d sequences exceed 65535 (grid y of the chunk kernel)", who, B);
   SPEC_REQUIRE(k <= kMaxK, SPEC_EUNSUPPORTED, "%s: k=%d exceeds %d (one wave per sequence)", who,
                k, kMaxK);
   SPEC_REQUIRE((long)V <= (long)kMaxE * kThreads * kThreads, SPEC_EUNSUPPORTED,

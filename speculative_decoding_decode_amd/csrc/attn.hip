@@ -701,6 +701,8 @@ int check_shape(int B, int K1, int Hq, int Hkv, int D, int page_size, int max_pa
   SPEC_REQUIRE(Hq % Hkv == 0, SPEC_EINVAL, "spec_verify_attn: Hq=%d not a multiple of Hkv=%d", Hq, Hkv);
   SPEC_REQUIRE(window >= 0, SPEC_EINVAL, "spec_verify_attn: window=%d is negative", window);
   SPEC_REQUIRE(K1 <= 64, SPEC_EUNSUPPORTED, "spec_verify_attn: K1=%d exceeds 64", K1);
+  SPEC_REQUIRE((long long)B * K1 * Hq <= 0x7fffffffLL, SPEC_EUNSUPPORTED,
+               "spec_verify_attn: B*K1*Hq output rows exceed one grid");
   SPEC_REQUIRE(D == 64 || D == 128 || D == 256 || D == 512, SPEC_EUNSUPPORTED,
                "spec_verify_attn: head dim %d not in {64, 128, 256, 512}", D);
   SPEC_REQUIRE(page_size == kPage, SPEC_EUNSUPPORTED, "spec_verify_attn: page_size=%d, only 16", page_size);

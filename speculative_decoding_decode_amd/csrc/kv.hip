@@ -59,6 +59,8 @@ extern "C" int spec_kv_append(const void *k_new, const void *v_new, void *k_pool
   SPEC_REQUIRE(B > 0 && K1 > 0 && Hkv > 0 && D > 0 && num_pages > 0 && max_pages_per_seq > 0,
                SPEC_EINVAL, "spec_kv_append: sizes must be positive");
   SPEC_REQUIRE(page_size == kPage, SPEC_EUNSUPPORTED, "spec_kv_append: page_size=%d, only 16", page_size);
+  SPEC_REQUIRE((long long)B * K1 * Hkv <= 0x7fffffffLL, SPEC_EUNSUPPORTED,
+               "spec_kv_append: B*K1*Hkv rows exceed one grid");
   SPEC_REQUIRE(dtype == SPEC_F32 || dtype == SPEC_BF16, SPEC_EUNSUPPORTED,
                "spec_kv_append: unsupported dtype %d", (int)dtype);
   const int epg = dtype == SPEC_BF16 ? 8 : 4;

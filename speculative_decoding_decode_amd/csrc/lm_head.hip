@@ -45,6 +45,7 @@ constexpr int kFinChunk = 4096;                   // vocab entries per finalize 
 constexpr long kFinWideWGs = 2048;                // above this many, 4x larger chunks
 constexpr size_t kGemvMaxLds = 128 * 1024;        // hidden rows resident in LDS (GEMV path)
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kMaxRows = 65535;                   // rows per call (grid y of the finalize)
 
 template <typename T> struct Mma;
 template <> struct Mma<uint16_t> {  // bf16 table: one 16x16x32 MFMA per 16-byte fragment
@@ -810,6 +811,9 @@ int lm_head_check(const void *hidden, const void *weight, const float *temperatu
   SPEC_REQUIRE(dtype == SPEC_F32 || dtype == SPEC_BF16, SPEC_EUNSUPPORTED,
                "%s: unsupported dtype %d", who, (int)dtype);
   SPEC_REQUIRE(H % 8 == 0, SPEC_EUNSUPPORTED, "%s: H=%d must be a multiple of 8", who, H);
+  SPEC_REQUIRE(R <= kMaxRows, SPEC_EUNSUPPORTED,
+               "%s: R=%d rows exceed %d (one grid row of the softmax finalize per row)", who, R,
+               kMaxRows);
   SPEC_REQUIRE(aligned16(hidden) && aligned16(weight) && aligned16(probs) &&
                    (logits == nullptr || aligned16(logits)),
                SPEC_EINVAL, "%s: hidden, weight, probs and logits need 16-byte alignment", who);

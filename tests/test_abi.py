@@ -80,6 +80,8 @@ def test_attn_argument_errors(lib):
     assert b"alignment" in lib.spec_last_error()
     assert attn_call(lib, wsb=16) == EWS
     assert b"workspace" in lib.spec_last_error()
+    assert attn_call(lib, B=1 << 25, K1=8, Hq=16, Hkv=4) == EUNSUP   # 2^32 output rows
+    assert b"grid" in lib.spec_last_error()
 
 
 def test_lm_head_argument_errors(lib):
@@ -96,6 +98,8 @@ def test_lm_head_argument_errors(lib):
     assert call(logits=FAKE + 8) == EINVAL
     assert call(wsb=8) == EWS
     assert call(ws=None) == EWS
+    assert call(R=65536) == EUNSUP
+    assert b"65535" in lib.spec_last_error()
 
 
 def test_accept_argument_errors(lib):
@@ -110,6 +114,26 @@ def test_accept_argument_errors(lib):
     assert call(q=None) == EINVAL
     assert call(k=0, q=None, d=None, wsb=1) == EWS   # q may be NULL when k == 0
     assert call(wsb=1) == EWS
+    assert call(B=65536) == EUNSUP
+    assert b"65535" in lib.spec_last_error()
+
+
+def test_kv_argument_errors(lib):
+    def append(**kw):
+        a = dict(kn=FAKE, vn=FAKE, kp=FAKE, vp=FAKE, table=FAKE, ctx=FAKE, B=1, K1=3, Hkv=2,
+                 D=256, ps=16, P=100, maxp=64, dtype=1)
+        a.update(kw)
+        return lib.spec_kv_append(*a.values(), None)
+
+    assert append(kn=None) == EINVAL
+    assert append(B=0) == EINVAL
+    assert append(ps=32) == EUNSUP
+    assert append(D=12) == EUNSUP
+    assert append(kp=FAKE + 8) == EINVAL
+    assert append(B=1 << 26, K1=8, Hkv=4) == EUNSUP
+    assert b"grid" in lib.spec_last_error()
+    assert lib.spec_kv_commit(None, FAKE, 1, 3, None) == EINVAL
+    assert lib.spec_kv_commit(FAKE, FAKE, 0, 3, None) == EINVAL
 
 
 def test_product_path_never_touches_the_oracle():
