@@ -57,8 +57,8 @@ METRIC = "verified tokens/sec and verify-step HBM GB/s (% peak), batch 1, k=2, 8
 PROFILED_TRAFFIC = {
     "workload": DEFAULT_WORKLOAD,
     "source": "speculative_decoding_decode_amd/csrc/lm_head.hip",
-    "sha256": "1b003ce544e3888b2b0d33cf798b4ffacc91bf096c4252d29c47e6939f1d1dec",
-    "bytes_per_launch": 1345637740,
+    "sha256": "77e82faf148164d39694c628d9861f0f041d3b327d03aafd91cade7b6435fdf4",
+    "bytes_per_launch": 1345639734,
 }
 
 
