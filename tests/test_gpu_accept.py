@@ -67,6 +67,27 @@ def test_edge_cases():
     assert n[0] == 0 and n[1] == 1 and n[2] == k and n[3] == 0
 
 
+def test_maximum_k():
+    # k = 63 (K1 = 64 uniforms per sequence, one wave lane per draft): sequences whose drafter
+    # equals the target accept all 63 drafts and draw the bonus token; the others stop at
+    # their first rejection anywhere along the 63 positions
+    rng = np.random.default_rng(9)
+    B, k, V = 6, 63, 300
+    p = rng.dirichlet(np.ones(V) * 0.5, size=(B, k + 1)).astype(np.float32)
+    q = rng.dirichlet(np.ones(V) * 0.5, size=(B, k)).astype(np.float32)
+    q[:2] = p[:2, :k]                                   # q == p: every draft accepted
+    mix = 0.9 * p[2:4, :k] + 0.1 * q[2:4]               # close drafter: long accepted runs
+    q[2:4] = (mix / mix.sum(-1, keepdims=True)).astype(np.float32)
+    draft = np.empty((B, k), np.int32)
+    for b in range(B):
+        for i in range(k):
+            pr = q[b, i].astype(np.float64)
+            draft[b, i] = rng.choice(V, p=pr / pr.sum())
+    u = rng.random((B, k + 1), dtype=np.float32)
+    n = compare(draft, q, p, u, "k = 63")
+    assert n[0] == k and n[1] == k
+
+
 def test_k_zero_plain_sampling():
     rng = np.random.default_rng(6)
     B, V = 64, 3000

@@ -77,6 +77,18 @@ def test_ragged_small(dtype, hq, hkv, d, window, k):
     check(inp, dtype, f"ragged small {dtype} hq{hq}/hkv{hkv} d{d} w{window} k{k}")
 
 
+@pytest.mark.parametrize("dtype,hq,hkv,d,window", [
+    ("bf16", 8, 2, 128, 0), ("bf16", 8, 2, 512, 100), ("f32", 4, 4, 64, 0)])
+def test_maximum_k1(dtype, hq, hkv, d, window):
+    # K1 = 64 verified positions, the most the call takes: 256 query rows per KV head (eight
+    # row chunks of 32) at G = 4, two chunks at G = 1
+    w = small_workload(dtype, hq, hkv, d, window, 63)
+    ctx = np.array([64, 300, 1000], dtype=np.int32)
+    table, P = gen.page_tables(w, ctx, max_pages=64)
+    inp = attn_inputs(w, 0, dev(), ctx=ctx, table=table, num_pages=P)
+    check(inp, dtype, f"K1 = 64 {dtype} hq{hq}/hkv{hkv} d{d} w{window}")
+
+
 def test_context_clamped_to_table():
     w = small_workload("bf16", 8, 2, 256, 0, 2, batch=2)
     ctx = np.array([64, 64], dtype=np.int32)
