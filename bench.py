@@ -57,8 +57,8 @@ METRIC = "verified tokens/sec and verify-step HBM GB/s (% peak), batch 1, k=2, 8
 PROFILED_TRAFFIC = {
     "workload": DEFAULT_WORKLOAD,
     "source": "speculative_decoding_decode_amd/csrc/lm_head.hip",
-    "sha256": "77e82faf148164d39694c628d9861f0f041d3b327d03aafd91cade7b6435fdf4",
-    "bytes_per_launch": 1345639734,
+    "sha256": "b1fe29994735139cba90a8a05c8a3862cae4aead27ed2c3f574a01e7272087af",
+    "bytes_per_launch": 1348163083,
 }
 
 

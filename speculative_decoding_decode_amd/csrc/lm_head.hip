@@ -7,16 +7,13 @@
 // from memory (same guide, introduction).  At R = 3..96 rows the kernel is a stream over the
 // V x H table: every table element is read once from HBM and used R times.
 //
-// Design (gfx950).  Three contraction kernels share one softmax finalize; which one runs was
-// set by timing all three on MI355X at 1..8 rows:
-//  * R <= 3 rows over rows of at most 5 KB (batch-1 verification): a bandwidth-bound GEMV
-//    with the hidden rows in registers.  Each wave owns 64 table rows and streams them two at
-//    a time; every load instruction reads 1 KB of contiguous table with a nontemporal load (the
-//    table is used once per call) and products accumulate in fp32 with v_dot2_f32_bf16 (fp32
-//    tables: FMAs); a wave reduction gives each row's logit.  About 6.5 TB/s in the step.
-//  * other R <= 2: the same stream as (row pair, 1 KB column chunk) items with the hidden rows
-//    in LDS (one LDS read serves two table rows); when the hidden rows fill LDS the loads run a
-//    tile ahead of the compute.
+// Design (gfx950).  Two contraction kernels share one softmax finalize; which one runs was
+// set by timing both on MI355X at 1..8 rows:
+//  * R <= 3 rows (batch-1 verification): a bandwidth-bound GEMV.  Each wave owns 64 table rows
+//    and walks the hidden dimension in 128-byte chunks, eight rows per load instruction, with
+//    nontemporal loads (the table is used once per call); every lane accumulates its slot of
+//    eight rows in fp32 with v_dot2_f32_bf16 (fp32 tables: FMAs) and a three-step DPP
+//    reduction inside each 8-lane group gives each row's logit.  About 6.5 TB/s in the step.
 //  * every other R: MFMA (v_mfma_f32_16x16x32_bf16; fp32 tables: four v_mfma_f32_16x16x4_f32).
 //    One workgroup = 512 vocab rows against up to 96 hidden rows per pass; chunks of 128 bytes
 //    of every row are loaded as 128-byte contiguous runs per row and transposed into MFMA
@@ -43,7 +40,6 @@ constexpr int kWaves = kThreads / kWave;          // 4
 constexpr int kBlockRows = 256;                   // vocab rows per statistics block
 constexpr int kFinChunk = 4096;                   // vocab entries per finalize workgroup
 constexpr long kFinWideWGs = 2048;                // above this many, 4x larger chunks
-constexpr size_t kGemvMaxLds = 128 * 1024;        // hidden rows resident in LDS (GEMV path)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kMaxRows = 65535;                   // rows per call (grid y of the finalize)
 
@@ -333,9 +329,8 @@ __global__ __launch_bounds__(kMmaThreads, 1) void lm_head_mfma(
 // ------------------------------------------------------------------------- small-R GEMV path
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
-constexpr int kGemvMaxR = 2;     // above this the MFMA contraction streams faster
+constexpr int kGemvMaxR = 3;         // above this the MFMA contraction streams faster
 constexpr int kRowsPerWave = 64;     // one table row per lane in the epilogue
-constexpr int kTile = 2;             // items (row pair x 1 KB chunk) per prefetch tile
 
 template <typename T> struct Dot;
 template <> struct Dot<uint16_t> {
@@ -411,263 +406,118 @@ __device__ __forceinline__ void gemv_epilogue(const float (&keep)[RT], int v0, i
     if (vok && !greedy[r]) probs[(size_t)r * V + v] = ex[r];
 }
 
-// Grid: ceil(V / 256).  RT = R (rows of hidden states), 1..8.
-template <typename T, int RT, bool Deep>
-__global__ __launch_bounds__(kThreads) void lm_head_gemv(
+// Grid: ceil(V / 256).  The GEMV for R <= 3 rows and any H.  A wave owns 64 table rows and
+// walks the hidden dimension in chunks of 128 bytes: one load instruction covers 8 rows x 128
+// contiguous bytes (lane 8 g + s reads 16-byte slot s of row t + 8 g of the wave's 64, for
+// load t = 0..7), so a chunk of the wave's 64 rows is eight nontemporal loads and the same
+// 16-byte slot of the R hidden rows (read by every wave, cache-resident).  Every lane keeps
+// 8 x R partial dot products (v_dot2_f32_bf16; fp32 tables: FMAs) across all chunks, so the
+// only cross-lane work is one three-step DPP reduction inside each 8-lane group at the end
+// (quad swaps and the half-row mirror), after which lane 8 g + t holds row t + 8 g's logits.
+// Two chunks are in flight per wave; a fetch past the last chunk reads one valid 16-byte
+// location, and slots past H are zeroed on both operands.  (At three rows one register is
+// spilled around the main loop, not inside it.)
+template <typename T, int RT>
+__global__ __launch_bounds__(kThreads, 4) void lm_head_gemv(
     const T *__restrict__ X, const T *__restrict__ W, const float *__restrict__ temp,
     float *__restrict__ logits, float *__restrict__ probs, float2 *__restrict__ stats,
     int *__restrict__ amax, int H, int V) {
   using Dt = Dot<T>;
   constexpr int EPL = Dt::kEPL;
-  constexpr int CW = kWave * EPL;                   // elements per 1 KB chunk
-  extern __shared__ __align__(16) unsigned char smem[];
-  T *xs = reinterpret_cast<T *>(smem);               // [RT][H]
-
+  constexpr int CE = 8 * EPL;                       // elements per 128-byte chunk
+  constexpr int kRowsPerLoad = 8;
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int g = lane >> 3, sl = lane & 7;
   const int blk = blockIdx.x;
   const int v0 = blk * kBlockRows + wave * kRowsPerWave;
-  for (int e = threadIdx.x; e < RT * (H / EPL); e += kThreads)
-    reinterpret_cast<uint4 *>(xs)[e] = reinterpret_cast<const uint4 *>(X)[e];
-  __syncthreads();
+  // Element offsets from the wave's first row (below 64 H: 32 bits); rows past V are clamped
+  // to the last row (their sums are never used).
+  const T *wbase = W + (size_t)v0 * H;
+  int off[kRowsPerLoad];
+#pragma unroll
+  for (int t = 0; t < kRowsPerLoad; ++t) off[t] = (min(v0 + t + 8 * g, V - 1) - v0) * H;
+  const int off_end = (min(v0, V - 1) - v0) * H;    // the location read past the last chunk
+  const int nch = (H + CE - 1) / CE;
 
-  const int NG = (H + CW - 1) / CW;                 // chunks per row
-  const int nitems = (kRowsPerWave / 2) * NG;       // (row pair, chunk) items of this wave
-  const int ntiles = (nitems + kTile - 1) / kTile;
+  float acc[kRowsPerLoad][RT];
+#pragma unroll
+  for (int t = 0; t < kRowsPerLoad; ++t)
+#pragma unroll
+    for (int r = 0; r < RT; ++r) acc[t][r] = 0.f;
+  struct Chunk {
+    u32x4_t w[kRowsPerLoad];
+    u32x4_t x[RT];
+  };
+  auto fetch = [&](Chunk &ch, int c) __attribute__((always_inline)) {
+    const bool live = c < nch;   // uniform
+    const int col = min(c * CE + sl * EPL, H - EPL);
+#pragma unroll
+    for (int t = 0; t < kRowsPerLoad; ++t)
+      ch.w[t] = load_stream(wbase + (live ? off[t] + col : off_end));
+#pragma unroll
+    for (int r = 0; r < RT; ++r)
+      ch.x[r] = *reinterpret_cast<const u32x4_t *>(X + (live ? r * H + col : 0));
+  };
+  auto compute = [&](const Chunk &ch, int c) __attribute__((always_inline)) {
+    const bool in = c * CE + sl * EPL < H;           // false for every slot of a chunk past the end
+    uint4 xv[RT];
+#pragma unroll
+    for (int r = 0; r < RT; ++r) xv[r] = __builtin_bit_cast(uint4, mask16(ch.x[r], in));
+#pragma unroll
+    for (int t = 0; t < kRowsPerLoad; ++t) {
+      const uint4 wv = __builtin_bit_cast(uint4, mask16(ch.w[t], in));
+#pragma unroll
+      for (int r = 0; r < RT; ++r) acc[t][r] = Dt::run(wv, xv[r], acc[t][r]);
+    }
+  };
+  // The scheduling barriers keep each phase where it is written, so the wait before a compute
+  // is for that chunk only and the other chunk's loads stay in flight.
+  Chunk ca, cb;
+  fetch(ca, 0);
+  fetch(cb, 1);
+  for (int c = 0; c < nch; c += 2) {
+    __builtin_amdgcn_sched_barrier(0);
+    compute(ca, c);
+    __builtin_amdgcn_sched_barrier(0);
+    fetch(ca, c + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(cb, c + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    fetch(cb, c + 3);
+  }
   float keep[RT];
 #pragma unroll
-  for (int r = 0; r < RT; ++r) keep[r] = -INFINITY;
-  float acc[2][RT];
+  for (int r = 0; r < RT; ++r) keep[r] = 0.f;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int t = 0; t < kRowsPerLoad; ++t)
 #pragma unroll
-    for (int r = 0; r < RT; ++r) acc[i][r] = 0.f;
-
-  // (row pair, chunk) position of the next item to load and of the next item to consume,
-  // advanced incrementally (items are visited in order; no division in the loop).
-  int lpr = 0, lj = 0, litem = 0, cpr = 0, cj = 0;
-  auto compute = [&](const u32x4_t(&w)[kTile][2], int tile) __attribute__((always_inline)) {
-#pragma unroll
-    for (int u = 0; u < kTile; ++u) {
-      const int item = tile * kTile + u;
-      if (item >= nitems) break;                    // uniform
-      const int pr = cpr, j = cj;
-      if (++cj == NG) { cj = 0; ++cpr; }
-      const int col = j * CW + lane * EPL;
-      if (col < H) {
-        const uint4 w0 = __builtin_bit_cast(uint4, w[u][0]), w1 = __builtin_bit_cast(uint4, w[u][1]);
-#pragma unroll
-        for (int r = 0; r < RT; ++r) {
-          const uint4 xv = *reinterpret_cast<const uint4 *>(xs + r * H + col);
-          acc[0][r] = Dt::run(w0, xv, acc[0][r]);
-          acc[1][r] = Dt::run(w1, xv, acc[1][r]);
-        }
-      }
-      if (j == NG - 1) {                            // row pair complete (uniform)
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-          for (int r = 0; r < RT; ++r) {
-            const float t = wave_sum(acc[i][r]);
-            if (lane == 2 * pr + i) keep[r] = t;
-            acc[i][r] = 0.f;
-          }
-      }
+    for (int r = 0; r < RT; ++r) {
+      float v = acc[t][r];
+      v += spec::dpp_move<0xb1>(v);    // quad_perm [1, 0, 3, 2]
+      v += spec::dpp_move<0x4e>(v);    // quad_perm [2, 3, 0, 1]
+      v += spec::dpp_move<0x141>(v);   // row_half_mirror: the other quad of the 8 lanes
+      if (sl == t) keep[r] = v;        // lane 8 g + t: row t + 8 g = v0 + lane
     }
-  };
-  u32x4_t wa[kTile][2], wb[kTile][2];
-  if constexpr (Deep) {
-    // Few waves per SIMD (the hidden rows fill LDS): each wave keeps the next tile in flight
-    // while it computes.  Loads are unconditional so the compiler's wait before each compute
-    // leaves that tile outstanding: rows past V and tail-chunk lanes past H read a clamped
-    // valid address (their sums are never used), items past the wave's last read the table's
-    // first 16 bytes in every lane.
-    auto load = [&](u32x4_t(&w)[kTile][2]) __attribute__((always_inline)) {
-#pragma unroll
-      for (int u = 0; u < kTile; ++u) {
-        const bool real = litem < nitems;
-        const int col = min(lj * CW + lane * EPL, H - EPL);
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          const int v = min(v0 + 2 * lpr + i, V - 1);
-          w[u][i] = load_stream(real ? W + (size_t)v * H + col : W);
-        }
-        ++litem;
-        if (++lj == NG) { lj = 0; ++lpr; }
-      }
-    };
-    load(wa);
-    load(wb);
-    for (int t = 0; t < ntiles; t += 2) {
-      compute(wa, t);
-      load(wa);
-      compute(wb, t + 1);
-      load(wb);
-    }
-  } else {
-    // Many waves per SIMD: each wave loads the next tile and then computes the current one;
-    // the loads past the ends are skipped (the waits then drain each tile, and the
-    // parallelism comes from the other waves, which measured faster at this occupancy).
-    auto load = [&](u32x4_t(&w)[kTile][2]) __attribute__((always_inline)) {
-#pragma unroll
-      for (int u = 0; u < kTile; ++u) {
-        const int col = lj * CW + lane * EPL;
-        const int v = v0 + 2 * lpr;
-        const bool ok = litem < nitems && col < H;
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-          w[u][i] = (ok && v + i < V) ? load_stream(W + (size_t)(v + i) * H + col) : u32x4_t{0u, 0u, 0u, 0u};
-        ++litem;
-        if (++lj == NG) { lj = 0; ++lpr; }
-      }
-    };
-    load(wa);
-    for (int t = 0; t < ntiles; t += 2) {
-      if (t + 1 < ntiles) load(wb);
-      compute(wa, t);
-      if (t + 1 < ntiles) {
-        if (t + 2 < ntiles) load(wa);
-        compute(wb, t + 1);
-      }
-    }
-  }
-
   gemv_epilogue<RT>(keep, v0, lane, wave, blk, temp, logits, probs, stats, amax, V);
-}
-
-// Grid: ceil(V / 256).  Small R * H: the hidden rows live in registers (lane l holds columns
-// j * 512 + 8 l, j < NG, of every row; 1 KB of a table row per wave load), so the inner loop
-// is table loads and dot products only.  Each wave streams its 64 table rows kXrRows at a
-// time: all NG chunks of those rows are issued together and consumed in order.  The first
-// rows' loads are issued before the hidden rows are read, so every wave's start overlaps the
-// hidden-row reads (the same R x H elements for every wave, served from cache) with HBM
-// latency.  A tail chunk past H is masked to zero on both operands.
-constexpr int kXrRows = 2;
-
-template <typename T, int RT, int NG>
-__global__ __launch_bounds__(kThreads) void lm_head_gemv_xr(
-    const T *__restrict__ X, const T *__restrict__ W, const float *__restrict__ temp,
-    float *__restrict__ logits, float *__restrict__ probs, float2 *__restrict__ stats,
-    int *__restrict__ amax, int H, int V) {
-  using Dt = Dot<T>;
-  constexpr int EPL = Dt::kEPL;
-  constexpr int CW = kWave * EPL;                   // elements per 1 KB chunk
-  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-  const int blk = blockIdx.x;
-  const int v0 = blk * kBlockRows + wave * kRowsPerWave;
-  const bool tail_ok = (NG - 1) * CW + lane * EPL < H;   // this lane's part of the last chunk
-
-  uint4 xr[RT][NG];
-  float keep[RT];
-#pragma unroll
-  for (int r = 0; r < RT; ++r) keep[r] = -INFINITY;
-
-  auto load = [&](u32x4_t(&w)[kXrRows][NG], int rb) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < kXrRows; ++i) {
-      const T *row = W + (size_t)min(v0 + rb + i, V - 1) * H;
-#pragma unroll
-      for (int j = 0; j < NG; ++j)
-        w[i][j] = load_stream(row + min(j * CW + lane * EPL, H - EPL));
-    }
-  };
-  auto consume = [&](const u32x4_t(&w)[kXrRows][NG], int rb) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < kXrRows; ++i) {
-      float sdot[RT];
-#pragma unroll
-      for (int r = 0; r < RT; ++r) sdot[r] = 0.f;
-#pragma unroll
-      for (int j = 0; j < NG; ++j) {
-        uint4 wv = __builtin_bit_cast(uint4, w[i][j]);
-        if (j == NG - 1 && !tail_ok) wv = uint4{0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int r = 0; r < RT; ++r) sdot[r] = Dt::run(wv, xr[r][j], sdot[r]);
-      }
-#pragma unroll
-      for (int r = 0; r < RT; ++r) {
-        const float t = wave_sum(sdot[r]);
-        if (lane == rb + i) keep[r] = t;
-      }
-    }
-  };
-  u32x4_t w[kXrRows][NG];
-  load(w, 0);
-  __builtin_amdgcn_sched_barrier(0);   // the first table loads stay ahead of the hidden rows
-#pragma unroll
-  for (int r = 0; r < RT; ++r)
-#pragma unroll
-    for (int j = 0; j < NG; ++j) {
-      const int col = j * CW + lane * EPL;
-      const uint4 xv = *reinterpret_cast<const uint4 *>(X + (size_t)r * H + min(col, H - EPL));
-      xr[r][j] = col < H ? xv : uint4{0u, 0u, 0u, 0u};
-    }
-  consume(w, 0);
-  for (int rb = kXrRows; rb < kRowsPerWave; rb += kXrRows) {
-    load(w, rb);
-    consume(w, rb);
-  }
-  gemv_epilogue<RT>(keep, v0, lane, wave, blk, temp, logits, probs, stats, amax, V);
-}
-
-template <typename T, int RT, int NG>
-int launch_gemv_xr(const void *X, const void *W, const float *temp, float *logits, float *probs,
-                   float2 *stats, int *amax, int H, int V, hipStream_t st) {
-  hipLaunchKernelGGL((lm_head_gemv_xr<T, RT, NG>), dim3(spec::ceil_div(V, kBlockRows)),
-                     dim3(kThreads), 0, st, static_cast<const T *>(X), static_cast<const T *>(W),
-                     temp, logits, probs, stats, amax, H, V);
-  return spec::launched("lm_head_gemv_xr");
-}
-
-// Register-resident hidden rows for R <= 3 and H within 5 chunks of 1 KB.
-constexpr int kXrMaxR = 3, kXrMaxChunks = 5;
-
-template <typename T>
-int launch_gemv_xr_r(int R, const void *X, const void *W, const float *temp, float *logits,
-                     float *probs, float2 *stats, int *amax, int H, int V, hipStream_t st) {
-  const int ng = spec::ceil_div(H, kWave * Dot<T>::kEPL);
-#define XR_CASE(RR, NN) \
-  if (R == RR && ng == NN) return launch_gemv_xr<T, RR, NN>(X, W, temp, logits, probs, stats, amax, H, V, st);
-#define XR_ROW(NN) XR_CASE(1, NN) XR_CASE(2, NN) XR_CASE(3, NN)
-  XR_ROW(1) XR_ROW(2) XR_ROW(3) XR_ROW(4) XR_ROW(5)
-#undef XR_ROW
-#undef XR_CASE
-  return spec::fail(SPEC_EHIP, "spec_lm_head: no register-resident GEMV for R=%d H=%d", R, H);
-}
-
-// Above this LDS footprint of the hidden rows fewer than 8 workgroups fit a CU, and each
-// wave then keeps a tile in flight (Deep).
-constexpr size_t kDeepLds = 20 * 1024;
-
-template <typename T, int RT, bool Deep>
-int launch_gemv_p(const void *X, const void *W, const float *temp, float *logits, float *probs,
-                  float2 *stats, int *amax, int H, int V, size_t lds, hipStream_t st) {
-  static bool attr_set = false;
-  if (!attr_set && lds > 64 * 1024) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void *>(&lm_head_gemv<T, RT, Deep>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
-      return spec::fail(SPEC_EHIP, "spec_lm_head: cannot reserve %zu bytes of LDS", lds);
-    attr_set = true;
-  }
-  hipLaunchKernelGGL((lm_head_gemv<T, RT, Deep>), dim3(spec::ceil_div(V, kBlockRows)),
-                     dim3(kThreads), lds, st, static_cast<const T *>(X), static_cast<const T *>(W),
-                     temp, logits, probs, stats, amax, H, V);
-  return spec::launched("lm_head_gemv");
 }
 
 template <typename T, int RT>
 int launch_gemv(const void *X, const void *W, const float *temp, float *logits, float *probs,
                 float2 *stats, int *amax, int H, int V, hipStream_t st) {
-  const size_t lds = (size_t)RT * H * sizeof(T);
-  return lds > kDeepLds
-             ? launch_gemv_p<T, RT, true>(X, W, temp, logits, probs, stats, amax, H, V, lds, st)
-             : launch_gemv_p<T, RT, false>(X, W, temp, logits, probs, stats, amax, H, V, lds, st);
+  hipLaunchKernelGGL((lm_head_gemv<T, RT>), dim3(spec::ceil_div(V, kBlockRows)), dim3(kThreads),
+                     0, st, static_cast<const T *>(X), static_cast<const T *>(W), temp, logits,
+                     probs, stats, amax, H, V);
+  return spec::launched("lm_head_gemv");
 }
 
 template <typename T>
 int launch_gemv_r(int R, const void *X, const void *W, const float *temp, float *logits,
                   float *probs, float2 *stats, int *amax, int H, int V, hipStream_t st) {
-  return R == 1 ? launch_gemv<T, 1>(X, W, temp, logits, probs, stats, amax, H, V, st)
-                : launch_gemv<T, 2>(X, W, temp, logits, probs, stats, amax, H, V, st);
+  switch (R) {
+    case 1: return launch_gemv<T, 1>(X, W, temp, logits, probs, stats, amax, H, V, st);
+    case 2: return launch_gemv<T, 2>(X, W, temp, logits, probs, stats, amax, H, V, st);
+    default: return launch_gemv<T, 3>(X, W, temp, logits, probs, stats, amax, H, V, st);
+  }
 }
 
 // Merge the block statistics of row blockIdx.y and normalise its chunk of p in place.
@@ -828,15 +678,8 @@ int lm_head_contract(const void *hidden, const void *weight, const float *temper
   g_prof_start = g_prof_stop = nullptr;
   if (ev0 != nullptr && hipEventRecord(ev0, st) != hipSuccess)
     return spec::fail(SPEC_EHIP, "spec_lm_head: hipEventRecord(start) failed");
-  const size_t esz = dtype == SPEC_BF16 ? 2 : 4;
-  const bool gemv = R <= kGemvMaxR && (size_t)R * H * esz <= kGemvMaxLds;
-  const bool gemv_xr = R <= kXrMaxR && spec::ceil_div(H, kWave * (int)(16 / esz)) <= kXrMaxChunks;
   int rc;
-  if (gemv_xr)
-    rc = dtype == SPEC_BF16
-             ? launch_gemv_xr_r<uint16_t>(R, hidden, weight, temperature, logits, probs, stats, amax, H, V, st)
-             : launch_gemv_xr_r<float>(R, hidden, weight, temperature, logits, probs, stats, amax, H, V, st);
-  else if (gemv)
+  if (R <= kGemvMaxR)
     rc = dtype == SPEC_BF16
              ? launch_gemv_r<uint16_t>(R, hidden, weight, temperature, logits, probs, stats, amax, H, V, st)
              : launch_gemv_r<float>(R, hidden, weight, temperature, logits, probs, stats, amax, H, V, st);

@@ -74,7 +74,7 @@ def test_greedy_ties_take_first_index(R):
     assert pc[:, 7].tolist() == [1.0] * R and float(pc.sum()) == float(R)
 
 
-@pytest.mark.parametrize("R", [2, 3, 20])     # both GEMVs' epilogue and the MFMA path
+@pytest.mark.parametrize("R", [2, 3, 20])     # the GEMV (two and three rows) and the MFMA path
 @pytest.mark.parametrize("ties", [[45, 13, 2, 3, 130], [50, 33, 17], [1, 0], [255, 64, 128, 192],
                                   [63, 62, 61, 48, 47, 31, 16, 15]])
 def test_greedy_ties_within_a_wave(R, ties):
