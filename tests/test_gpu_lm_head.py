@@ -52,7 +52,9 @@ def test_tiny_fp32_workload():
                                           (96, 72, 1536, "f32"), (2, 2568, 3000, "bf16"),
                                           (2, 5376, 1500, "bf16"), (4, 2560, 2000, "bf16"),
                                           (1, 2560, 3001, "bf16"), (3, 2560, 4097, "bf16"),
-                                          (3, 5376, 2500, "bf16"), (1, 5376, 777, "bf16")])
+                                          (3, 5376, 2500, "bf16"), (1, 5376, 777, "bf16"),
+                                          (2, 8, 100, "bf16"), (3, 24, 65, "f32"),
+                                          (1, 8, 1, "bf16")])
 def test_ragged_shapes(R, H, V, dtype):
     torch.manual_seed(R * 7 + V)
     td = torch.float32 if dtype == "f32" else torch.bfloat16
