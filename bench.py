@@ -57,8 +57,8 @@ METRIC = "verified tokens/sec and verify-step HBM GB/s (% peak), batch 1, k=2, 8
 PROFILED_TRAFFIC = {
     "workload": DEFAULT_WORKLOAD,
     "source": "speculative_decoding_decode_amd/csrc/lm_head.hip",
-    "sha256": "b1fe29994735139cba90a8a05c8a3862cae4aead27ed2c3f574a01e7272087af",
-    "bytes_per_launch": 1348163083,
+    "sha256": "db7fbf8a4acf56e2529fb152b382c16421ab957b095f5183517b9c5e74b06933",
+    "bytes_per_launch": 1348161125,
 }
 
 

@@ -106,7 +106,7 @@ int spec_verify_attn(const void *q, const void *k_pool, const void *v_pool,
  *   logits       [R, V] fp32, or NULL when the raw logits are not wanted
  *   probs        [R, V] fp32  p, rows summing to 1
  *   H % 8 == 0 (16-byte rows for bf16); R <= 65535.  Accumulation is fp32 (dot products in
- *   the GEMVs that serve one to three rows, MFMA otherwise).
+ *   the GEMV that serves one to three rows, MFMA otherwise).
  * ---------------------------------------------------------------------------------------- */
 size_t spec_lm_head_workspace(int R, int H, int V);
 

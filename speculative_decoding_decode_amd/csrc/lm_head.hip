@@ -72,7 +72,7 @@ __device__ __forceinline__ bool better(float m, int a, float om, int oa) {
   return spec::first_max_better(m, a, om, oa);
 }
 
-// Contraction + per-block statistics for every R the GEMVs do not take.  512 threads, two
+// Contraction + per-block statistics for every R the GEMV does not take.  512 threads, two
 // waves per SIMD; a workgroup owns 512 vocab rows (two statistics blocks) and NH <= 6 tiles of
 // 16 hidden rows.
 // Grid: (ceil(V / 512), ceil(R / (16 NH))).  Wave w multiplies vocab rows 64 w + [0, 64) of the
