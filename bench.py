@@ -23,11 +23,17 @@ accept call with k = 0.  Both are prepared before timing.
 prints one JSON line with the step time per k, the tokens per step (from the per-position
 acceptance measured at KMAX), verified tokens/s per k, and the k the telemetry picks.
 
-Prints one JSON line: verified tokens/s (accepted drafts + the correction/bonus token per
-sequence per step), the step's HBM GB/s for the algorithmic bytes (KV read + lm-head table), a
-roofline object for the dominant kernel (the lm-head contraction, timed with HIP events the
-library records around it) and the fp64 oracle's CPU rate on a bounded sample of the same
-workload.
+Prints one JSON line:
+  value       verified tokens/s = B x E[n + 1] / measured step time, where E[n + 1] (accepted
+              drafts + the correction / bonus token) is the closed form of the timed steps'
+              input sets, 1 + sum_j prod_{i<=j} sum_v min(p_i, q_i); the count actually emitted
+              over the timed steps is reported beside it (value_sampled), since over a few
+              steps it carries the luck of the draws;
+  step_hbm_gbs  the step's algorithmic bytes (KV read + lm-head table) / step time;
+  roofline    the dominant kernel (the lm-head contraction), timed with HIP events the library
+              records right around it, in a separate pass of 100-500 steps after the timed one;
+  hbm_ceiling the rates of a plain device copy and sum on the same box;
+  cpu_baseline  the fp64 oracle on the host cores, on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -48,7 +54,7 @@ sys.path.insert(0, ROOT)
 DEFAULT_WORKLOAD = "b1_k2_sliding256_8k"
 MAX_SETS = 64
 SET_BUDGET_BYTES = 48 << 30   # KV-cache bytes allowed for all input sets together
-SAMPLE_EVERY = 16     # steps whose contraction kernel is bracketed by HIP events
+BRACKET_MIN, BRACKET_MAX = 100, 500   # steps of the pass that brackets the contraction kernel
 HBM_PEAK_GBS = 8000.0
 METRIC = "verified tokens/sec and verify-step HBM GB/s (% peak), batch 1, k=2, 8K ctx"
 # HBM bytes per launch of the contraction kernel from rocprofv3 FETCH_SIZE / WRITE_SIZE runs,
@@ -165,13 +171,30 @@ def prepare(w, device, torch, sv, gen, noise_sigma):
         # rows of this set (a diagnostic of the inputs, computed before timing)
         _, pt = sv.lm_head(x, W, temps)
         alpha = torch.minimum(pt.view(B, K1, -1)[:, :k], qd.view(B, k, -1)).sum(-1)
-        alphas.append(alpha.mean(0))
+        alphas.append(alpha)                                 # [B, k]
         sets.append(dict(q=qs, x=x, qd=qd.view(B, k, -1),
                          table=tables[s * B:(s + 1) * B], ctx=ctx_dev[s * B:(s + 1) * B]))
     torch.cuda.synchronize(device)
-    alpha_pos = torch.stack(alphas).mean(0).cpu().tolist() if k else []
+    alpha = (torch.stack(alphas).double().cpu().numpy() if k
+             else np.zeros((nsets, B, 0)))                   # [sets, B, k]
+    alpha_pos = alpha.mean(axis=(0, 1)).tolist() if k else []
     return dict(pools=pools, W=W, temps=temps, sets=sets, P=P, ctx=ctx1, nsets=nsets,
-                max_pages=table_all.shape[1], alpha_pos=alpha_pos)
+                max_pages=table_all.shape[1], alpha_pos=alpha_pos,
+                expected_tokens=expected_tokens(alpha))
+
+
+def expected_tokens(alpha):
+    """Expected emitted tokens per sequence and input set, E[n + 1] = 1 + sum_j prod_{i<=j} a_i
+    with a_i = sum_v min(p_i, q_i) the closed-form acceptance at draft position i (the rows of
+    one input set do not depend on the drafted prefix, so the positions are independent).
+    alpha [sets, B, k] -> [sets, B]."""
+    sets, B, k = alpha.shape
+    out = np.ones((sets, B))
+    run = np.ones((sets, B))
+    for i in range(k):
+        run = run * alpha[:, :, i]
+        out += run
+    return out
 
 
 def cpu_baseline(w, gen, seconds_target=12.0, max_steps=400):
@@ -179,11 +202,16 @@ def cpu_baseline(w, gen, seconds_target=12.0, max_steps=400):
     import oracle
     from oracle.step import verify_step
     from workloads import noise_sigma
-    try:
-        from threadpoolctl import threadpool_info
-        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        blas_threads = 1
+    from threadpoolctl import threadpool_info, threadpool_limits
+    cores = len(os.sched_getaffinity(0))
+    limiter = threadpool_limits(limits=cores)       # BLAS threads = the cores this process has
+    blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    cpu_model = "unknown"
+    with open("/proc/cpuinfo") as f:
+        for line in f:
+            if line.startswith("model name"):
+                cpu_model = line.split(":", 1)[1].strip()
+                break
     ctx = gen.context_lengths(w)
     table, P = gen.page_tables(w, ctx)
     pools = [gen.kv_pools(w, li, P, "cpu") for li in range(len(w.layers))]
@@ -209,8 +237,9 @@ def cpu_baseline(w, gen, seconds_target=12.0, max_steps=400):
         t_total += time.perf_counter() - t0
         tokens_out += int(np.sum(n + 1))
         steps += 1
-    return {"value": tokens_out / t_total, "unit": "verified tokens/s", "cores": int(blas_threads),
-            "kind": "oracle",
+    limiter.restore_original_limits()
+    return {"value": tokens_out / t_total, "unit": "verified tokens/s", "cores": int(cores),
+            "blas_threads": int(blas_threads), "cpu_model": cpu_model, "kind": "oracle",
             "sample": f"{steps} verify steps of the same workload (fp64 numpy oracle: attention, "
                       f"lm-head, softmax, accept; table converted to fp64 once, untimed), "
                       f"{t_total:.1f} s"}
@@ -309,6 +338,35 @@ def adjacent_calls(w, inp, lib, sv, gen, torch, device, sptr, dt, ws_attn, n_out
             "iterations": iters}
 
 
+def hbm_ceiling(torch, device, nbytes=1 << 30, reps=10):
+    """HBM rates of plain library kernels on this machine: a device-to-device copy (read + write
+    bytes counted) and a sum reduction (read) over 1 GiB, timed with HIP events on the current
+    stream (the verify step's)."""
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device=device)
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+        src.sum()
+    sptr = torch.cuda.current_stream(device).cuda_stream
+    sptr = ctypes.c_void_p(sptr) if sptr else None
+    ev = HipEvents(3)
+    ev.record(0, sptr)
+    for _ in range(reps):
+        dst.copy_(src)
+    ev.record(1, sptr)
+    acc = torch.zeros((), dtype=torch.float32, device=device)
+    for _ in range(reps):
+        acc += src.sum()
+    ev.record(2, sptr)
+    torch.cuda.synchronize(device)
+    copy_gbs = 2 * nbytes * reps / (ev.ms(0, 1) * 1e-3) / 1e9
+    read_gbs = nbytes * reps / (ev.ms(1, 2) * 1e-3) / 1e9
+    ev.close()
+    del src, dst
+    return {"copy_gbs": round(copy_gbs, 1), "sum_read_gbs": round(read_gbs, 1),
+            "how": "torch copy_ and sum over 1 GiB fp32, 10 launches each, HIP events"}
+
+
 def measure(w, steps, warmup, device):
     """Prepare w's input sets and time `steps` verify steps after `warmup` untimed ones."""
     import torch
@@ -326,7 +384,7 @@ def measure(w, steps, warmup, device):
     lib = _lib.load()
     stream = torch.cuda.current_stream(device)
     sptr = ctypes.c_void_p(stream.cuda_stream) if stream.cuda_stream else None
-    nsteps = warmup + steps
+    nsteps = warmup + max(steps, BRACKET_MAX, 200)   # the timed steps and the passes after them
     U = torch.from_numpy(np.stack([gen.uniforms(w, step=1000 + s) for s in range(nsteps)])).to(device)
     # the drafter samples its drafts anew every step: d ~ q of that step's input set, drawn by
     # the accept call with k = 0 (plain sampling) before timing
@@ -387,32 +445,37 @@ def measure(w, steps, warmup, device):
         step(i)
     torch.cuda.synchronize(device)
 
+    # (1) the timed region: K steps, nothing else on the stream
     K = steps
-    nsamp = (K + SAMPLE_EVERY - 1) // SAMPLE_EVERY
-    ev_lm = HipEvents(2 * nsamp)
     ev_tot = HipEvents(2)
-    log(f"[bench] timing {K} steps (contraction bracketed on every {SAMPLE_EVERY}th step)")
+    log(f"[bench] timing {K} steps")
     torch.cuda.synchronize(device)
     t0 = time.perf_counter()
     ev_tot.record(0, sptr)
     for j in range(K):
-        if j % SAMPLE_EVERY == 0:
-            step(warmup + j, ev_lm, 2 * (j // SAMPLE_EVERY))
-        else:
-            step(warmup + j)
+        step(warmup + j)
     ev_tot.record(1, sptr)
     torch.cuda.synchronize(device)
     t1 = time.perf_counter()
     wall = t1 - t0
-
-    lm_ms = np.array([ev_lm.ms(2 * i, 2 * i + 1) for i in range(nsamp)])
     gpu_total_ms = ev_tot.ms(0, 1)
-    ev_lm.close()
     ev_tot.close()
+    n_all = n_out[warmup:warmup + K].cpu().numpy()
+    tok_all = tok_out[warmup:warmup + K].cpu().numpy()
 
-    # distribution of single-step times: a separate pass with every step between two HIP
-    # events, less the median time of an empty event pair (the events' own cost)
-    P = min(200, steps)
+    # (2) the contraction kernel alone: a separate pass of the same steps with HIP events
+    # recorded by the library right before and after that kernel on every step
+    NB = max(BRACKET_MIN, min(K, BRACKET_MAX))
+    ev_lm = HipEvents(2 * NB)
+    for j in range(NB):
+        step(warmup + j, ev_lm, 2 * j)
+    torch.cuda.synchronize(device)
+    lm_ms = np.array([ev_lm.ms(2 * j, 2 * j + 1) for j in range(NB)])
+    ev_lm.close()
+
+    # (3) distribution of single-step times: every step between two HIP events, less the
+    # median time of an empty event pair (the events' own cost)
+    P = min(200, max(steps, 50))
     ev_d = HipEvents(2 * P + 2 * 32)
     for j in range(32):
         ev_d.record(2 * P + 2 * j, sptr)
@@ -429,12 +492,27 @@ def measure(w, steps, warmup, device):
            "p50": round(float(np.percentile(step_us, 50)), 2),
            "p90": round(float(np.percentile(step_us, 90)), 2),
            "steps": P, "event_pair_floor_us": round(floor_ms * 1e3, 2)}
-    n_all = n_out[warmup:].cpu().numpy()
-    tok_all = tok_out[warmup:].cpu().numpy()
+
+    # (4) warm run: the same input set on every step (its KV, queries and drafter rows stay in
+    # the caches; the table, far larger than the caches, still streams from HBM)
+    WM = max(50, min(K, 500))
+    mult = -(-nsteps // nsets)          # steps i < nsteps with i % nsets == 0: set 0's inputs
+    ev_w = HipEvents(2)
+    ev_w.record(0, sptr)
+    for j in range(WM):
+        step((j % mult) * nsets)
+    ev_w.record(1, sptr)
+    torch.cuda.synchronize(device)
+    warm_us = ev_w.ms(0, 1) * 1e3 / WM
+    ev_w.close()
+
     assert ((tok_all >= -1) & (tok_all < V)).all()
     emitted = int(np.sum(n_all + 1))
     stats = accept_stats(n_all, k)
-    value = emitted / wall
+    # expected tokens of exactly the timed steps' input sets (closed form of their rows)
+    exp_tok = float(sum(inp["expected_tokens"][(warmup + j) % nsets].sum() for j in range(K)))
+    value = exp_tok / wall
+    value_sampled = emitted / wall
     kv_bytes, table_bytes = algorithmic_bytes(w, inp["ctx"])
     step_bytes = kv_bytes + table_bytes
     ms_per_step = wall * 1e3 / K
@@ -445,13 +523,16 @@ def measure(w, steps, warmup, device):
     step_gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
     log(f"[bench] gpu {gpu_total_ms * 1e3 / K:.1f} us/step; lm-head contraction "
         f"{lm_avg_ms * 1e3:.1f} us = {achieved:.0f} GB/s; wall {ms_per_step * 1e3:.1f} us/step; "
-        f"acceptance pos {stats.per_position}")
+        f"warm {warm_us:.1f} us/step; expected tokens/step {exp_tok / K:.4f}, sampled "
+        f"{emitted / K:.4f}; acceptance pos {stats.per_position}")
 
     return dict(inp=inp, lib=lib, sptr=sptr, dt=dt, ws_attn=ws_attn, n_out=n_out, wall=wall,
-                value=value, ms_per_step=ms_per_step, lm_avg_ms=lm_avg_ms, achieved=achieved,
-                traffic=traffic, traffic_bytes=traffic_bytes, step_gbs=step_gbs,
-                step_bytes=step_bytes, table_bytes=table_bytes, gpu_total_ms=gpu_total_ms,
-                stats=stats, nsamp=nsamp, nsets=nsets, step_us_percentiles=pct)
+                value=value, value_sampled=value_sampled, ms_per_step=ms_per_step,
+                lm_avg_ms=lm_avg_ms, lm_launches=NB, achieved=achieved, traffic=traffic,
+                traffic_bytes=traffic_bytes, step_gbs=step_gbs, step_bytes=step_bytes,
+                table_bytes=table_bytes, gpu_total_ms=gpu_total_ms, stats=stats, nsets=nsets,
+                step_us_percentiles=pct, warm_us=warm_us, tokens_expected=exp_tok / K,
+                tokens_sampled=emitted / K)
 
 
 def sweep_k(w, kmax, steps, warmup, device):
@@ -534,8 +615,9 @@ def main():
     value, ms_per_step, lm_avg_ms, achieved = r["value"], r["ms_per_step"], r["lm_avg_ms"], r["achieved"]
     traffic, traffic_bytes, step_gbs = r["traffic"], r["traffic_bytes"], r["step_gbs"]
     step_bytes, table_bytes, gpu_total_ms, stats = r["step_bytes"], r["table_bytes"], r["gpu_total_ms"], r["stats"]
-    nsamp, nsets, pct = r["nsamp"], r["nsets"], r["step_us_percentiles"]
+    nsets, pct = r["nsets"], r["step_us_percentiles"]
     K = args.steps
+    ceiling = hbm_ceiling(torch, device)
 
     adjacent = adjacent_calls(w, inp, lib, sv, gen, torch, device, sptr, dt, ws_attn, n_out,
                               args.warmup)
@@ -572,7 +654,12 @@ def main():
         "step_algorithmic_bytes": step_bytes,
         "gpu_event_ms_per_step": round(gpu_total_ms / K, 5),
         "step_us_percentiles": pct,
-        "tokens_per_step": round(stats.mean_accepted_length, 4),
+        "tokens_per_step": round(r["tokens_expected"], 4),
+        "tokens_per_step_basis": "closed form E[n+1] = 1 + sum_j prod_{i<=j} sum_v min(p_i, q_i) "
+                                 "of each timed step's input set; value = B x that / wall time",
+        "value_sampled": round(r["value_sampled"], 2),
+        "tokens_per_step_sampled": round(r["tokens_sampled"], 4),
+        "warm_ms_per_step": round(r["warm_us"] * 1e-3, 5),
         "acceptance_per_position": [round(a, 4) for a in stats.per_position],
         "closed_form_acceptance_per_position": [round(a, 4) for a in inp["alpha_pos"]],
         "roofline": {"kernel": "lm-head vocab-table contraction", "bound": "hbm",
@@ -580,7 +667,9 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "traffic_bytes_per_launch": traffic_bytes,
                      "bytes_per_launch": table_bytes, "avg_launch_us": round(lm_avg_ms * 1e3, 2),
-                     "launches_timed": int(nsamp)},
+                     "launches_timed": int(r["lm_launches"]),
+                     "frac_of_measured_copy": round(achieved / ceiling["copy_gbs"], 4)},
+        "hbm_ceiling": ceiling,
         "adjacent": adjacent,
         "cpu_baseline": cpu,
     }

@@ -20,8 +20,11 @@
  *
  * Conventions for every call:
  *   - Pointers are device pointers owned by the caller (except where noted).  The library
- *     allocates nothing and keeps no handles; scratch memory is the caller's `workspace`,
- *     at least as large as the matching *_workspace() query says.
+ *     allocates nothing; scratch memory is the caller's `workspace`, at least as large as the
+ *     matching *_workspace() query says.  Its only state is per host thread: the message of
+ *     the last error (spec_last_error) and the one-shot profiling bracket armed by
+ *     spec_profile_lm_head; every call is otherwise independent of earlier calls and may be
+ *     made from any thread.
  *   - `stream` is a hipStream_t (NULL: the null stream).  Calls only enqueue work on it and
  *     return; results are valid once the stream has reached that point.
  *   - Return value: SPEC_OK (0) or a negative spec_status.  Host-checkable argument errors are
@@ -66,6 +69,12 @@ const char *spec_last_error(void);
  * (i) Verify attention: K1 = k + 1 causal queries per sequence over a paged KV cache, one
  *     layer per call, grouped-query heads.
  *
+ * Passages: the target scores all k drafts in one forward pass (llm-wiki "Gemma 4 MTP ...",
+ * section "투기적 디코딩(Speculative Decoding)의 기본 구조"; butteryoon guide, section 4
+ * "실행 흐름", parallel verification step); over the KV cache the drafter shares with it
+ * (same guide, section 1 table, KV-cache row); with local heads of dim 256 and global heads of
+ * dim 512 (same guide, section 7 settings table).
+ *
  * The K1 verified positions are the last K1 tokens of each sequence's cache (their K/V are
  * already written).  Query i of sequence b sits at position t = ctx_lens[b] - K1 + i and sees
  * the key positions s with lo <= s <= t, lo = 0 for a global layer (window == 0) and
@@ -83,8 +92,9 @@ const char *spec_last_error(void);
  *   B * K1 * Hq < 2^31 (SPEC_EUNSUPPORTED otherwise).
  *
  * Device-data preconditions: K1 <= ctx_lens[b] <= max_pages_per_seq * page_size.  ctx_lens
- * beyond that bound are clamped to it; a page id outside [0, num_pages) hides the keys on
- * that page; a query with no visible key gets a zero output row.
+ * beyond that bound are clamped to it (the verified positions then sit at the clamped length
+ * - K1 + i); a page id outside [0, num_pages) hides the keys on that page; a query with no
+ * visible key gets a zero output row.
  * ---------------------------------------------------------------------------------------- */
 size_t spec_verify_attn_workspace(int B, int K1, int Hq, int Hkv, int D, int page_size,
                                   int max_pages_per_seq, int window);
@@ -100,6 +110,11 @@ int spec_verify_attn(const void *q, const void *k_pool, const void *v_pool,
  *      distributions p = softmax(logits / T) (temperature per row; T <= 0 gives the one-hot
  *      vector at the first maximal logit, i.e. greedy).
  *
+ * Passages: every verified position is compared with the target's own distribution
+ * (butteryoon guide, section 4 "실행 흐름"); the projection onto the 256k vocabulary is a large
+ * part of the cost (same guide, section 1; damoang's text of the MTP announcement, section on
+ * the drafters' internals: the final logit computation is a major bottleneck).
+ *
  *   hidden       [R, H]  dtype  (rows b-major: row b*K1 + i is query position i of sequence b)
  *   weight       [V, H]  dtype  vocab x hidden table, row-major
  *   temperature  [R] fp32 (device)
@@ -114,15 +129,24 @@ int spec_lm_head(const void *hidden, const void *weight, const float *temperatur
                  float *logits, float *probs, int R, int H, int V, spec_dtype dtype,
                  void *workspace, size_t workspace_bytes, void *stream);
 
-/* Profiling aid for (ii): arms a one-shot bracket around the contraction kernel of the next
+/* Profiling aid for (ii), and the library's one piece of state besides the error message:
+ * arms a one-shot bracket, held per host thread, around the contraction kernel of the next
  * spec_lm_head call on this thread.  `start_event` / `stop_event` are hipEvent_t handles
  * created by the caller (either may be NULL); the call records them on its stream right
  * before and right after the contraction kernel (not around the softmax finalize), then
- * disarms.  Returns SPEC_OK. */
+ * disarms.  Returns SPEC_OK.  Not part of the verify step itself: a benchmark uses it to time
+ * the dominant kernel on the stream it runs on. */
 int spec_profile_lm_head(void *start_event, void *stop_event);
 
 /* ------------------------------------------------------------------------------------------
  * (iii) Accept / reject (Leviathan et al.), with the correction or bonus token.
+ *
+ * Passages: drafts are confirmed up to the first wrong one, where the target generates the
+ * token itself, leaving the output distribution unchanged (llm-wiki "Gemma 4 MTP ...",
+ * section "투기적 디코딩(Speculative Decoding)의 기본 구조"; butteryoon guide, section 4,
+ * accept/reject step); when the whole draft is accepted the same forward yields one extra
+ * token (news.hada.io 29214, section "MTP가 동작하는 방식"; damoang, section "추측적 해독은
+ * 어떻게 작동하는가", which cites Leviathan et al. for the rule).
  *
  * For each sequence b and i < k: draft i is accepted iff u[b][i] * q[b][i][d] < p[b][i][d]
  * with d = draft[b][i], evaluated exactly (fp64 product of fp32 values); acceptance stops at

@@ -638,13 +638,10 @@ int launch_partial(const void *q, const void *kp, const void *vp, const int32_t 
                    int max_pages, int window, float scale, const AttnPlan &pl, float2 *ml,
                    float *acc, hipStream_t st) {
   using S = AttnShape<D, T, RT>;
-  static bool attr_set = false;   // per instantiation; setting it twice is harmless
-  if (!attr_set) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void *>(&attn_partial<D, T, RT>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)S::kLds) != hipSuccess)
-      return spec::fail(SPEC_EHIP, "spec_verify_attn: cannot reserve %zu bytes of LDS", S::kLds);
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_set{0};   // per instantiation: one bit per device
+  const int rc = spec::ensure_dynamic_lds(reinterpret_cast<const void *>(&attn_partial<D, T, RT>),
+                                          S::kLds, lds_set, "spec_verify_attn");
+  if (rc != SPEC_OK) return rc;
   hipLaunchKernelGGL((attn_partial<D, T, RT>), dim3(pl.nwg), dim3(kThreads), S::kLds, st,
                      static_cast<const T *>(q), static_cast<const T *>(kp),
                      static_cast<const T *>(vp), table, ctx, ml, acc, B, K1, Hq, Hkv, num_pages,

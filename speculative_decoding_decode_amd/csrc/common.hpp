@@ -5,6 +5,8 @@
 #include <stdint.h>
 #include <stddef.h>
 
+#include <atomic>
+
 #include "spec_verify.h"
 
 namespace spec {
@@ -16,6 +18,12 @@ int fail(int code, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
 void clear_error();
 int launched(const char *what);  // SPEC_OK, or SPEC_EHIP with the runtime's message
 int device_cus();                // compute units of the current device (cached per device)
+// Raise `kernel`'s dynamic-LDS limit to `bytes` on the current device, once per device.
+// `done` holds one bit per device id (< 64; higher ids set the attribute on every call); the
+// bit is set with an atomic OR after the attribute call succeeds, so concurrent first calls
+// at worst both set it (the call is idempotent).
+int ensure_dynamic_lds(const void *kernel, size_t bytes, std::atomic<uint64_t> &done,
+                       const char *who);
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 inline int ceil_div(int a, int b) { return (a + b - 1) / b; }

@@ -589,13 +589,10 @@ template <typename T, int NH>
 int launch_nh(const void *X, const void *W, const float *temp, float *logits, float *probs,
               float2 *stats, int *amax, int R, int H, int V, hipStream_t st) {
   using S = MmaShape<NH>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void *>(&lm_head_mfma<T, NH>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)S::kLds) != hipSuccess)
-      return spec::fail(SPEC_EHIP, "spec_lm_head: cannot reserve %zu bytes of LDS", S::kLds);
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_set{0};   // per instantiation: one bit per device
+  const int rc = spec::ensure_dynamic_lds(reinterpret_cast<const void *>(&lm_head_mfma<T, NH>),
+                                          S::kLds, lds_set, "spec_lm_head");
+  if (rc != SPEC_OK) return rc;
   dim3 grid(spec::ceil_div(V, kMmaRows), spec::ceil_div(R, NH * 16));
   hipLaunchKernelGGL((lm_head_mfma<T, NH>), grid, dim3(kMmaThreads), S::kLds, st,
                      static_cast<const T *>(X), static_cast<const T *>(W), temp, logits, probs,

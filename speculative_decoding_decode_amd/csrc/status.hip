@@ -44,6 +44,19 @@ int device_cus() {
   return cached[dev];
 }
 
+int ensure_dynamic_lds(const void *kernel, size_t bytes, std::atomic<uint64_t> &done,
+                       const char *who) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(SPEC_EHIP, "%s: hipGetDevice failed", who);
+  const uint64_t bit = (dev >= 0 && dev < 64) ? (1ull << dev) : 0ull;
+  if (bit != 0 && (done.load(std::memory_order_acquire) & bit) != 0) return SPEC_OK;
+  if (hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes) !=
+      hipSuccess)
+    return fail(SPEC_EHIP, "%s: cannot reserve %zu bytes of LDS on device %d", who, bytes, dev);
+  done.fetch_or(bit, std::memory_order_release);
+  return SPEC_OK;
+}
+
 }  // namespace spec
 
 extern "C" int spec_version(void) { return (1 << 16) | 0; }

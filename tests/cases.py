@@ -16,6 +16,10 @@ from workloads import WORKLOADS, gen
 # moves p by at most p * e / T, and the fp32 exp/normalise adds a few ulp).
 TOL = {"bf16": 1e-2, "f32": 1e-5}
 P_TOL = 1e-5
+# Regression bound on top of TOL: errors measured on MI355X are ~1e-6 (attention) and ~6e-6
+# (logits) with bf16 inputs, and a one-key slip of the sliding window at the 8K batch-1 shape
+# moves attention outputs by ~7e-3, inside the 1e-2 bar; 1e-4 catches such indexing errors.
+REG_TOL = {"bf16": 1e-4, "f32": 1e-5}
 
 
 def say(msg: str) -> None:

@@ -10,7 +10,7 @@ import torch
 import speculative_decoding_decode_amd as sv
 from workloads import WORKLOADS, gen
 from workloads.configs import Layer, Workload
-from cases import TOL, attn_inputs, oracle_attn, say, dev
+from cases import TOL, REG_TOL, attn_inputs, oracle_attn, say, dev
 
 pytestmark = pytest.mark.gpu
 
@@ -30,6 +30,7 @@ def check(inp, dtype, label, rows=None):
     say(f"    max |err| = {err:.3e}")
     assert np.isfinite(got).all()
     assert err <= TOL[dtype]
+    assert err <= REG_TOL[dtype]
     return out
 
 
@@ -90,15 +91,20 @@ def test_maximum_k1(dtype, hq, hkv, d, window):
 
 
 def test_context_clamped_to_table():
+    # a context beyond the page table (max_pages * 16 = 64 tokens) is clamped to it, and the
+    # verified positions then sit at the clamped context - K1 + i: the result equals the
+    # oracle on the clamped context
     w = small_workload("bf16", 8, 2, 256, 0, 2, batch=2)
     ctx = np.array([64, 64], dtype=np.int32)
     table, P = gen.page_tables(w, ctx, max_pages=4)
     inp = attn_inputs(w, 0, dev(), ctx=ctx, table=table, num_pages=P)
-    ref_out = sv.verify_attn(**inp).clone()
+    ref = oracle_attn(inp)
     inp["ctx_lens"] = torch.tensor([64, 10_000], dtype=torch.int32, device=dev())
     out = sv.verify_attn(**inp)
     torch.cuda.synchronize()
-    assert torch.equal(out, ref_out)
+    err = np.abs(out.cpu().numpy().astype(np.float64) - ref).max()
+    say(f"[attn] clamped context: max |err| against the oracle at ctx 64 = {err:.3e}")
+    assert err <= REG_TOL["bf16"]
 
 
 def test_deterministic_repeat():

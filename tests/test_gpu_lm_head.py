@@ -8,7 +8,7 @@ import torch
 import oracle
 import speculative_decoding_decode_amd as sv
 from workloads import WORKLOADS, gen
-from cases import TOL, P_TOL, say, dev
+from cases import TOL, REG_TOL, P_TOL, say, dev
 
 pytestmark = pytest.mark.gpu
 
@@ -29,6 +29,7 @@ def run_and_compare(x, w, temps, dtype, rows=None, label=""):
     ez, ep = np.abs(z - z_ref).max(), np.abs(pg - p_ref).max()
     say(f"    max |logit err| = {ez:.3e}   max |p err| = {ep:.3e}")
     assert ez <= TOL[dtype]
+    assert ez <= REG_TOL[dtype]
     assert ep <= P_TOL
     np.testing.assert_allclose(pg.sum(axis=1), 1.0, atol=1e-5)
     for i, r in enumerate(rows):
