@@ -219,6 +219,20 @@ int spec_kv_append(const void *k_new, const void *v_new, void *k_pool, void *v_p
 
 int spec_kv_commit(int32_t *ctx_lens, const int32_t *n_accepted, int B, int K1, void *stream);
 
+/* ------------------------------------------------------------------------------------------
+ * Measurement aid, not part of the verify step: the HBM ceilings its streaming kernels are
+ * compared with on the same GPU (decoding is bound by streaming weights from memory,
+ * butteryoon guide, introduction).  Both probes use 16-byte nontemporal loads, 1 KB contiguous
+ * per wave instruction, a grid of spec_hbm_probe_grid() workgroups striding over the buffer.
+ *   mode 0  read `bytes` of src; dst receives 4 * spec_hbm_probe_grid() uint32 words whose
+ *           XOR equals the XOR of every 32-bit word of src (so no load is dead);
+ *   mode 1  copy `bytes` from src to dst (nontemporal stores); the buffers must not overlap.
+ * bytes a positive multiple of 16; src and dst 16-byte aligned.  Asynchronous on `stream`.
+ * ---------------------------------------------------------------------------------------- */
+int spec_hbm_probe_grid(void);
+
+int spec_hbm_probe(int mode, const void *src, void *dst, size_t bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

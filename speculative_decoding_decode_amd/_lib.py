@@ -29,6 +29,8 @@ SIGNATURES = {
                            + [c_int] * 3 + [c_void_p, c_size_t, c_void_p]),
     "spec_kv_append": (c_int, [c_void_p] * 6 + [c_int] * 7 + [c_int, c_void_p]),
     "spec_kv_commit": (c_int, [c_void_p, c_void_p, c_int, c_int, c_void_p]),
+    "spec_hbm_probe_grid": (c_int, []),
+    "spec_hbm_probe": (c_int, [c_int, c_void_p, c_void_p, c_size_t, c_void_p]),
 }
 
 _lib = None
