@@ -129,6 +129,22 @@ int spec_lm_head(const void *hidden, const void *weight, const float *temperatur
                  float *logits, float *probs, int R, int H, int V, spec_dtype dtype,
                  void *workspace, size_t workspace_bytes, void *stream);
 
+/* (ii) without a workspace, for callers that cannot allocate device memory (code under HIP
+ * graph capture, serving loops or harnesses that forbid hipMalloc).  Same arguments, results
+ * and errors as spec_lm_head, minus the workspace: the scratch it needs (the per-256-row
+ * vocabulary block softmax statistics) lives in a static device array of
+ * SPEC_LM_HEAD_STATIC_SCRATCH_BYTES that every GPU the library runs on holds until the process
+ * ends.  Usable whenever spec_lm_head_workspace(R, H, V) <= SPEC_LM_HEAD_STATIC_SCRATCH_BYTES
+ * (R * ceil(V / 256) * 12 bytes, rounded up: at V = 262144 up to 680 rows); larger problems
+ * return SPEC_EUNSUPPORTED before anything is enqueued.  Allocates nothing.  Every call on one
+ * GPU uses that GPU's one array: calls that overlap on a GPU (concurrent streams, threads)
+ * race and must be serialised by the caller. */
+#define SPEC_LM_HEAD_STATIC_SCRATCH_BYTES (8u << 20)
+
+int spec_lm_head_noalloc(const void *hidden, const void *weight, const float *temperature,
+                         float *logits, float *probs, int R, int H, int V, spec_dtype dtype,
+                         void *stream);
+
 /* Profiling aid for (ii), and the library's one piece of state besides the error message:
  * arms a one-shot bracket, held per host thread, around the contraction kernel of the next
  * spec_lm_head call on this thread.  `start_event` / `stop_event` are hipEvent_t handles

@@ -6,6 +6,7 @@ torch only provides device memory and the current stream:
 
     verify_attn(q, k_pool, v_pool, page_table, ctx_lens, window, ...)   -> out [B, K1, Hq, D]
     lm_head(hidden, weight, temperature, ...)                            -> (logits | None, p)
+    lm_head_noalloc(hidden, weight, temperature, ...)  (no workspace)    -> (logits | None, p)
     accept(draft, q, p, uniforms, ...)                                   -> (n_accepted, tokens)
     accept_philox(draft, q, p, seed, offset, ...)                        -> (n_accepted, tokens, u)
 
@@ -151,6 +152,34 @@ def lm_head(hidden, weight, temperature, probs=None, logits=None, want_logits: b
         logits.data_ptr() if logits is not None else None, probs.data_ptr(), R, H, V,
         _dtype_code(hidden), ws.data_ptr(), ws.numel(), _stream_ptr(dev, stream))
     _lib.check("spec_lm_head", rc)
+    return logits, probs
+
+
+def lm_head_noalloc(hidden, weight, temperature, probs=None, logits=None,
+                    want_logits: bool = False, stream=None):
+    """lm_head() through the entry point that allocates nothing: its scratch is the library's
+    static device array (spec_lm_head_noalloc).  Outputs are allocated here unless given."""
+    torch = _torch()
+    dev = hidden.device
+    _need(hidden, "hidden", device=dev)
+    _need(weight, "weight", hidden.dtype, dev)
+    _need(temperature, "temperature", torch.float32, dev)
+    R, H = hidden.shape
+    V, H2 = weight.shape
+    if H2 != H or temperature.shape != (R,):
+        raise ValueError("weight must be [V, H] and temperature [R]")
+    if probs is None:
+        probs = torch.empty((R, V), dtype=torch.float32, device=dev)
+    _need(probs, "probs", torch.float32, dev)
+    if logits is None and want_logits:
+        logits = torch.empty((R, V), dtype=torch.float32, device=dev)
+    if logits is not None:
+        _need(logits, "logits", torch.float32, dev)
+    rc = _lib.load().spec_lm_head_noalloc(
+        hidden.data_ptr(), weight.data_ptr(), temperature.data_ptr(),
+        logits.data_ptr() if logits is not None else None, probs.data_ptr(), R, H, V,
+        _dtype_code(hidden), _stream_ptr(dev, stream))
+    _lib.check("spec_lm_head_noalloc", rc)
     return logits, probs
 
 

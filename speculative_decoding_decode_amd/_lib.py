@@ -22,6 +22,7 @@ SIGNATURES = {
                                                                     c_size_t, c_void_p]),
     "spec_lm_head_workspace": (c_size_t, [c_int] * 3),
     "spec_lm_head": (c_int, [c_void_p] * 5 + [c_int] * 4 + [c_void_p, c_size_t, c_void_p]),
+    "spec_lm_head_noalloc": (c_int, [c_void_p] * 5 + [c_int] * 4 + [c_void_p]),
     "spec_profile_lm_head": (c_int, [c_void_p, c_void_p]),
     "spec_accept_workspace": (c_size_t, [c_int] * 3),
     "spec_accept": (c_int, [c_void_p] * 6 + [c_int] * 3 + [c_void_p, c_size_t, c_void_p]),

@@ -23,6 +23,8 @@
 //    statistics of all blocks and rescales p in place (or writes the greedy one-hot rows).
 #include <math.h>
 
+#include <mutex>
+
 #include "common.hpp"
 #include "softmax_stats.hpp"
 
@@ -713,21 +715,93 @@ extern "C" size_t spec_lm_head_workspace(int R, int H, int V) {
   return lm_stats_layout(R, V).bytes;
 }
 
+namespace {
+
+// Shared by spec_lm_head and spec_lm_head_noalloc: contraction + finalize into `workspace`
+// (at least lm_stats_layout(R, V).bytes).
+int lm_head_run(const void *hidden, const void *weight, const float *temperature, float *logits,
+                float *probs, int R, int H, int V, spec_dtype dtype, void *workspace,
+                hipStream_t st) {
+  const LmStats ls = lm_stats_layout(R, V);
+  float2 *stats = static_cast<float2 *>(workspace);
+  int *amax = reinterpret_cast<int *>(static_cast<char *>(workspace) + ls.amax_offset);
+  const int rc = lm_head_contract(hidden, weight, temperature, logits, probs, stats, amax, R, H,
+                                  V, dtype, st);
+  if (rc != SPEC_OK) return rc;
+  return lm_head_finalize_launch(probs, stats, amax, temperature, R, V, st);
+}
+
+}  // namespace
+
 extern "C" int spec_lm_head(const void *hidden, const void *weight, const float *temperature,
                             float *logits, float *probs, int R, int H, int V, spec_dtype dtype,
                             void *workspace, size_t workspace_bytes, void *stream) {
   spec::clear_error();
   int rc = lm_head_check(hidden, weight, temperature, probs, logits, R, H, V, dtype,
-                               "spec_lm_head");
+                         "spec_lm_head");
   if (rc != SPEC_OK) return rc;
   const LmStats ls = lm_stats_layout(R, V);
   SPEC_REQUIRE(workspace != nullptr && workspace_bytes >= ls.bytes, SPEC_EWORKSPACE,
                "spec_lm_head: workspace of %zu bytes needed, %zu given", ls.bytes, workspace_bytes);
-  float2 *stats = static_cast<float2 *>(workspace);
-  int *amax = reinterpret_cast<int *>(static_cast<char *>(workspace) + ls.amax_offset);
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  rc = lm_head_contract(hidden, weight, temperature, logits, probs, stats, amax, R, H, V,
-                              dtype, st);
+  return lm_head_run(hidden, weight, temperature, logits, probs, R, H, V, dtype, workspace,
+                     static_cast<hipStream_t>(stream));
+}
+
+// ------------------------------------------------------------------ allocation-free variant
+// For callers that cannot allocate (code under HIP graph capture, serving loops that forbid
+// allocation): the per-block statistics of spec_lm_head live in a file-scope device array
+// instead of a caller workspace.  Every GPU the library runs on holds its own copy of the
+// array, at its own address, until the process ends.  In host code the array's name is only a
+// stand-in for the symbol: its device address is looked up once per device with
+// hipGetSymbolAddress (with that device current) and only that address reaches a kernel.
+// The statistics are fully rewritten by every call before they are read, so nothing has to
+// be cleared between calls; calls that overlap on one GPU share the array and race.
+static __device__ __align__(256) unsigned char scratch[SPEC_LM_HEAD_STATIC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of this device's copy of `scratch`.
+int static_scratch(void **out, const char *who) {
+  int dev = 0;
+  const hipError_t ge = hipGetDevice(&dev);
+  if (ge != hipSuccess) return spec::fail(SPEC_EHIP, "%s: hipGetDevice: %s", who, hipGetErrorString(ge));
+  SPEC_REQUIRE(dev >= 0 && dev < kMaxDevices, SPEC_EUNSUPPORTED,
+               "%s: device id %d beyond the %d devices the static array is tracked for", who,
+               dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void *ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr)
+      return spec::fail(SPEC_EHIP, "%s: hipGetSymbolAddress(scratch) on device %d: %s", who,
+                        dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return SPEC_OK;
+}
+
+}  // namespace
+
+extern "C" int spec_lm_head_noalloc(const void *hidden, const void *weight,
+                                    const float *temperature, float *logits, float *probs, int R,
+                                    int H, int V, spec_dtype dtype, void *stream) {
+  spec::clear_error();
+  int rc = lm_head_check(hidden, weight, temperature, probs, logits, R, H, V, dtype,
+                         "spec_lm_head_noalloc");
   if (rc != SPEC_OK) return rc;
-  return lm_head_finalize_launch(probs, stats, amax, temperature, R, V, st);
+  const LmStats ls = lm_stats_layout(R, V);
+  SPEC_REQUIRE(ls.bytes <= (size_t)SPEC_LM_HEAD_STATIC_SCRATCH_BYTES, SPEC_EUNSUPPORTED,
+               "spec_lm_head_noalloc: R=%d rows over V=%d need %zu bytes of statistics, the "
+               "static array holds %zu (use spec_lm_head with a workspace)",
+               R, V, ls.bytes, (size_t)SPEC_LM_HEAD_STATIC_SCRATCH_BYTES);
+  void *ws = nullptr;
+  rc = static_scratch(&ws, "spec_lm_head_noalloc");
+  if (rc != SPEC_OK) return rc;
+  return lm_head_run(hidden, weight, temperature, logits, probs, R, H, V, dtype, ws,
+                     static_cast<hipStream_t>(stream));
 }

@@ -102,6 +102,25 @@ def test_lm_head_argument_errors(lib):
     assert b"65535" in lib.spec_last_error()
 
 
+def test_lm_head_noalloc_argument_errors(lib):
+    # every rejection happens on the host, before the static array's address is looked up
+    def call(**kw):
+        a = dict(x=FAKE, w=FAKE, t=FAKE, logits=None, p=FAKE, R=3, H=2560, V=262144, dtype=1)
+        a.update(kw)
+        return lib.spec_lm_head_noalloc(*a.values(), None)
+
+    assert call(p=None) == EINVAL
+    assert call(R=0) == EINVAL
+    assert call(H=2564) == EUNSUP
+    assert call(x=FAKE + 8) == EINVAL
+    # R * ceil(V / 256) * 12 bytes beyond the static array: 700 rows at V = 262144
+    need = lib.spec_lm_head_workspace(700, 2560, 262144)
+    assert need > 8 << 20
+    assert call(R=700) == EUNSUP
+    assert b"static array" in lib.spec_last_error()
+    assert lib.spec_lm_head_workspace(680, 2560, 262144) <= 8 << 20
+
+
 def test_accept_argument_errors(lib):
     def call(**kw):
         a = dict(d=FAKE, q=FAKE, p=FAKE, u=FAKE, n=FAKE, tok=FAKE, B=1, k=2, V=100, ws=FAKE,
