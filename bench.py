@@ -9,8 +9,9 @@ sliding-window attention layer (8 query / 2 KV heads, head dim 256, window 1024)
 1; drafter / target noise tuned for about 47% acceptance per position.  `--workload` selects any
 other workload of workloads/configs.py (measured the same way; not the headline).
 
-One step = spec_verify_attn for every attention layer -> spec_lm_head -> spec_accept, on inputs
-resident in HBM.  Up to 64 input sets (queries, cache regions of one shared page pool, hidden
+One step = spec_verify_attn for every attention layer -> spec_lm_head_accept (the lm-head and
+the accept / reject in one call; `--two-calls`: spec_lm_head -> spec_accept, same results), on
+inputs resident in HBM.  Up to 64 input sets (queries, cache regions of one shared page pool, hidden
 states, drafter distributions) rotate over the steps, and every step has its own drafts and
 uniforms, so KV and drafter rows are not cache-resident from the previous step.
 
@@ -298,7 +299,7 @@ def adjacent_calls(w, inp, lib, sv, gen, torch, device, sptr, dt, ws_attn, n_out
     qd = s0["qd"] if k else None
     dr0 = torch.zeros((B, k), dtype=torch.int32, device=device)
     u0 = torch.from_numpy(gen.uniforms(w, step=0)).to(device)
-    ws_acc = torch.empty(sv.accept_workspace_bytes(B, k, w.vocab), dtype=torch.uint8, device=device)
+    ws_acc = torch.zeros(sv.accept_workspace_bytes(B, k, w.vocab), dtype=torch.uint8, device=device)
     n_acc = torch.empty((B,), dtype=torch.int32, device=device)
     tok = torch.empty((B, K1), dtype=torch.int32, device=device)
     torch.cuda.synchronize(device)
@@ -376,8 +377,11 @@ def hbm_ceiling(torch, device, nbytes=2 << 30, reps=10):
                    "(read + write bytes), 10 launches each, HIP events"}
 
 
-def measure(w, steps, warmup, device):
-    """Prepare w's input sets and time `steps` verify steps after `warmup` untimed ones."""
+def measure(w, steps, warmup, device, two_calls=False):
+    """Prepare w's input sets and time `steps` verify steps after `warmup` untimed ones.
+
+    One step = spec_verify_attn per layer, then spec_lm_head_accept (the lm-head and the accept
+    step in one call), or with `two_calls` spec_lm_head then spec_accept (the same results)."""
     import torch
     import speculative_decoding_decode_amd as sv
     from speculative_decoding_decode_amd import _lib
@@ -403,11 +407,15 @@ def measure(w, steps, warmup, device):
     attn_out = [torch.empty((B, K1, L.hq, L.head_dim), dtype=torch.float32, device=device)
                 for L in w.layers]
     probs = torch.empty((R, V), dtype=torch.float32, device=device)
-    ws_attn = torch.empty(max(sv.verify_attn_workspace_bytes(B, K1, L.hq, L.hkv, L.head_dim,
+    # workspaces zero-filled once (the library's completion counters start at zero and every
+    # call leaves them there)
+    ws_attn = torch.zeros(max(sv.verify_attn_workspace_bytes(B, K1, L.hq, L.hkv, L.head_dim,
                                                              inp["max_pages"], L.window)
                               for L in w.layers), dtype=torch.uint8, device=device)
-    ws_lm = torch.empty(sv.lm_head_workspace_bytes(R, H, V), dtype=torch.uint8, device=device)
-    ws_acc = torch.empty(sv.accept_workspace_bytes(B, k, V), dtype=torch.uint8, device=device)
+    ws_lm = torch.zeros(sv.lm_head_workspace_bytes(R, H, V), dtype=torch.uint8, device=device)
+    ws_acc = torch.zeros(sv.accept_workspace_bytes(B, k, V), dtype=torch.uint8, device=device)
+    ws_fu = torch.zeros(sv.lm_head_accept_workspace_bytes(B, k, H, V), dtype=torch.uint8,
+                        device=device)
     dt = sv.SPEC_BF16 if w.dtype == "bf16" else sv.SPEC_F32
 
     # argument tuples of the C calls for every input set (pointers only)
@@ -433,6 +441,14 @@ def measure(w, steps, warmup, device):
                 _lib.check("spec_verify_attn", rc)
         if ev is not None:
             lib.spec_profile_lm_head(ev.ev[evi], ev.ev[evi + 1])
+        if not two_calls:
+            rc = lib.spec_lm_head_accept(m[0], m[1], m[2], drafts[i].data_ptr() if k else None,
+                                         q_ptr, U[i].data_ptr(), 0, 0, None, n_out[i].data_ptr(),
+                                         tok_out[i].data_ptr(), B, k, H, V, dt, ws_fu.data_ptr(),
+                                         ws_fu.numel(), sptr)
+            if rc:
+                _lib.check("spec_lm_head_accept", rc)
+            return
         rc = lib.spec_lm_head(*m)
         if rc:
             _lib.check("spec_lm_head", rc)
@@ -581,6 +597,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--two-calls", action="store_true",
+                    help="run the lm-head and the accept step as spec_lm_head + spec_accept "
+                         "instead of spec_lm_head_accept (same results; for comparison)")
     ap.add_argument("--sweep-k", type=int, default=None, metavar="KMAX",
                     help="time the workload's verify step at k = 0..KMAX drafts and print the "
                          "tokens-per-step curve, throughput per k and the chosen k (one JSON line)")
@@ -619,7 +638,7 @@ def main():
     if args.sweep_k is not None:
         sweep_k(w, args.sweep_k, args.steps, args.warmup, device)
         return
-    r = measure(w, args.steps, args.warmup, device)
+    r = measure(w, args.steps, args.warmup, device, two_calls=args.two_calls)
     inp, lib, sptr, dt, ws_attn, n_out = r["inp"], r["lib"], r["sptr"], r["dt"], r["ws_attn"], r["n_out"]
     value, ms_per_step, lm_avg_ms, achieved = r["value"], r["ms_per_step"], r["lm_avg_ms"], r["achieved"]
     traffic, traffic_bytes, step_gbs = r["traffic"], r["traffic_bytes"], r["step_gbs"]
@@ -652,6 +671,8 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic",
         "config": {"workload": w.name, "batch": B, "k": k, "verified_positions": K1,
+                   "lm_head_accept": "spec_lm_head + spec_accept" if args.two_calls
+                   else "spec_lm_head_accept",
                    "ctx": [int(c) for c in inp["ctx"]] if B <= 8 else
                    {"min": int(inp["ctx"].min()), "max": int(inp["ctx"].max()),
                     "mean": float(inp["ctx"].mean())},

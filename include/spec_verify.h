@@ -21,7 +21,8 @@
  * Conventions for every call:
  *   - Pointers are device pointers owned by the caller (except where noted).  The library
  *     allocates nothing; scratch memory is the caller's `workspace`, at least as large as the
- *     matching *_workspace() query says.  Its only state is per host thread: the message of
+ *     matching *_workspace() query says, with no required contents (every call writes what it
+ *     reads).  Its only state is per host thread: the message of
  *     the last error (spec_last_error) and the one-shot profiling bracket armed by
  *     spec_profile_lm_head; every call is otherwise independent of earlier calls and may be
  *     made from any thread.
@@ -122,6 +123,7 @@ int spec_verify_attn(const void *q, const void *k_pool, const void *v_pool,
  *   probs        [R, V] fp32  p, rows summing to 1
  *   H % 8 == 0 (16-byte rows for bf16); R <= 65535.  Accumulation is fp32 (dot products in
  *   the GEMV that serves one to three rows, MFMA otherwise).
+ *   Workspace: per 256-row vocabulary block and row the softmax statistics.
  * ---------------------------------------------------------------------------------------- */
 size_t spec_lm_head_workspace(int R, int H, int V);
 
@@ -135,8 +137,8 @@ int spec_lm_head(const void *hidden, const void *weight, const float *temperatur
  * vocabulary block softmax statistics) lives in a static device array of
  * SPEC_LM_HEAD_STATIC_SCRATCH_BYTES that every GPU the library runs on holds until the process
  * ends.  Usable whenever spec_lm_head_workspace(R, H, V) <= SPEC_LM_HEAD_STATIC_SCRATCH_BYTES
- * (R * ceil(V / 256) * 12 bytes, rounded up: at V = 262144 up to 680 rows); larger problems
- * return SPEC_EUNSUPPORTED before anything is enqueued.  Allocates nothing.  Every call on one
+ * (about R * ceil(V / 256) * 12 bytes: at V = 262144 up to 681 rows); larger problems return
+ * SPEC_EUNSUPPORTED before anything is enqueued.  Allocates nothing.  Every call on one
  * GPU uses that GPU's one array: calls that overlap on a GPU (concurrent streams, threads)
  * race and must be serialised by the caller. */
 #define SPEC_LM_HEAD_STATIC_SCRATCH_BYTES (8u << 20)
@@ -184,6 +186,7 @@ int spec_profile_lm_head(void *start_event, void *stop_event);
  * Device-data preconditions: p and q rows are distributions (non-negative, summing to 1).  A
  * draft id outside [0, V) is rejected without being read.  A p row whose weights are all 0
  * draws index 0.
+ * Workspace: per sequence the weight sums of its vocabulary chunks and the count n.
  * ---------------------------------------------------------------------------------------- */
 size_t spec_accept_workspace(int B, int k, int V);
 
@@ -209,6 +212,41 @@ int spec_accept_philox(const int32_t *draft, const float *q, const float *p, uin
                        uint64_t offset, float *uniforms_out, int32_t *n_accepted,
                        int32_t *tokens, int B, int k, int V, void *workspace,
                        size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------------------------------
+ * (ii) + (iii) in one call: the lm-head contraction of the R = B * K1 verify rows, then the
+ * accept / reject and the correction or bonus draw, without the softmax finalize pass over p.
+ * The accept kernel forms the values of p it needs (at the drafts, and the chunks of row n it
+ * sums and draws from) from the contraction's per-block exp values and statistics, with the
+ * operations of spec_lm_head's finalize, so n_accepted and tokens equal those of spec_lm_head
+ * followed by spec_accept (or spec_accept_philox) on the same arguments, bit for bit.  Four
+ * launches (contraction, row statistics once per row, accept chunks, draw) and no pass over p:
+ * the softmax finalize that reads and rewrites all of p [R, V] (100 MB at 96 rows over a 256k
+ * vocabulary) is not run, and each row's statistics are reduced once instead of by every
+ * finalize workgroup of the row; p itself is not returned.
+ *
+ * Passages: the verify forward compares every drafted position with the target's own
+ * distribution and accepts or rejects in the same step (butteryoon guide, section 4 "실행
+ * 흐름"); the serving guide runs sampling on a dedicated GPU backend (section 7 settings
+ * table); the bonus token comes out of the same forward (news.hada.io 29214, section "MTP가
+ * 동작하는 방식").
+ *
+ *   hidden, weight, temperature   as spec_lm_head (R = B * (k + 1) rows, b-major)
+ *   draft, q                      as spec_accept
+ *   uniforms    [B, K1] fp32, or NULL: then u[b][i] is Philox4x32-10 at (seed, offset) as in
+ *               spec_accept_philox, and uniforms_out (if not NULL) receives the values used
+ *   n_accepted, tokens            as spec_accept
+ *   Limits of both calls apply (R <= 65535, k <= 63, H % 8 == 0).  Workspace: the
+ *   contraction's exp values [R, V] fp32, its block and row statistics, the accept step's
+ *   chunk sums.
+ * ---------------------------------------------------------------------------------------- */
+size_t spec_lm_head_accept_workspace(int B, int k, int H, int V);
+
+int spec_lm_head_accept(const void *hidden, const void *weight, const float *temperature,
+                        const int32_t *draft, const float *q, const float *uniforms,
+                        uint64_t seed, uint64_t offset, float *uniforms_out,
+                        int32_t *n_accepted, int32_t *tokens, int B, int k, int H, int V,
+                        spec_dtype dtype, void *workspace, size_t workspace_bytes, void *stream);
 
 /* ------------------------------------------------------------------------------------------
  * KV-cache bookkeeping around the verify step.  Drafts from the first rejected one on are

@@ -9,9 +9,11 @@ torch only provides device memory and the current stream:
     lm_head_noalloc(hidden, weight, temperature, ...)  (no workspace)    -> (logits | None, p)
     accept(draft, q, p, uniforms, ...)                                   -> (n_accepted, tokens)
     accept_philox(draft, q, p, seed, offset, ...)                        -> (n_accepted, tokens, u)
+    lm_head_accept(hidden, weight, temperature, draft, q, uniforms | seed/offset)
+                                                                          -> (n_accepted, tokens, u)
 
-Workspaces are allocated once per device and size class and reused (calls on one stream are
-ordered, so reuse is safe; concurrent streams should pass their own `workspace`).
+Workspaces are allocated once per device and kind and reused (calls on one stream are ordered,
+so reuse is safe; concurrent streams should pass their own `workspace`).
 """
 from __future__ import annotations
 
@@ -73,7 +75,7 @@ def _workspace(kind: str, device, nbytes: int, given=None):
     key = (kind, str(device))
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+        ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
         _workspaces[key] = ws
     return ws
 
@@ -250,6 +252,68 @@ def accept_philox(draft, q, p, seed: int, offset: int, return_uniforms: bool = F
         tokens.data_ptr(), B, k, V, ws.data_ptr(), ws.numel(), _stream_ptr(dev, stream))
     _lib.check("spec_accept_philox", rc)
     return n_accepted, tokens, u
+
+
+def lm_head_accept_workspace_bytes(B, k, H, V) -> int:
+    n = _lib.load().spec_lm_head_accept_workspace(B, k, H, V)
+    if n == 0:
+        raise SpecError("spec_lm_head_accept_workspace", -1, _lib.last_error())
+    return int(n)
+
+
+def lm_head_accept(hidden, weight, temperature, draft, q, uniforms=None, seed: int = 0,
+                   offset: int = 0, return_uniforms: bool = False, n_accepted=None, tokens=None,
+                   workspace=None, stream=None):
+    """lm-head of the B * (k + 1) verify rows and accept / reject in one call (no finalize pass
+    over p); n_accepted and tokens equal lm_head() then accept() bit for bit.  uniforms [B, k+1]
+    fp32, or None for Philox4x32-10 at (seed, offset).  Returns (n_accepted, tokens, u or None)."""
+    torch = _torch()
+    dev = hidden.device
+    _need(hidden, "hidden", device=dev)
+    _need(weight, "weight", hidden.dtype, dev)
+    _need(temperature, "temperature", torch.float32, dev)
+    R, H = hidden.shape
+    V, H2 = weight.shape
+    if k_of(draft) is None:
+        raise ValueError("draft must be [B, k] int32")
+    B, k = draft.shape
+    if H2 != H or R != B * (k + 1) or temperature.shape != (R,):
+        raise ValueError("hidden must be [B*(k+1), H], weight [V, H], temperature [B*(k+1)]")
+    if k > 0:
+        _need(draft, "draft", torch.int32, dev)
+        _need(q, "q", torch.float32, dev)
+        if tuple(q.shape) != (B, k, V):
+            raise ValueError("q must be [B, k, V]")
+    if uniforms is not None:
+        _need(uniforms, "uniforms", torch.float32, dev)
+        if tuple(uniforms.shape) != (B, k + 1):
+            raise ValueError("uniforms must be [B, k+1]")
+    if not (0 <= seed < 2 ** 64 and 0 <= offset < 2 ** 64):
+        raise ValueError("seed and offset are unsigned 64-bit integers")
+    if n_accepted is None:
+        n_accepted = torch.empty((B,), dtype=torch.int32, device=dev)
+    if tokens is None:
+        tokens = torch.empty((B, k + 1), dtype=torch.int32, device=dev)
+    _need(n_accepted, "n_accepted", torch.int32, dev)
+    _need(tokens, "tokens", torch.int32, dev)
+    u = torch.empty((B, k + 1), dtype=torch.float32, device=dev) if return_uniforms else None
+    ws = _workspace("lm_head_accept", dev, lm_head_accept_workspace_bytes(B, k, H, V), workspace)
+    rc = _lib.load().spec_lm_head_accept(
+        hidden.data_ptr(), weight.data_ptr(), temperature.data_ptr(),
+        draft.data_ptr() if k > 0 else None, q.data_ptr() if k > 0 else None,
+        uniforms.data_ptr() if uniforms is not None else None, int(seed), int(offset),
+        u.data_ptr() if u is not None else None, n_accepted.data_ptr(), tokens.data_ptr(),
+        B, k, H, V, _dtype_code(hidden), ws.data_ptr(), ws.numel(), _stream_ptr(dev, stream))
+    _lib.check("spec_lm_head_accept", rc)
+    return n_accepted, tokens, u
+
+
+def k_of(draft):
+    """k of a [B, k] draft tensor, or None if it is not one."""
+    torch = _torch()
+    if not isinstance(draft, torch.Tensor) or draft.dim() != 2:
+        return None
+    return int(draft.shape[1])
 
 
 def kv_append(k_new, v_new, k_pool, v_pool, page_table, ctx_lens, stream=None):

@@ -28,6 +28,9 @@ SIGNATURES = {
     "spec_accept": (c_int, [c_void_p] * 6 + [c_int] * 3 + [c_void_p, c_size_t, c_void_p]),
     "spec_accept_philox": (c_int, [c_void_p] * 3 + [c_uint64, c_uint64] + [c_void_p] * 3
                            + [c_int] * 3 + [c_void_p, c_size_t, c_void_p]),
+    "spec_lm_head_accept_workspace": (c_size_t, [c_int] * 4),
+    "spec_lm_head_accept": (c_int, [c_void_p] * 6 + [c_uint64, c_uint64] + [c_void_p] * 3
+                            + [c_int] * 5 + [c_void_p, c_size_t, c_void_p]),
     "spec_kv_append": (c_int, [c_void_p] * 6 + [c_int] * 7 + [c_int, c_void_p]),
     "spec_kv_commit": (c_int, [c_void_p, c_void_p, c_int, c_int, c_void_p]),
     "spec_hbm_probe_grid": (c_int, []),

@@ -22,7 +22,19 @@
 //                  weights of one vocabulary chunk of the row it will be drawn from;
 //  accept_draw     grid (B): one workgroup per sequence scans the chunk sums, finds the chunk
 //                  holding the threshold, scans inside it and writes n and the tokens.
+// (A single kernel whose last chunk workgroup per sequence draws, found with a completion
+// counter, measured slower on MI355X at batch 1: the counter's round trip and the device-scope
+// reads of the chunk sums cost more than the second launch.)
+//
+// spec_lm_head_accept runs the lm-head contraction and this kernel back to back, without the
+// softmax finalize pass over p: the accept kernel forms the p values it needs (at the drafts and
+// in its chunk of row n) from the contraction's exp values and statistics, with the operations
+// of the finalize (softmax_stats.hpp), so its results equal spec_lm_head + spec_accept bit for
+// bit.  This is the sampling pipeline run as part of the verify forward, the role the serving
+// guide gives its dedicated sampling backend (butteryoon "Gemma 4 MTP 서빙 가이드 해설",
+// section 7 settings table).
 #include "common.hpp"
+#include "softmax_stats.hpp"
 
 namespace {
 
@@ -38,7 +50,6 @@ __device__ __forceinline__ uint64_t fixed_weight(float x) {
   return s > 0.f ? static_cast<uint64_t>(s) : 0ull;   // truncation == floor for s >= 0
 }
 
-// Number of accepted drafts of sequence b.  Must be called by a whole wave (lanes 0..63).
 // Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As Easy as 1, 2, 3",
 // SC'11): ten rounds of two 32 x 32 -> 64-bit products with the published multipliers, the
 // new counter (hi(p2) ^ c1 ^ k0, lo(p2), hi(p0) ^ c3 ^ k1, lo(p0)), and the key bumped by the
@@ -72,24 +83,6 @@ struct UniformSource {
     return u != nullptr ? u[(size_t)b * K1 + i] : philox_uniform(seed, offset, b, i);
   }
 };
-
-// ul: this lane's uniform (lane i < k tests draft i).
-__device__ int accepted_count(const int32_t *__restrict__ draft, const float *__restrict__ q,
-                              const float *__restrict__ p, float ul, int b, int k, int V,
-                              int lane) {
-  bool ok = false;
-  if (lane < k) {
-    const int d = draft[(size_t)b * k + lane];
-    if (d >= 0 && d < V) {
-      const double qd = q[((size_t)b * k + lane) * V + d];
-      const double pd = p[((size_t)b * (k + 1) + lane) * V + d];
-      ok = (double)ul * qd < pd;
-    }
-  }
-  const uint64_t acc = __ballot(ok);
-  // lanes >= k never accept, so ~acc has a set bit at or below k
-  return min(k, __builtin_ctzll(~acc));
-}
 
 __device__ __forceinline__ uint64_t shfl_up_u64(uint64_t v, int d) {
   const uint32_t lo = __shfl_up((uint32_t)v, d), hi = __shfl_up((uint32_t)(v >> 32), d);
@@ -127,9 +120,7 @@ __device__ __forceinline__ uint64_t wg_inclusive_scan(uint64_t v, uint64_t *sh) 
   return v + base;
 }
 
-// Chunk c of a sequence's row: elements [c * chunk, (c + 1) * chunk), chunk = kThreads * E;
-// thread t owns the E contiguous elements starting at c * chunk + t * E (E is 4 for one
-// sequence over a 256k vocabulary, larger for big batches; a multiple of 4 is read as float4s).
+// E contiguous entries of a row starting at j0 (zero past V); a multiple of 4 is read as float4s.
 template <int E>
 __device__ __forceinline__ void load_run(const float *__restrict__ row, int j0, int V, float (&x)[E]) {
   if (E % 4 == 0 && j0 + E <= V && (V & 3) == 0) {
@@ -146,29 +137,100 @@ __device__ __forceinline__ void load_run(const float *__restrict__ row, int j0, 
 
 __device__ __forceinline__ uint64_t residual(uint64_t P, uint64_t Q) { return P > Q ? P - Q : 0ull; }
 
-// Grid: (nchunks, B).  Round trips: drafts, then p/q at the drafts (n), then the chunk of the
-// row the draw uses.  (Loading every row's chunk with the drafts, to pick row n from registers,
-// measured slower at batch 1: the extra bytes cost more than the round trip.)
-template <int E>
+// Where the target's p comes from.
+//  * normalised p [B * K1, V] (spec_accept): `stats` is null;
+//  * the lm-head contraction's output (spec_lm_head_accept): `p` holds e = 2^((z - block max) c)
+//    for the rows with T > 0, and p = e * 2^((block max - M) c) / L is formed here from the
+//    block maxima and the row statistics with the same operations as the lm-head's softmax
+//    finalize, so every p value equals the one spec_lm_head would have stored, bit for bit;
+//    greedy rows (T <= 0) are the one-hot vector at the row's first argmax.
+struct PSource {
+  const float *p;
+  const float2 *stats;           // [nblk][R] block (max, sum), or null
+  const spec::RowStat *rows;     // [R] row statistics (lm_row_stats), or null
+};
+
+// The E entries j0 .. j0 + E - 1 of p's row `row` (E divides 256, so they share one block).
+template <int E, bool FS>
+__device__ __forceinline__ void p_run(const PSource &ps, int row, int R, int j0, int V,
+                                      const spec::RowStat &rs, float (&x)[E]) {
+  if constexpr (FS) {
+    if (rs.c == 0.f) {                                   // greedy row: one-hot at A
+#pragma unroll
+      for (int e = 0; e < E; ++e) x[e] = (j0 + e == rs.a) ? 1.f : 0.f;
+      return;
+    }
+    const int blk = min(j0, V - 1) / spec::kStatBlock;
+    const float bm = ps.stats[(size_t)blk * R + row].x;
+    load_run<E>(ps.p + (size_t)row * V, j0, V, x);
+    const float f = spec::stat_factor(bm, rs);
+#pragma unroll
+    for (int e = 0; e < E; ++e) x[e] *= f;
+  } else {
+    load_run<E>(ps.p + (size_t)row * V, j0, V, x);
+  }
+}
+
+// Row statistics of the K1 rows of sequence b into LDS (spec_lm_head_accept): lanes of wave 0.
+// A barrier must follow before they are read.
+__device__ __forceinline__ void seq_row_stats(const PSource &ps, int b, int K1,
+                                              spec::RowStat *rs_sh) {
+  if (threadIdx.x < K1) rs_sh[threadIdx.x] = ps.rows[(size_t)b * K1 + threadIdx.x];
+}
+
+// Grid: (nchunks, B).  Every workgroup finds n for its sequence (wave 0: lane i tests draft i
+// exactly in fp64, a ballot gives the first rejection) and sums the integer weights of its
+// chunk of the row the draw uses.  Round trips: drafts (and, from statistics, the rows'
+// partials), then p and q at the drafts, then the chunk.
+template <int E, bool FS>
 __global__ __launch_bounds__(kThreads) void accept_chunks(
-    const int32_t *__restrict__ draft, const float *__restrict__ q, const float *__restrict__ p,
-    UniformSource us, uint64_t *__restrict__ wsum, uint64_t *__restrict__ psum,
-    int32_t *__restrict__ nbuf, int k, int V, int nchunks) {
-  __shared__ int n_sh;
+    const int32_t *__restrict__ draft, const float *__restrict__ q, PSource ps, UniformSource us,
+    uint64_t *__restrict__ wsum, uint64_t *__restrict__ psum, int32_t *__restrict__ nbuf, int k,
+    int V, int nchunks) {
   __shared__ uint64_t red[kThreads / spec::kWave];
+  __shared__ int n_sh;
+  __shared__ spec::RowStat rs_sh[FS ? kMaxK + 1 : 1];
   const int b = blockIdx.y, c = blockIdx.x, tid = threadIdx.x;
-  const int K1 = k + 1;
+  const int K1 = k + 1, R = (int)gridDim.y * K1;
+
+  // drafts and uniforms (wave 0), p (or e and its block max) and q at the drafts
+  int d = -1;
+  float ul = 0.f, pe = 0.f, bm = 0.f;
+  double qd = 0.0;
+  if (tid < k) {
+    d = draft[(size_t)b * k + tid];
+    ul = us(b, K1, tid);
+    if (d >= 0 && d < V) {
+      qd = q[((size_t)b * k + tid) * V + d];
+      pe = ps.p[((size_t)b * K1 + tid) * V + d];
+      if constexpr (FS) bm = ps.stats[(size_t)(d / spec::kStatBlock) * R + (size_t)b * K1 + tid].x;
+    }
+  }
+  if constexpr (FS) {
+    seq_row_stats(ps, b, K1, rs_sh);
+    __syncthreads();
+  }
   if (tid < spec::kWave) {
-    const float ul = tid < k ? us(b, K1, tid) : 0.f;
-    const int n = accepted_count(draft, q, p, ul, b, k, V, tid);
-    if (tid == 0) n_sh = n;
+    bool ok = false;
+    if (tid < k && d >= 0 && d < V) {
+      double pd = pe;
+      if constexpr (FS) {
+        const spec::RowStat rs = rs_sh[tid];
+        pd = rs.c == 0.f ? (d == rs.a ? 1.0 : 0.0) : (double)(pe * spec::stat_factor(bm, rs));
+      }
+      ok = (double)ul * qd < pd;
+    }
+    const uint64_t acc = __ballot(ok);
+    // lanes >= k never accept, so ~acc has a set bit at or below k
+    if (tid == 0) n_sh = min(k, __builtin_ctzll(~acc));
   }
   __syncthreads();
   const int n = n_sh;
+  const bool corr = n < k;
+  const spec::RowStat rsn = FS ? rs_sh[FS ? n : 0] : spec::RowStat{0.f, 0.f, 0.f, 0};
   const int j0 = c * kThreads * E + tid * E;
   float pv[E], qv[E];
-  load_run<E>(p + ((size_t)b * K1 + n) * V, j0, V, pv);
-  const bool corr = n < k;
+  p_run<E, FS>(ps, b * K1 + n, R, j0, V, rsn, pv);
   if (corr) load_run<E>(q + ((size_t)b * k + n) * V, j0, V, qv);
   uint64_t sp = 0, sw = 0;
 #pragma unroll
@@ -186,19 +248,22 @@ __global__ __launch_bounds__(kThreads) void accept_chunks(
   }
 }
 
-// Grid: (B).  Round trips: n, chunk sums, uniform and drafts together; then the chosen chunk.
-template <int E>
+// Grid: (B).  One workgroup per sequence scans the chunk sums, finds the chunk holding the
+// threshold, scans inside it, and writes n and the tokens.  Round trips: n, the chunk sums, the
+// uniform, the drafts (and, from statistics, the rows' partials) together; then the chosen
+// chunk.
+template <int E, bool FS>
 __global__ __launch_bounds__(kThreads) void accept_draw(
-    const int32_t *__restrict__ draft, const float *__restrict__ q, const float *__restrict__ p,
-    UniformSource us, const uint64_t *__restrict__ wsum,
-    const uint64_t *__restrict__ psum, const int32_t *__restrict__ nbuf,
-    int32_t *__restrict__ n_out, int32_t *__restrict__ tokens, float *__restrict__ u_out, int k,
-    int V, int nchunks) {
+    const int32_t *__restrict__ draft, const float *__restrict__ q, PSource ps, UniformSource us,
+    const uint64_t *__restrict__ wsum, const uint64_t *__restrict__ psum,
+    const int32_t *__restrict__ nbuf, int32_t *__restrict__ n_out, int32_t *__restrict__ tokens,
+    float *__restrict__ u_out, int k, int V, int nchunks) {
   __shared__ uint64_t red[kThreads / spec::kWave];
   __shared__ int found_sh;
   __shared__ uint64_t base_sh;
+  __shared__ spec::RowStat rs_sh[FS ? kMaxK + 1 : 1];
   const int b = blockIdx.x, tid = threadIdx.x;
-  const int K1 = k + 1;
+  const int K1 = k + 1, R = (int)gridDim.x * K1;
   if (tid == 0) found_sh = 0;   // ordered before the scans by the barriers inside wg_sum
   // everything independent of n at once (nchunks <= kThreads)
   const int n = nbuf[b];
@@ -207,9 +272,11 @@ __global__ __launch_bounds__(kThreads) void accept_draw(
   const float uk = us(b, K1, k);
   if (u_out != nullptr && tid < K1) u_out[(size_t)b * K1 + tid] = us(b, K1, tid);
   const int dtok = tid < k ? draft[(size_t)b * k + tid] : -1;
+  if constexpr (FS) seq_row_stats(ps, b, K1, rs_sh);   // the barriers of wg_sum follow
 
   const uint64_t wtot = wg_sum(cw, red);
-  const bool fallback = n < k && wtot == 0ull;   // every correction weight 0: draw from p
+  const bool corr = n < k;
+  const bool fallback = corr && wtot == 0ull;   // every correction weight 0: draw from p
   const uint64_t mine = fallback ? cp : cw;
   const uint64_t total = fallback ? wg_sum(cp, red) : wtot;
 
@@ -230,16 +297,17 @@ __global__ __launch_bounds__(kThreads) void accept_draw(
     const uint64_t t2 = t - base_sh;
 
     // 2) inside the chunk: running weights in index order, E contiguous elements per thread
-    const bool corr = n < k && !fallback;
+    const bool wcorr = corr && !fallback;
     const int j0 = cstar * kThreads * E + tid * E;
+    const spec::RowStat rsn = FS ? rs_sh[FS ? n : 0] : spec::RowStat{0.f, 0.f, 0.f, 0};
     float pv[E], qv[E];
-    load_run<E>(p + ((size_t)b * K1 + n) * V, j0, V, pv);
-    if (corr) load_run<E>(q + ((size_t)b * k + n) * V, j0, V, qv);
+    p_run<E, FS>(ps, b * K1 + n, R, j0, V, rsn, pv);
+    if (wcorr) load_run<E>(q + ((size_t)b * k + n) * V, j0, V, qv);
     uint64_t w[E], wsum_t = 0;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       const uint64_t P = fixed_weight(pv[e]);
-      w[e] = corr ? residual(P, fixed_weight(qv[e])) : P;
+      w[e] = wcorr ? residual(P, fixed_weight(qv[e])) : P;
       wsum_t += w[e];
     }
     {
@@ -286,50 +354,85 @@ AcceptPlan plan(int B, int V) {
   return pl;
 }
 
-template <int E>
-int launch(const AcceptPlan &pl, const int32_t *draft, const float *q, const float *p,
+template <int E, bool FS>
+int launch(const AcceptPlan &pl, const int32_t *draft, const float *q, const PSource &ps,
            UniformSource us, float *u_out, int32_t *n_accepted, int32_t *tokens, int B, int k,
-           int V, uint64_t *wsum, uint64_t *psum, int32_t *nbuf, hipStream_t st) {
-  hipLaunchKernelGGL((accept_chunks<E>), dim3(pl.nchunks, B), dim3(kThreads), 0, st, draft, q,
-                     p, us, wsum, psum, nbuf, k, V, pl.nchunks);
+           int V, char *ws, hipStream_t st) {
+  uint64_t *wsum = reinterpret_cast<uint64_t *>(ws + pl.off_w);
+  uint64_t *psum = reinterpret_cast<uint64_t *>(ws + pl.off_p);
+  int32_t *nbuf = reinterpret_cast<int32_t *>(ws + pl.off_n);
+  hipLaunchKernelGGL((accept_chunks<E, FS>), dim3(pl.nchunks, B), dim3(kThreads), 0, st, draft,
+                     q, ps, us, wsum, psum, nbuf, k, V, pl.nchunks);
   int rc = spec::launched("accept_chunks");
   if (rc != SPEC_OK) return rc;
-  hipLaunchKernelGGL((accept_draw<E>), dim3(B), dim3(kThreads), 0, st, draft, q, p, us,
+  hipLaunchKernelGGL((accept_draw<E, FS>), dim3(B), dim3(kThreads), 0, st, draft, q, ps, us,
                      wsum, psum, nbuf, n_accepted, tokens, u_out, k, V, pl.nchunks);
   return spec::launched("accept_draw");
+}
+
+template <bool FS>
+int launch_e(const AcceptPlan &pl, const int32_t *draft, const float *q, const PSource &ps,
+             UniformSource us, float *u_out, int32_t *n_accepted, int32_t *tokens, int B, int k,
+             int V, char *ws, hipStream_t st) {
+  switch (pl.E) {
+    case 1: return launch<1, FS>(pl, draft, q, ps, us, u_out, n_accepted, tokens, B, k, V, ws, st);
+    case 2: return launch<2, FS>(pl, draft, q, ps, us, u_out, n_accepted, tokens, B, k, V, ws, st);
+    case 4: return launch<4, FS>(pl, draft, q, ps, us, u_out, n_accepted, tokens, B, k, V, ws, st);
+    case 8: return launch<8, FS>(pl, draft, q, ps, us, u_out, n_accepted, tokens, B, k, V, ws, st);
+    case 16: return launch<16, FS>(pl, draft, q, ps, us, u_out, n_accepted, tokens, B, k, V, ws, st);
+    case 32: return launch<32, FS>(pl, draft, q, ps, us, u_out, n_accepted, tokens, B, k, V, ws, st);
+    default: return launch<64, FS>(pl, draft, q, ps, us, u_out, n_accepted, tokens, B, k, V, ws, st);
+  }
+}
+
+int accept_check(const char *who, const int32_t *draft, const float *q, int32_t *n_accepted,
+                 int32_t *tokens, int B, int k, int V) {
+  SPEC_REQUIRE(B > 0 && V > 0 && k >= 0, SPEC_EINVAL, "%s: B=%d k=%d V=%d out of range", who, B,
+               k, V);
+  SPEC_REQUIRE(B <= 65535, SPEC_EUNSUPPORTED,
+               "%s: B=%d sequences exceed 65535 (grid y of the accept kernel)", who, B);
+  SPEC_REQUIRE(k <= kMaxK, SPEC_EUNSUPPORTED, "%s: k=%d exceeds %d (one wave per sequence)", who,
+               k, kMaxK);
+  SPEC_REQUIRE((long)V <= (long)kMaxE * kThreads * kThreads, SPEC_EUNSUPPORTED,
+               "%s: V=%d exceeds %ld", who, V, (long)kMaxE * kThreads * kThreads);
+  SPEC_REQUIRE(n_accepted && tokens && (k == 0 || (draft && q)), SPEC_EINVAL,
+               "%s: null pointer argument", who);
+  return SPEC_OK;
 }
 
 // Shared by spec_accept and spec_accept_philox: checks, workspace, launch.
 int accept_run(const char *who, const int32_t *draft, const float *q, const float *p,
                UniformSource us, float *u_out, int32_t *n_accepted, int32_t *tokens, int B,
                int k, int V, void *workspace, size_t workspace_bytes, void *stream) {
-  SPEC_REQUIRE(B > 0 && V > 0 && k >= 0, SPEC_EINVAL, "%s: B=%d k=%d V=%d out of range", who, B,
-               k, V);
-  SPEC_REQUIRE(B <= 65535, SPEC_EUNSUPPORTED,
-               "%s: B=%d sequences exceed 65535 (grid y of the chunk kernel)", who, B);
-  SPEC_REQUIRE(k <= kMaxK, SPEC_EUNSUPPORTED, "%s: k=%d exceeds %d (one wave per sequence)", who,
-               k, kMaxK);
-  SPEC_REQUIRE((long)V <= (long)kMaxE * kThreads * kThreads, SPEC_EUNSUPPORTED,
-               "%s: V=%d exceeds %ld", who, V, (long)kMaxE * kThreads * kThreads);
-  SPEC_REQUIRE(p && n_accepted && tokens && (k == 0 || (draft && q)), SPEC_EINVAL,
-               "%s: null pointer argument", who);
+  int rc = accept_check(who, draft, q, n_accepted, tokens, B, k, V);
+  if (rc != SPEC_OK) return rc;
+  SPEC_REQUIRE(p != nullptr, SPEC_EINVAL, "%s: null pointer argument", who);
   const AcceptPlan pl = plan(B, V);
   SPEC_REQUIRE(workspace != nullptr && workspace_bytes >= pl.bytes, SPEC_EWORKSPACE,
                "%s: workspace of %zu bytes needed, %zu given", who, pl.bytes, workspace_bytes);
-  char *ws = static_cast<char *>(workspace);
-  uint64_t *wsum = reinterpret_cast<uint64_t *>(ws + pl.off_w);
-  uint64_t *psum = reinterpret_cast<uint64_t *>(ws + pl.off_p);
-  int32_t *nbuf = reinterpret_cast<int32_t *>(ws + pl.off_n);
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  switch (pl.E) {
-    case 1: return launch<1>(pl, draft, q, p, us, u_out, n_accepted, tokens, B, k, V, wsum, psum, nbuf, st);
-    case 2: return launch<2>(pl, draft, q, p, us, u_out, n_accepted, tokens, B, k, V, wsum, psum, nbuf, st);
-    case 4: return launch<4>(pl, draft, q, p, us, u_out, n_accepted, tokens, B, k, V, wsum, psum, nbuf, st);
-    case 8: return launch<8>(pl, draft, q, p, us, u_out, n_accepted, tokens, B, k, V, wsum, psum, nbuf, st);
-    case 16: return launch<16>(pl, draft, q, p, us, u_out, n_accepted, tokens, B, k, V, wsum, psum, nbuf, st);
-    case 32: return launch<32>(pl, draft, q, p, us, u_out, n_accepted, tokens, B, k, V, wsum, psum, nbuf, st);
-    default: return launch<64>(pl, draft, q, p, us, u_out, n_accepted, tokens, B, k, V, wsum, psum, nbuf, st);
-  }
+  const PSource ps{p, nullptr, nullptr};
+  return launch_e<false>(pl, draft, q, ps, us, u_out, n_accepted, tokens, B, k, V,
+                         static_cast<char *>(workspace), static_cast<hipStream_t>(stream));
+}
+
+// Workspace of spec_lm_head_accept: the contraction's output e [R, V], its block and row
+// statistics, the accept step's chunk sums.
+struct FusedPlan {
+  spec::LmLayout lm;
+  AcceptPlan acc;
+  size_t off_e, off_lm, off_acc, bytes;
+};
+
+FusedPlan fused_plan(int B, int k, int V) {
+  FusedPlan f;
+  const int R = B * (k + 1);
+  f.lm = spec::lm_layout(R, V);
+  f.acc = plan(B, V);
+  f.off_e = 0;
+  f.off_lm = spec::align_up((size_t)R * V * sizeof(float), 256);
+  f.off_acc = f.off_lm + spec::align_up(f.lm.bytes, 256);
+  f.bytes = f.off_acc + f.acc.bytes;
+  return f;
 }
 
 }  // namespace
@@ -359,4 +462,47 @@ extern "C" int spec_accept_philox(const int32_t *draft, const float *q, const fl
   return accept_run("spec_accept_philox", draft, q, p, UniformSource{nullptr, seed, offset},
                     uniforms_out, n_accepted, tokens, B, k, V, workspace, workspace_bytes,
                     stream);
+}
+
+extern "C" size_t spec_lm_head_accept_workspace(int B, int k, int H, int V) {
+  spec::clear_error();
+  if (B <= 0 || k < 0 || H <= 0 || V <= 0 || k > kMaxK) {
+    spec::fail(SPEC_EINVAL, "spec_lm_head_accept_workspace: B=%d k=%d H=%d V=%d out of range",
+               B, k, H, V);
+    return 0;
+  }
+  return fused_plan(B, k, V).bytes;
+}
+
+extern "C" int spec_lm_head_accept(const void *hidden, const void *weight,
+                                   const float *temperature, const int32_t *draft,
+                                   const float *q, const float *uniforms, uint64_t seed,
+                                   uint64_t offset, float *uniforms_out, int32_t *n_accepted,
+                                   int32_t *tokens, int B, int k, int H, int V, spec_dtype dtype,
+                                   void *workspace, size_t workspace_bytes, void *stream) {
+  spec::clear_error();
+  const char *who = "spec_lm_head_accept";
+  int rc = accept_check(who, draft, q, n_accepted, tokens, B, k, V);
+  if (rc != SPEC_OK) return rc;
+  SPEC_REQUIRE((long)B * (k + 1) <= 65535, SPEC_EUNSUPPORTED,
+               "%s: B*(k+1)=%ld rows exceed 65535", who, (long)B * (k + 1));
+  const int R = B * (k + 1);
+  const FusedPlan f = fused_plan(B, k, V);
+  SPEC_REQUIRE(workspace != nullptr && workspace_bytes >= f.bytes, SPEC_EWORKSPACE,
+               "%s: workspace of %zu bytes needed, %zu given", who, f.bytes, workspace_bytes);
+  char *ws = static_cast<char *>(workspace);
+  float *e = reinterpret_cast<float *>(ws + f.off_e);
+  rc = spec::lm_head_check(hidden, weight, temperature, e, nullptr, R, H, V, dtype, who);
+  if (rc != SPEC_OK) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const spec::StatsOut so = spec::lm_stats_out(f.lm, ws + f.off_lm);
+  spec::RowStat *rows = reinterpret_cast<spec::RowStat *>(ws + f.off_lm + f.lm.off_rows);
+  rc = spec::lm_head_contract(hidden, weight, temperature, nullptr, e, so, R, H, V, dtype, st);
+  if (rc != SPEC_OK) return rc;
+  rc = spec::lm_row_stats_launch(so, temperature, rows, R, st);
+  if (rc != SPEC_OK) return rc;
+  const PSource ps{e, so.stats, rows};
+  const UniformSource us{uniforms, seed, offset};
+  return launch_e<true>(f.acc, draft, q, ps, us, uniforms_out, n_accepted, tokens, B, k, V,
+                        ws + f.off_acc, st);
 }

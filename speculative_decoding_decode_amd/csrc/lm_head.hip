@@ -122,8 +122,8 @@ __device__ __forceinline__ int swz(int row, int slot) { return row * 128 + ((slo
 template <typename T, int NH>
 __global__ __launch_bounds__(kMmaThreads, 1) void lm_head_mfma(
     const T *__restrict__ X, const T *__restrict__ W, const float *__restrict__ temp,
-    float *__restrict__ logits, float *__restrict__ probs, float2 *__restrict__ stats,
-    int *__restrict__ amax, int R, int H, int V) {
+    float *__restrict__ logits, float *__restrict__ probs, spec::StatsOut so, int R, int H,
+    int V) {
   using M = Mma<T>;
   using S = MmaShape<NH>;
   constexpr int NT = NH;
@@ -305,8 +305,8 @@ __global__ __launch_bounds__(kMmaThreads, 1) void lm_head_mfma(
         }
       const float sum = ((red_s[g0][c] + red_s[g0 + 1][c]) + red_s[g0 + 2][c]) +
                         red_s[g0 + 3][c];
-      stats[(size_t)sb * R + r] = make_float2(m, sum);
-      amax[(size_t)sb * R + r] = a;
+      so.stats[(size_t)sb * R + r] = make_float2(m, sum);
+      so.amax[(size_t)sb * R + r] = a;
     }
   }
 #pragma unroll
@@ -363,8 +363,7 @@ template <int RT>
 __device__ __forceinline__ void gemv_epilogue(const float (&keep)[RT], int v0, int lane, int wave,
                                               int blk, const float *__restrict__ temp,
                                               float *__restrict__ logits, float *__restrict__ probs,
-                                              float2 *__restrict__ stats, int *__restrict__ amax,
-                                              int V) {
+                                              const spec::StatsOut &so, int V) {
   __shared__ float red_m[kWaves][RT];
   __shared__ float red_s[kWaves][RT];
   __shared__ int red_i[kWaves][RT];
@@ -400,8 +399,8 @@ __device__ __forceinline__ void gemv_epilogue(const float (&keep)[RT], int v0, i
     for (int w2 = 1; w2 < kWaves; ++w2)
       if (better(m, a, red_m[w2][r], red_i[w2][r])) { m = red_m[w2][r]; a = red_i[w2][r]; }
     const float sum = ((red_s[0][r] + red_s[1][r]) + red_s[2][r]) + red_s[3][r];
-    stats[(size_t)blk * RT + r] = make_float2(m, sum);
-    amax[(size_t)blk * RT + r] = a;
+    so.stats[(size_t)blk * RT + r] = make_float2(m, sum);
+    so.amax[(size_t)blk * RT + r] = a;
   }
 #pragma unroll
   for (int r = 0; r < RT; ++r)
@@ -422,8 +421,7 @@ __device__ __forceinline__ void gemv_epilogue(const float (&keep)[RT], int v0, i
 template <typename T, int RT>
 __global__ __launch_bounds__(kThreads, 4) void lm_head_gemv(
     const T *__restrict__ X, const T *__restrict__ W, const float *__restrict__ temp,
-    float *__restrict__ logits, float *__restrict__ probs, float2 *__restrict__ stats,
-    int *__restrict__ amax, int H, int V) {
+    float *__restrict__ logits, float *__restrict__ probs, spec::StatsOut so, int H, int V) {
   using Dt = Dot<T>;
   constexpr int EPL = Dt::kEPL;
   constexpr int CE = 8 * EPL;                       // elements per 128-byte chunk
@@ -500,25 +498,25 @@ __global__ __launch_bounds__(kThreads, 4) void lm_head_gemv(
       v += spec::dpp_move<0x141>(v);   // row_half_mirror: the other quad of the 8 lanes
       if (sl == t) keep[r] = v;        // lane 8 g + t: row t + 8 g = v0 + lane
     }
-  gemv_epilogue<RT>(keep, v0, lane, wave, blk, temp, logits, probs, stats, amax, V);
+  gemv_epilogue<RT>(keep, v0, lane, wave, blk, temp, logits, probs, so, V);
 }
 
 template <typename T, int RT>
 int launch_gemv(const void *X, const void *W, const float *temp, float *logits, float *probs,
-                float2 *stats, int *amax, int H, int V, hipStream_t st) {
+                const spec::StatsOut &so, int H, int V, hipStream_t st) {
   hipLaunchKernelGGL((lm_head_gemv<T, RT>), dim3(spec::ceil_div(V, kBlockRows)), dim3(kThreads),
                      0, st, static_cast<const T *>(X), static_cast<const T *>(W), temp, logits,
-                     probs, stats, amax, H, V);
+                     probs, so, H, V);
   return spec::launched("lm_head_gemv");
 }
 
 template <typename T>
 int launch_gemv_r(int R, const void *X, const void *W, const float *temp, float *logits,
-                  float *probs, float2 *stats, int *amax, int H, int V, hipStream_t st) {
+                  float *probs, const spec::StatsOut &so, int H, int V, hipStream_t st) {
   switch (R) {
-    case 1: return launch_gemv<T, 1>(X, W, temp, logits, probs, stats, amax, H, V, st);
-    case 2: return launch_gemv<T, 2>(X, W, temp, logits, probs, stats, amax, H, V, st);
-    default: return launch_gemv<T, 3>(X, W, temp, logits, probs, stats, amax, H, V, st);
+    case 1: return launch_gemv<T, 1>(X, W, temp, logits, probs, so, H, V, st);
+    case 2: return launch_gemv<T, 2>(X, W, temp, logits, probs, so, H, V, st);
+    default: return launch_gemv<T, 3>(X, W, temp, logits, probs, so, H, V, st);
   }
 }
 
@@ -526,22 +524,20 @@ int launch_gemv_r(int R, const void *X, const void *W, const float *temp, float 
 // Grid: (ceil(V / CH), R), CH = 4096 or 16384 vocabulary entries per workgroup (the larger
 // chunk when there are enough rows to fill the GPU, so fewer workgroups repeat the row's
 // statistics reduction and each thread streams more entries).  Every load the workgroup needs
-// (its share of the row's block statistics, the statistics of the blocks it rescales, its p
-// entries) is issued before the first wait, so the kernel costs one memory round trip plus two
-// cross-wave exchanges.
+// (the row's block statistics, its p entries) is issued before the first wait, so the kernel
+// costs one memory round trip plus two exchanges through LDS.
 template <int CH>
 __global__ __launch_bounds__(kThreads) void lm_head_finalize(
     float *__restrict__ probs, const float2 *__restrict__ stats, const int *__restrict__ amax,
     const float *__restrict__ temp, int R, int V, int nblk) {
   constexpr int kPer = CH / kThreads;             // p entries per thread
   constexpr int kBlocks = CH / kBlockRows;        // statistics blocks per chunk
-  __shared__ float sm[spec::kStatWaves], ss[spec::kStatWaves];
-  __shared__ int si[spec::kStatWaves];
   __shared__ float fac[kBlocks];
+  __shared__ float sm[kWaves], ss[kWaves];
+  __shared__ int si[kWaves];
   const int r = blockIdx.y, tid = threadIdx.x;
-  const float tr = temp[r];
-  const bool greedy = !(tr > 0.f);
-  float c[1] = {spec::stat_scale(tr)};
+  const float c = spec::stat_scale(temp[r]);
+  const bool greedy = c == 0.f;
   const int v0 = blockIdx.x * CH;
   const int blk0 = v0 / kBlockRows;
   float *row = probs + (size_t)r * V;
@@ -556,20 +552,14 @@ __global__ __launch_bounds__(kThreads) void lm_head_finalize(
       pv[i] = v < V ? *reinterpret_cast<const float4 *>(row + v) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
   }
-  // statistics of the chunk's own blocks (for the rescale factors)
-  float own_m = 0.f;
-  if (tid < kBlocks && blk0 + tid < nblk) own_m = stats[(size_t)(blk0 + tid) * R + r].x;
-
-  const spec::RowPartial w[1] = {spec::stat_partial(stats, amax, R, r, nblk, c[0], tid)};
-  float gmax[1], gsum[1];
-  int garg[1];
-  spec::stat_reduce<1>(w, c, 1, gmax, garg, gsum, sm, si, ss);
+  // maxima of the chunk's own blocks (for the rescale factors)
+  const float own_m = (tid < kBlocks && blk0 + tid < nblk) ? stats[(size_t)(blk0 + tid) * R + r].x : 0.f;
+  const spec::RowStat rs = spec::row_stat_wg<kThreads>(stats, amax, R, r, nblk, c, sm, ss, si);
   if (greedy) {
-    for (int v = v0 + tid; v < min(V, v0 + CH); v += kThreads) row[v] = (v == garg[0]) ? 1.f : 0.f;
+    for (int v = v0 + tid; v < min(V, v0 + CH); v += kThreads) row[v] = (v == rs.a) ? 1.f : 0.f;
     return;
   }
-  const float inv = 1.f / gsum[0];
-  if (tid < kBlocks) fac[tid] = spec::stat_factor(own_m, gmax[0], c[0], inv);
+  if (tid < kBlocks) fac[tid] = spec::stat_factor(own_m, rs);
   __syncthreads();
   if (vec) {
 #pragma unroll
@@ -587,9 +577,24 @@ __global__ __launch_bounds__(kThreads) void lm_head_finalize(
   }
 }
 
+// Grid: R.  The statistics of row blockIdx.x (the reduction of the finalize, once per row)
+// into rows[r], for the fused lm-head + accept call.
+__global__ __launch_bounds__(kThreads) void lm_row_stats(const float2 *__restrict__ stats,
+                                                         const int *__restrict__ amax,
+                                                         const float *__restrict__ temp,
+                                                         spec::RowStat *__restrict__ rows, int R,
+                                                         int nblk) {
+  __shared__ float sm[kWaves], ss[kWaves];
+  __shared__ int si[kWaves];
+  const int r = blockIdx.x;
+  const spec::RowStat rs =
+      spec::row_stat_wg<kThreads>(stats, amax, R, r, nblk, spec::stat_scale(temp[r]), sm, ss, si);
+  if (threadIdx.x == 0) rows[r] = rs;
+}
+
 template <typename T, int NH>
 int launch_nh(const void *X, const void *W, const float *temp, float *logits, float *probs,
-              float2 *stats, int *amax, int R, int H, int V, hipStream_t st) {
+              const spec::StatsOut &so, int R, int H, int V, hipStream_t st) {
   using S = MmaShape<NH>;
   static std::atomic<uint64_t> lds_set{0};   // per instantiation: one bit per device
   const int rc = spec::ensure_dynamic_lds(reinterpret_cast<const void *>(&lm_head_mfma<T, NH>),
@@ -598,28 +603,27 @@ int launch_nh(const void *X, const void *W, const float *temp, float *logits, fl
   dim3 grid(spec::ceil_div(V, kMmaRows), spec::ceil_div(R, NH * 16));
   hipLaunchKernelGGL((lm_head_mfma<T, NH>), grid, dim3(kMmaThreads), S::kLds, st,
                      static_cast<const T *>(X), static_cast<const T *>(W), temp, logits, probs,
-                     stats, amax, R, H, V);
+                     so, R, H, V);
   return spec::launched("lm_head_mfma");
 }
 
 // One pass over the table covers up to 96 hidden rows; more rows take further passes.
 template <typename T>
 int launch(int R, const void *X, const void *W, const float *temp, float *logits, float *probs,
-           float2 *stats, int *amax, int H, int V, hipStream_t st) {
+           const spec::StatsOut &so, int H, int V, hipStream_t st) {
   switch (min(kMaxNH, spec::ceil_div(R, 16))) {
-    case 1: return launch_nh<T, 1>(X, W, temp, logits, probs, stats, amax, R, H, V, st);
-    case 2: return launch_nh<T, 2>(X, W, temp, logits, probs, stats, amax, R, H, V, st);
-    case 3: return launch_nh<T, 3>(X, W, temp, logits, probs, stats, amax, R, H, V, st);
-    case 4: return launch_nh<T, 4>(X, W, temp, logits, probs, stats, amax, R, H, V, st);
-    case 5: return launch_nh<T, 5>(X, W, temp, logits, probs, stats, amax, R, H, V, st);
-    default: return launch_nh<T, 6>(X, W, temp, logits, probs, stats, amax, R, H, V, st);
+    case 1: return launch_nh<T, 1>(X, W, temp, logits, probs, so, R, H, V, st);
+    case 2: return launch_nh<T, 2>(X, W, temp, logits, probs, so, R, H, V, st);
+    case 3: return launch_nh<T, 3>(X, W, temp, logits, probs, so, R, H, V, st);
+    case 4: return launch_nh<T, 4>(X, W, temp, logits, probs, so, R, H, V, st);
+    case 5: return launch_nh<T, 5>(X, W, temp, logits, probs, so, R, H, V, st);
+    default: return launch_nh<T, 6>(X, W, temp, logits, probs, so, R, H, V, st);
   }
 }
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 thread_local hipEvent_t g_prof_start = nullptr, g_prof_stop = nullptr;
-
 
 }  // namespace
 
@@ -629,25 +633,32 @@ extern "C" int spec_profile_lm_head(void *start_event, void *stop_event) {
   return SPEC_OK;
 }
 
-static_assert(kBlockRows == spec::kStatBlock && kThreads == spec::kStatThreads,
-              "statistics blocks and reducing workgroups must match the shared routine");
+static_assert(kBlockRows == spec::kStatBlock, "statistics blocks of the kernels and the reductions");
 
-namespace {
+namespace spec {
 
-// Workspace of the lm-head statistics: per 256-row vocabulary block and hidden row, (block
-// max, block sum of exp) as float2 [nblk][R] at offset 0, then the block's first argmax as int
-// [nblk][R] at amax_offset.
-struct LmStats {
-  size_t amax_offset, bytes;
-  int nblk;
-};
-
-LmStats lm_stats_layout(int R, int V) {
-  LmStats l;
-  l.nblk = spec::ceil_div(V, kBlockRows);
-  l.amax_offset = spec::align_up((size_t)l.nblk * R * sizeof(float2), 256);
-  l.bytes = l.amax_offset + spec::align_up((size_t)l.nblk * R * sizeof(int), 256);
+LmLayout lm_layout(int R, int V) {
+  LmLayout l;
+  l.nblk = ceil_div(V, kBlockRows);
+  size_t o = 0;
+  l.off_stats = o; o += align_up((size_t)l.nblk * R * sizeof(float2), 256);
+  l.off_amax = o;  o += align_up((size_t)l.nblk * R * sizeof(int), 256);
+  l.off_rows = o;  o += align_up((size_t)R * sizeof(RowStat), 256);
+  l.bytes = o;
   return l;
+}
+
+StatsOut lm_stats_out(const LmLayout &l, void *ws) {
+  char *b = static_cast<char *>(ws);
+  return StatsOut{reinterpret_cast<float2 *>(b + l.off_stats), reinterpret_cast<int *>(b + l.off_amax),
+                  l.nblk};
+}
+
+int lm_row_stats_launch(const StatsOut &so, const float *temperature, RowStat *rows, int R,
+                        hipStream_t st) {
+  hipLaunchKernelGGL(lm_row_stats, dim3(R), dim3(kThreads), 0, st, so.stats, so.amax,
+                     temperature, rows, R, so.nblk);
+  return launched("lm_row_stats");
 }
 
 int lm_head_check(const void *hidden, const void *weight, const float *temperature,
@@ -670,39 +681,53 @@ int lm_head_check(const void *hidden, const void *weight, const float *temperatu
 }
 
 int lm_head_contract(const void *hidden, const void *weight, const float *temperature,
-                     float *logits, float *probs, float2 *stats, int *amax, int R, int H, int V,
+                     float *logits, float *probs, const StatsOut &so, int R, int H, int V,
                      spec_dtype dtype, hipStream_t st) {
-
   hipEvent_t ev0 = g_prof_start, ev1 = g_prof_stop;
   g_prof_start = g_prof_stop = nullptr;
   if (ev0 != nullptr && hipEventRecord(ev0, st) != hipSuccess)
-    return spec::fail(SPEC_EHIP, "spec_lm_head: hipEventRecord(start) failed");
+    return fail(SPEC_EHIP, "spec_lm_head: hipEventRecord(start) failed");
   int rc;
   if (R <= kGemvMaxR)
     rc = dtype == SPEC_BF16
-             ? launch_gemv_r<uint16_t>(R, hidden, weight, temperature, logits, probs, stats, amax, H, V, st)
-             : launch_gemv_r<float>(R, hidden, weight, temperature, logits, probs, stats, amax, H, V, st);
+             ? launch_gemv_r<uint16_t>(R, hidden, weight, temperature, logits, probs, so, H, V, st)
+             : launch_gemv_r<float>(R, hidden, weight, temperature, logits, probs, so, H, V, st);
   else
     rc = dtype == SPEC_BF16
-             ? launch<uint16_t>(R, hidden, weight, temperature, logits, probs, stats, amax, H, V, st)
-             : launch<float>(R, hidden, weight, temperature, logits, probs, stats, amax, H, V, st);
+             ? launch<uint16_t>(R, hidden, weight, temperature, logits, probs, so, H, V, st)
+             : launch<float>(R, hidden, weight, temperature, logits, probs, so, H, V, st);
   if (rc != SPEC_OK) return rc;
   if (ev1 != nullptr && hipEventRecord(ev1, st) != hipSuccess)
-    return spec::fail(SPEC_EHIP, "spec_lm_head: hipEventRecord(stop) failed");
+    return fail(SPEC_EHIP, "spec_lm_head: hipEventRecord(stop) failed");
   return SPEC_OK;
 }
 
-int lm_head_finalize_launch(float *probs, const float2 *stats, const int *amax,
-                            const float *temperature, int R, int V, hipStream_t st) {
-  const int nblk = spec::ceil_div(V, kBlockRows);
+}  // namespace spec
+
+namespace {
+
+int lm_head_finalize_launch(float *probs, const spec::StatsOut &so, const float *temperature,
+                            int R, int V, hipStream_t st) {
   if ((long)R * spec::ceil_div(V, kFinChunk) > kFinWideWGs) {
     hipLaunchKernelGGL(lm_head_finalize<4 * kFinChunk>, dim3(spec::ceil_div(V, 4 * kFinChunk), R),
-                       dim3(kThreads), 0, st, probs, stats, amax, temperature, R, V, nblk);
+                       dim3(kThreads), 0, st, probs, so.stats, so.amax, temperature, R, V, so.nblk);
   } else {
     hipLaunchKernelGGL(lm_head_finalize<kFinChunk>, dim3(spec::ceil_div(V, kFinChunk), R),
-                       dim3(kThreads), 0, st, probs, stats, amax, temperature, R, V, nblk);
+                       dim3(kThreads), 0, st, probs, so.stats, so.amax, temperature, R, V, so.nblk);
   }
   return spec::launched("lm_head_finalize");
+}
+
+// Shared by spec_lm_head and spec_lm_head_noalloc: contraction + finalize with the statistics
+// in `workspace` (at least spec::lm_layout(R, V).bytes).
+int lm_head_run(const void *hidden, const void *weight, const float *temperature, float *logits,
+                float *probs, int R, int H, int V, spec_dtype dtype, void *workspace,
+                hipStream_t st) {
+  const spec::StatsOut so = spec::lm_stats_out(spec::lm_layout(R, V), workspace);
+  const int rc = spec::lm_head_contract(hidden, weight, temperature, logits, probs, so, R, H, V,
+                                        dtype, st);
+  if (rc != SPEC_OK) return rc;
+  return lm_head_finalize_launch(probs, so, temperature, R, V, st);
 }
 
 }  // namespace
@@ -712,37 +737,19 @@ extern "C" size_t spec_lm_head_workspace(int R, int H, int V) {
     spec::fail(SPEC_EINVAL, "spec_lm_head_workspace: R=%d H=%d V=%d must be positive", R, H, V);
     return 0;
   }
-  return lm_stats_layout(R, V).bytes;
+  return spec::lm_layout(R, V).bytes;
 }
-
-namespace {
-
-// Shared by spec_lm_head and spec_lm_head_noalloc: contraction + finalize into `workspace`
-// (at least lm_stats_layout(R, V).bytes).
-int lm_head_run(const void *hidden, const void *weight, const float *temperature, float *logits,
-                float *probs, int R, int H, int V, spec_dtype dtype, void *workspace,
-                hipStream_t st) {
-  const LmStats ls = lm_stats_layout(R, V);
-  float2 *stats = static_cast<float2 *>(workspace);
-  int *amax = reinterpret_cast<int *>(static_cast<char *>(workspace) + ls.amax_offset);
-  const int rc = lm_head_contract(hidden, weight, temperature, logits, probs, stats, amax, R, H,
-                                  V, dtype, st);
-  if (rc != SPEC_OK) return rc;
-  return lm_head_finalize_launch(probs, stats, amax, temperature, R, V, st);
-}
-
-}  // namespace
 
 extern "C" int spec_lm_head(const void *hidden, const void *weight, const float *temperature,
                             float *logits, float *probs, int R, int H, int V, spec_dtype dtype,
                             void *workspace, size_t workspace_bytes, void *stream) {
   spec::clear_error();
-  int rc = lm_head_check(hidden, weight, temperature, probs, logits, R, H, V, dtype,
-                         "spec_lm_head");
+  int rc = spec::lm_head_check(hidden, weight, temperature, probs, logits, R, H, V, dtype,
+                               "spec_lm_head");
   if (rc != SPEC_OK) return rc;
-  const LmStats ls = lm_stats_layout(R, V);
-  SPEC_REQUIRE(workspace != nullptr && workspace_bytes >= ls.bytes, SPEC_EWORKSPACE,
-               "spec_lm_head: workspace of %zu bytes needed, %zu given", ls.bytes, workspace_bytes);
+  const size_t need = spec::lm_layout(R, V).bytes;
+  SPEC_REQUIRE(workspace != nullptr && workspace_bytes >= need, SPEC_EWORKSPACE,
+               "spec_lm_head: workspace of %zu bytes needed, %zu given", need, workspace_bytes);
   return lm_head_run(hidden, weight, temperature, logits, probs, R, H, V, dtype, workspace,
                      static_cast<hipStream_t>(stream));
 }
@@ -791,14 +798,14 @@ extern "C" int spec_lm_head_noalloc(const void *hidden, const void *weight,
                                     const float *temperature, float *logits, float *probs, int R,
                                     int H, int V, spec_dtype dtype, void *stream) {
   spec::clear_error();
-  int rc = lm_head_check(hidden, weight, temperature, probs, logits, R, H, V, dtype,
-                         "spec_lm_head_noalloc");
+  int rc = spec::lm_head_check(hidden, weight, temperature, probs, logits, R, H, V, dtype,
+                               "spec_lm_head_noalloc");
   if (rc != SPEC_OK) return rc;
-  const LmStats ls = lm_stats_layout(R, V);
-  SPEC_REQUIRE(ls.bytes <= (size_t)SPEC_LM_HEAD_STATIC_SCRATCH_BYTES, SPEC_EUNSUPPORTED,
+  const size_t need = spec::lm_layout(R, V).bytes;
+  SPEC_REQUIRE(need <= (size_t)SPEC_LM_HEAD_STATIC_SCRATCH_BYTES, SPEC_EUNSUPPORTED,
                "spec_lm_head_noalloc: R=%d rows over V=%d need %zu bytes of statistics, the "
                "static array holds %zu (use spec_lm_head with a workspace)",
-               R, V, ls.bytes, (size_t)SPEC_LM_HEAD_STATIC_SCRATCH_BYTES);
+               R, V, need, (size_t)SPEC_LM_HEAD_STATIC_SCRATCH_BYTES);
   void *ws = nullptr;
   rc = static_scratch(&ws, "spec_lm_head_noalloc");
   if (rc != SPEC_OK) return rc;

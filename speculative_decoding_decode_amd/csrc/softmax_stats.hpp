@@ -1,115 +1,128 @@
-// Row softmax from the per-block statistics of the lm-head contraction: the reduction every
-// finalize workgroup runs for its row, in a fixed order so all of them get the same bits.
+// Row softmax of the lm-head from the statistics its contraction leaves, shared by the softmax
+// finalize (spec_lm_head) and the row-statistics kernel of the fused lm-head + accept call
+// (spec_lm_head_accept), so both compute every p entry with the same operations on the same
+// values, bit for bit.
 //
-// The contraction kernels leave, for every 256-row block of the vocabulary and every hidden row
-// r, (block max of the logits, sum over the block of exp((z - block max) / T)) in stats and the
-// block's first argmax in amax, and exp((z - block max) / T) in p.  A row's softmax is then
-//   M = max over blocks, L = sum over blocks of sum_blk * exp((max_blk - M) / T),
-//   p = exp((z - max_blk) / T) * exp((max_blk - M) / T) / L,
-// (butteryoon "Gemma 4 MTP 서빙 가이드 해설", section 4: the target's own distribution p over
-// the vocabulary at every verified position; temperature T, T <= 0 meaning greedy one-hot).
-//
+// What is computed (butteryoon "Gemma 4 MTP 서빙 가이드 해설", section 4: the target's own
+// distribution p over the vocabulary at every verified position; temperature T per row, T <= 0
+// meaning greedy one-hot).  With c = log2(e) / T:
+//   block statistics   per 256-row vocabulary block and row: the block max m_b, the sum
+//                      s_b = sum over the block of 2^((z - m_b) c), the block's first argmax;
+//                      the contraction also writes e = 2^((z - m_b) c) in place of p;
+//   row statistics     M = max over blocks, A = first argmax, L = sum_b s_b 2^((m_b - M) c);
+//   p                  p = e * (2^((m_b - M) c) * (1 / L))   (greedy rows: p = [index == A]).
 // Reduction order (fixed, so every workgroup that reduces a row gets the same bits): thread t
-// merges blocks t, t + 256, t + 512, ... in that order; the 64 lanes of a wave are combined by
-// the fixed DPP-and-readlane pattern of spec::wave_reduce (the same bits in every lane); the
-// four waves' results are added in wave order.
+// of a 256-thread workgroup takes the maximum and then the rescaled sum of blocks t, t + 256,
+// ... in order; the 64 lanes of a wave combine by the fixed DPP / readlane pattern of
+// spec::wave_argmax and spec::wave_sum; the four waves' results are combined in wave order.
 #pragma once
+
+#include <limits.h>
 
 #include "common.hpp"
 
 namespace spec {
 
 constexpr int kStatBlock = 256;        // vocabulary rows per statistics block
-constexpr int kStatThreads = 256;      // threads of a workgroup that reduces a row
-constexpr int kStatWaves = kStatThreads / kWave;
-constexpr int kStatsPerThread = 4;     // blocks per thread and pass (V <= 262144 in one pass)
 constexpr float kStatLog2e = 1.4426950408889634f;
-
-__device__ __forceinline__ bool stat_better(float m, int a, float om, int oa) {
-  return first_max_better(m, a, om, oa);
-}
 
 // log2(e) / T, or 0 for a greedy row (T <= 0).
 __device__ __forceinline__ float stat_scale(float t) { return t > 0.f ? kStatLog2e / t : 0.f; }
 
-struct RowPartial {
-  float m;      // running max (-inf before any block)
-  float s;      // running sum, relative to m
-  int a;        // first argmax
+// Where the contraction leaves its statistics ([nblk][R], row fastest).
+struct StatsOut {
+  float2 *stats;      // (block max, block sum)
+  int *amax;          // block first argmax
+  int nblk;
 };
 
-// This thread's merge of blocks tid, tid + 256, ... of row r (stats laid out [nblk][R]).
-__device__ __forceinline__ RowPartial stat_partial(const float2 *__restrict__ stats,
-                                                   const int *__restrict__ amax, int R, int r,
-                                                   int nblk, float c, int tid) {
-  RowPartial w{-INFINITY, 0.f, 0x7fffffff};
-  for (int b0 = 0; b0 < nblk; b0 += kStatThreads * kStatsPerThread) {
-    float2 st[kStatsPerThread];
-    int ia[kStatsPerThread];
-#pragma unroll
-    for (int i = 0; i < kStatsPerThread; ++i) {
-      const int b = b0 + tid + i * kStatThreads;
-      st[i] = b < nblk ? stats[(size_t)b * R + r] : make_float2(-INFINITY, 0.f);
-      ia[i] = b < nblk ? amax[(size_t)b * R + r] : 0x7fffffff;
-    }
-#pragma unroll
-    for (int i = 0; i < kStatsPerThread; ++i) {
-      if (stat_better(w.m, w.a, st[i].x, ia[i])) w.a = ia[i];
-      const float nm = fmaxf(w.m, st[i].x);
-      if (nm != -INFINITY) {
-        w.s = w.s * exp2f((w.m - nm) * c) + st[i].y * exp2f((st[i].x - nm) * c);
-        w.m = nm;
-      }
-    }
-  }
-  return w;
-}
+// Workspace layout of the lm-head statistics (host side; defined in lm_head.hip): block
+// statistics, then the row statistics of the fused call.
+struct LmLayout {
+  int nblk;
+  size_t off_stats, off_amax, off_rows, bytes;
+};
+LmLayout lm_layout(int R, int V);
+StatsOut lm_stats_out(const LmLayout &l, void *ws);
+// Host-side argument checks of the lm-head calls.
+int lm_head_check(const void *hidden, const void *weight, const float *temperature,
+                  const float *probs, const float *logits, int R, int H, int V, spec_dtype dtype,
+                  const char *who);
+// Enqueue the contraction: logits (optional), e = 2^((z - block max) c) into `probs` for rows
+// with T > 0, block statistics into `so`.
+int lm_head_contract(const void *hidden, const void *weight, const float *temperature,
+                     float *logits, float *probs, const StatsOut &so, int R, int H, int V,
+                     spec_dtype dtype, hipStream_t st);
 
+// ---------------------------------------------------------------- row statistics
+struct RowStat {
+  float m;     // row max M
+  float inv;   // 1 / L
+  float c;     // log2(e) / T, 0 for a greedy row
+  int a;       // first argmax A
+};
 
-// Global (max, first argmax) and sum of row partials over the workgroup, for NR rows at once
-// (rows >= nrows are ignored).  sm / si / ss: LDS of kStatWaves * NR entries each.  Every
-// thread gets the results.
-template <int NR>
-__device__ __forceinline__ void stat_reduce(const RowPartial (&w)[NR], float (&c)[NR], int nrows,
-                                            float (&gmax)[NR], int (&garg)[NR], float (&gsum)[NR],
-                                            float *sm, int *si, float *ss) {
+// Enqueue one workgroup per row writing RowStat rows[R] (the fused call's row statistics).
+int lm_row_stats_launch(const StatsOut &so, const float *temperature, RowStat *rows, int R,
+                        hipStream_t st);
+
+// Row statistics of row r from its nblk block statistics, computed by a whole workgroup of
+// THREADS threads in the order stated at the top of this file.  c = stat_scale(T of row r).
+// All threads must call it; every thread gets the result.  sm, ss, si: LDS of THREADS / 64
+// entries each.
+template <int THREADS>
+__device__ RowStat row_stat_wg(const float2 *__restrict__ stats, const int *__restrict__ amax,
+                               int R, int r, int nblk, float c, float *sm, float *ss, int *si) {
+  constexpr int NW = THREADS / kWave, U = 4;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-  float m[NR];
-  int a[NR];
+  float m = -INFINITY, s = 0.f;
+  int a = INT_MAX;
+  for (int base = 0; base < nblk; base += THREADS * U) {
+    float2 v[U];
+    int ia[U];
 #pragma unroll
-  for (int i = 0; i < NR; ++i) {
-    m[i] = w[i].m;
-    a[i] = w[i].a;
-    if (i < nrows) wave_argmax(m[i], a[i]);
-    if (lane == 0) { sm[wave * NR + i] = m[i]; si[wave * NR + i] = a[i]; }
+    for (int u = 0; u < U; ++u) {
+      const int j = min(base + tid + THREADS * u, nblk - 1);
+      v[u] = stats[(size_t)j * R + r];
+      ia[u] = amax[(size_t)j * R + r];
+    }
+    // this thread's maximum (and first argmax) over the batch, then its rescaled sum
+    float bm = -INFINITY;
+    int ba = INT_MAX;
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (base + tid + THREADS * u < nblk && first_max_better(bm, ba, v[u].x, ia[u])) { bm = v[u].x; ba = ia[u]; }
+    if (bm != -INFINITY) {
+      float bs = 0.f;
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (base + tid + THREADS * u < nblk) bs += v[u].y * exp2f((v[u].x - bm) * c);
+      if (first_max_better(m, a, bm, ba)) a = ba;
+      const float nm = fmaxf(m, bm);
+      s = (m == -INFINITY ? 0.f : s * exp2f((m - nm) * c)) + bs * exp2f((bm - nm) * c);
+      m = nm;
+    }
   }
+  float M = m;
+  int A = a;
+  wave_argmax(M, A);
+  const float S = wave_sum(m == -INFINITY ? 0.f : s * exp2f((m - M) * c));
+  if (lane == 0) { sm[wave] = M; ss[wave] = S; si[wave] = A; }
   __syncthreads();
+  float Mw = sm[0];
+  int Aw = si[0];
 #pragma unroll
-  for (int i = 0; i < NR; ++i) {
-    float gm = sm[i];
-    int ga = si[i];
+  for (int w = 1; w < NW; ++w)
+    if (first_max_better(Mw, Aw, sm[w], si[w])) { Mw = sm[w]; Aw = si[w]; }
+  float L = 0.f;
 #pragma unroll
-    for (int x = 1; x < kStatWaves; ++x)
-      if (stat_better(gm, ga, sm[x * NR + i], si[x * NR + i])) { gm = sm[x * NR + i]; ga = si[x * NR + i]; }
-    gmax[i] = gm;
-    garg[i] = ga;
-    float v = w[i].m == -INFINITY ? 0.f : w[i].s * exp2f((w[i].m - gm) * c[i]);
-    if (i < nrows) v = wave_sum(v);
-    if (lane == 0) ss[wave * NR + i] = v;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int i = 0; i < NR; ++i) {
-    float s = ss[i];
-#pragma unroll
-    for (int x = 1; x < kStatWaves; ++x) s += ss[x * NR + i];
-    gsum[i] = s;
-  }
+  for (int w = 0; w < NW; ++w) L += sm[w] == -INFINITY ? 0.f : ss[w] * exp2f((sm[w] - Mw) * c);
+  return RowStat{Mw, 1.f / L, c, Aw};
 }
 
-// Rescale factor of block blk of a row: p = (value stored by the contraction) * factor.
-__device__ __forceinline__ float stat_factor(float blk_max, float gmax, float c, float inv) {
-  return exp2f((blk_max - gmax) * c) * inv;
+// p = e * factor for an entry of the block whose max is blk_max.
+__device__ __forceinline__ float stat_factor(float blk_max, const RowStat &rs) {
+  return exp2f((blk_max - rs.m) * rs.c) * rs.inv;
 }
 
 }  // namespace spec

@@ -118,7 +118,27 @@ def test_lm_head_noalloc_argument_errors(lib):
     assert need > 8 << 20
     assert call(R=700) == EUNSUP
     assert b"static array" in lib.spec_last_error()
-    assert lib.spec_lm_head_workspace(680, 2560, 262144) <= 8 << 20
+    assert lib.spec_lm_head_workspace(681, 2560, 262144) <= 8 << 20
+
+
+def test_lm_head_accept_argument_errors(lib):
+    def call(**kw):
+        a = dict(x=FAKE, w=FAKE, t=FAKE, d=FAKE, q=FAKE, u=None, seed=0, off=0, uo=None,
+                 n=FAKE, tok=FAKE, B=1, k=2, H=2560, V=262144, dtype=1, ws=FAKE, wsb=1 << 32)
+        a.update(kw)
+        return lib.spec_lm_head_accept(*a.values(), None)
+
+    assert call(q=None) == EINVAL
+    assert call(B=0) == EINVAL
+    assert call(k=64) == EUNSUP
+    assert call(H=2564) == EUNSUP
+    assert call(x=FAKE + 8) == EINVAL
+    assert call(B=30000, k=2) == EUNSUP          # 90000 rows
+    assert call(wsb=1 << 20) == EWS
+    need = lib.spec_lm_head_accept_workspace(1, 2, 2560, 262144)
+    # the contraction's exp values [R, V] fp32 plus statistics, sums and counters
+    assert need > 3 * 262144 * 4
+    assert lib.spec_lm_head_accept_workspace(1, 64, 8, 8) == 0
 
 
 def test_accept_argument_errors(lib):
