@@ -560,6 +560,45 @@ def measure(w, steps, warmup, device, two_calls=False):
                 tokens_sampled=emitted / K)
 
 
+def lm_head_rows(device, reps=30):
+    """The lm-head contraction alone at 1..8 rows over 2560- and 5376-wide bf16 tables of 262144
+    rows: the contraction kernel's time per launch (HIP events the library records around it),
+    for the library loaded (SPEC_VERIFY_LIB may name a build whose GEMV serves other row counts,
+    so that both kernels can be timed at every row count)."""
+    import torch
+    import speculative_decoding_decode_amd as sv
+    from speculative_decoding_decode_amd import _lib
+    lib = _lib.load()
+    V = 262144
+    sptr = torch.cuda.current_stream(device).cuda_stream
+    sptr = ctypes.c_void_p(sptr) if sptr else None
+    out = {}
+    for H in (2560, 5376):
+        g = torch.Generator(device=device).manual_seed(H)
+        W = (torch.randn(V, H, generator=g, device=device) / math.sqrt(H)).to(torch.bfloat16)
+        for R in range(1, 9):
+            x = torch.randn(R, H, generator=g, device=device).to(torch.bfloat16)
+            t = torch.ones(R, device=device)
+            probs = torch.empty((R, V), dtype=torch.float32, device=device)
+            ws = torch.empty(sv.lm_head_workspace_bytes(R, H, V), dtype=torch.uint8, device=device)
+            args = (x.data_ptr(), W.data_ptr(), t.data_ptr(), None, probs.data_ptr(), R, H, V,
+                    sv.SPEC_BF16, ws.data_ptr(), ws.numel(), sptr)
+            for _ in range(3):
+                _lib.check("spec_lm_head", lib.spec_lm_head(*args))
+            ev = HipEvents(2 * reps)
+            for i in range(reps):
+                lib.spec_profile_lm_head(ev.ev[2 * i], ev.ev[2 * i + 1])
+                _lib.check("spec_lm_head", lib.spec_lm_head(*args))
+            torch.cuda.synchronize(device)
+            us = float(np.mean([ev.ms(2 * i, 2 * i + 1) for i in range(reps)]) * 1e3)
+            ev.close()
+            out[f"{H}x{R}"] = round(us, 2)
+            log(f"[bench] lm-head H={H} R={R}: {us:.1f} us ({V * H * 2 / (us * 1e-6) / 1e9:.0f} GB/s)")
+        del W
+    print(json.dumps({"metric": "lm-head contraction time per launch, bf16 table 262144 rows",
+                      "unit": "us", "library": _lib.LIB_PATH, "times": out}), flush=True)
+
+
 def sweep_k(w, kmax, steps, warmup, device):
     """The workload's verify step at k = 0..kmax drafts (plain decoding at k = 0): measured step
     time and tokens per step at every k, the verified tokens per second they give, and the k
@@ -603,6 +642,9 @@ def main():
     ap.add_argument("--sweep-k", type=int, default=None, metavar="KMAX",
                     help="time the workload's verify step at k = 0..KMAX drafts and print the "
                          "tokens-per-step curve, throughput per k and the chosen k (one JSON line)")
+    ap.add_argument("--lm-head-rows", action="store_true",
+                    help="only time the lm-head contraction at 1..8 rows over 2560- and 5376-wide "
+                         "tables (one JSON line)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy 10 times (the reference kernel that "
                          "scales rocprofv3 FETCH_SIZE / WRITE_SIZE counters to bytes)")
@@ -637,6 +679,9 @@ def main():
     B, k, K1, V, H = w.batch, w.k, w.k1, w.vocab, w.hidden
     if args.sweep_k is not None:
         sweep_k(w, args.sweep_k, args.steps, args.warmup, device)
+        return
+    if args.lm_head_rows:
+        lm_head_rows(device)
         return
     r = measure(w, args.steps, args.warmup, device, two_calls=args.two_calls)
     inp, lib, sptr, dt, ws_attn, n_out = r["inp"], r["lib"], r["sptr"], r["dt"], r["ws_attn"], r["n_out"]

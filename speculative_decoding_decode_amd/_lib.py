@@ -1,14 +1,16 @@
 """ctypes loader for libspecverify.so: argument and return types of every exported symbol.
 
 The library must have been built in-tree (python -m speculative_decoding_decode_amd.build);
-there is no fallback of any kind: a missing library raises.
+there is no fallback of any kind: a missing library raises.  SPEC_VERIFY_LIB may name another
+build of the same sources (a timing variant, see build.py) to load instead.
 """
 from __future__ import annotations
 
 import ctypes
 import os
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libspecverify.so")
+LIB_PATH = os.environ.get("SPEC_VERIFY_LIB") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "libspecverify.so")
 
 c_int, c_float, c_size_t, c_void_p = ctypes.c_int, ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p
 c_char_p, c_uint64 = ctypes.c_char_p, ctypes.c_uint64

@@ -119,112 +119,21 @@ __device__ __forceinline__ u32x4_t mask16(u32x4_t v, bool keep) {
 // Byte offset of 16-byte slot `slot` of row `row` in a [rows][8 slots] LDS tile.
 __device__ __forceinline__ int swz(int row, int slot) { return row * 128 + ((slot ^ (row >> 1)) & 7) * 16; }
 
-template <typename T, int NH>
-__global__ __launch_bounds__(kMmaThreads, 1) void lm_head_mfma(
-    const T *__restrict__ X, const T *__restrict__ W, const float *__restrict__ temp,
-    float *__restrict__ logits, float *__restrict__ probs, spec::StatsOut so, int R, int H,
-    int V) {
-  using M = Mma<T>;
-  using S = MmaShape<NH>;
-  constexpr int NT = NH;
-  constexpr int EPL = M::kEPL;                    // elements per 16-byte slot
-  constexpr int KC = kMmaSlots * EPL;             // elements per chunk (two MFMA K-steps)
-  constexpr int XS = NT * 16 * kMmaSlots;         // hidden-row slots per chunk
-  constexpr int XL = (XS + kMmaThreads - 1) / kMmaThreads;   // of them per thread
-  extern __shared__ __align__(16) unsigned char smem[];
-
-  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-  const int lr = lane & 15, lq = lane >> 4;           // fragment row / K group
-  const int ls = tid & 7;                             // load slot
-  const int blk = blockIdx.x;
-  const int r0 = blockIdx.y * NT * 16;
-  const int vb = blk * kMmaRows;
-  const int vw = vb + wave * kMmaRowsW;
-  const int nch = (H + KC - 1) / KC;
-  unsigned char *wl = smem;                             // [2][512 rows][128 B]
-  unsigned char *xl = smem + 2 * (size_t)kMmaWBuf;      // [2][NH * 16 rows][128 B]
-
-  struct Chunk {
-    u32x4_t w[kMmaWL];
-    u32x4_t x[XL];
-  };
-  auto fetch = [&](Chunk &ch, int c) __attribute__((always_inline)) {
-    const size_t live = c < nch ? ~(size_t)0 : 0;   // uniform; past the end: offset 0
-    const int kk = min(c * KC + ls * EPL, H - EPL);
-#pragma unroll
-    for (int i = 0; i < kMmaWL; ++i) {
-      const size_t off = (size_t)min(vb + (tid + i * kMmaThreads) / kMmaSlots, V - 1) * H + kk;
-      ch.w[i] = load_stream(W + (off & live));
-    }
-#pragma unroll
-    for (int j = 0; j < XL; ++j) {
-      const int e = min(tid + j * kMmaThreads, XS - 1);
-      const int row = min(r0 + e / kMmaSlots, R - 1);
-      const size_t off = (size_t)row * H + min(c * KC + (e % kMmaSlots) * EPL, H - EPL);
-      ch.x[j] = *reinterpret_cast<const u32x4_t *>(X + (off & live));
-    }
-  };
-  // chunk c (the oldest in the ring) into LDS buffer c & 1; slots past H become zero
-  auto stage = [&](const Chunk &ch, int c) __attribute__((always_inline)) {
-    const int buf = c & 1;
-    const bool in = c * KC + ls * EPL < H;
-#pragma unroll
-    for (int i = 0; i < kMmaWL; ++i)
-      *reinterpret_cast<u32x4_t *>(wl + buf * kMmaWBuf + swz((tid + i * kMmaThreads) / kMmaSlots, ls)) =
-          mask16(ch.w[i], in);
-#pragma unroll
-    for (int j = 0; j < XL; ++j) {
-      const int e = min(tid + j * kMmaThreads, XS - 1);   // duplicates write the same bytes
-      *reinterpret_cast<u32x4_t *>(xl + buf * S::kXBuf + swz(e / kMmaSlots, e % kMmaSlots)) =
-          mask16(ch.x[j], c * KC + (e % kMmaSlots) * EPL < H);
-    }
-  };
-  f32x4_t acc[kMmaVT][NH];
-#pragma unroll
-  for (int vt = 0; vt < kMmaVT; ++vt)
-#pragma unroll
-    for (int n = 0; n < NH; ++n) acc[vt][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  auto compute = [&](int c) __attribute__((always_inline)) {
-    const int buf = c & 1;
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      u32x4_t a[kMmaVT], bx[NH];
-#pragma unroll
-      for (int vt = 0; vt < kMmaVT; ++vt)
-        a[vt] = *reinterpret_cast<const u32x4_t *>(
-            wl + buf * kMmaWBuf + swz(wave * kMmaRowsW + vt * 16 + lr, s * 4 + lq));
-#pragma unroll
-      for (int n = 0; n < NH; ++n)
-        bx[n] = *reinterpret_cast<const u32x4_t *>(
-            xl + buf * S::kXBuf + swz(n * 16 + lr, s * 4 + lq));
-#pragma unroll
-      for (int vt = 0; vt < kMmaVT; ++vt)
-#pragma unroll
-        for (int n = 0; n < NH; ++n) acc[vt][n] = M::run(a[vt], bx[n], acc[vt][n]);
-    }
-  };
-
-  Chunk ring;
-  fetch(ring, 0);
-  stage(ring, 0);
-  fetch(ring, 1);
-  // Scheduling barriers keep each phase where it is written, so the wait before a stage is
-  // for the chunk that stage writes and the next chunk's loads stay in flight.
-  for (int c = 0; c < nch; ++c) {
-    __syncthreads();          // chunk c is in LDS; every wave is done with chunk c - 1
-    __builtin_amdgcn_sched_barrier(0);
-    compute(c);
-    __builtin_amdgcn_sched_barrier(0);
-    stage(ring, c + 1);
-    fetch(ring, c + 2);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-
-  // ---- epilogue: block max / first argmax, then sum of exp, per hidden row.  Hidden row
+// Epilogue of the MFMA contractions: per 256-row statistics block and hidden row, the block
+// max / first argmax and the sum of exp, written to `so`; exp((z - block max) / T) into p (the
+// finalize rescales it); logits stored when asked for.  acc[vt][n]: lane l holds the logits of
+// vocab rows vw + 16 vt + 4 (l / 16) + e for hidden row r0 + 16 n + l % 16.  smem: at least
+// 3 * kMmaWaves * kMaxNH * 16 words of LDS no longer in use.
+template <int NH>
+__device__ __forceinline__ void mfma_epilogue(f32x4_t (&acc)[kMmaVT][NH], unsigned char *smem,
+                                              int wave, int lr, int lq, int vb, int vw, int r0,
+                                              const float *__restrict__ temp,
+                                              float *__restrict__ logits, float *__restrict__ probs,
+                                              const spec::StatsOut &so, int R, int V) {
+  // block max / first argmax, then sum of exp, per hidden row.  Hidden row
   // slot c = n * 16 + lr of the wave is row r0 + 16 n + lr; the four 64-row slices
   // of a statistics block (waves g0 + q) are merged in slice order.
   const int g0 = wave & ~3;                     // first wave of this wave's block
-  __syncthreads();   // the chunk buffers are free: they hold the reduction arrays now
   typedef float RowF[kMaxNH * 16];
   typedef int RowI[kMaxNH * 16];
   RowF *red_m = reinterpret_cast<RowF *>(smem);
@@ -328,10 +237,123 @@ __global__ __launch_bounds__(kMmaThreads, 1) void lm_head_mfma(
   }
 }
 
+template <typename T, int NH>
+__global__ __launch_bounds__(kMmaThreads, 1) void lm_head_mfma(
+    const T *__restrict__ X, const T *__restrict__ W, const float *__restrict__ temp,
+    float *__restrict__ logits, float *__restrict__ probs, spec::StatsOut so, int R, int H,
+    int V) {
+  using M = Mma<T>;
+  using S = MmaShape<NH>;
+  constexpr int NT = NH;
+  constexpr int EPL = M::kEPL;                    // elements per 16-byte slot
+  constexpr int KC = kMmaSlots * EPL;             // elements per chunk (two MFMA K-steps)
+  constexpr int XS = NT * 16 * kMmaSlots;         // hidden-row slots per chunk
+  constexpr int XL = (XS + kMmaThreads - 1) / kMmaThreads;   // of them per thread
+  extern __shared__ __align__(16) unsigned char smem[];
+
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const int lr = lane & 15, lq = lane >> 4;           // fragment row / K group
+  const int ls = tid & 7;                             // load slot
+  const int blk = blockIdx.x;
+  const int r0 = blockIdx.y * NT * 16;
+  const int vb = blk * kMmaRows;
+  const int vw = vb + wave * kMmaRowsW;
+  const int nch = (H + KC - 1) / KC;
+  unsigned char *wl = smem;                             // [2][512 rows][128 B]
+  unsigned char *xl = smem + 2 * (size_t)kMmaWBuf;      // [2][NH * 16 rows][128 B]
+
+  struct Chunk {
+    u32x4_t w[kMmaWL];
+    u32x4_t x[XL];
+  };
+  auto fetch = [&](Chunk &ch, int c) __attribute__((always_inline)) {
+    const size_t live = c < nch ? ~(size_t)0 : 0;   // uniform; past the end: offset 0
+    const int kk = min(c * KC + ls * EPL, H - EPL);
+#pragma unroll
+    for (int i = 0; i < kMmaWL; ++i) {
+      const size_t off = (size_t)min(vb + (tid + i * kMmaThreads) / kMmaSlots, V - 1) * H + kk;
+      ch.w[i] = load_stream(W + (off & live));
+    }
+#pragma unroll
+    for (int j = 0; j < XL; ++j) {
+      const int e = min(tid + j * kMmaThreads, XS - 1);
+      const int row = min(r0 + e / kMmaSlots, R - 1);
+      const size_t off = (size_t)row * H + min(c * KC + (e % kMmaSlots) * EPL, H - EPL);
+      ch.x[j] = *reinterpret_cast<const u32x4_t *>(X + (off & live));
+    }
+  };
+  // chunk c (the oldest in the ring) into LDS buffer c & 1; slots past H become zero
+  auto stage = [&](const Chunk &ch, int c) __attribute__((always_inline)) {
+    const int buf = c & 1;
+    const bool in = c * KC + ls * EPL < H;
+#pragma unroll
+    for (int i = 0; i < kMmaWL; ++i)
+      *reinterpret_cast<u32x4_t *>(wl + buf * kMmaWBuf + swz((tid + i * kMmaThreads) / kMmaSlots, ls)) =
+          mask16(ch.w[i], in);
+#pragma unroll
+    for (int j = 0; j < XL; ++j) {
+      const int e = min(tid + j * kMmaThreads, XS - 1);   // duplicates write the same bytes
+      *reinterpret_cast<u32x4_t *>(xl + buf * S::kXBuf + swz(e / kMmaSlots, e % kMmaSlots)) =
+          mask16(ch.x[j], c * KC + (e % kMmaSlots) * EPL < H);
+    }
+  };
+  f32x4_t acc[kMmaVT][NH];
+#pragma unroll
+  for (int vt = 0; vt < kMmaVT; ++vt)
+#pragma unroll
+    for (int n = 0; n < NH; ++n) acc[vt][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](int c) __attribute__((always_inline)) {
+    const int buf = c & 1;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      u32x4_t a[kMmaVT], bx[NH];
+#pragma unroll
+      for (int vt = 0; vt < kMmaVT; ++vt)
+        a[vt] = *reinterpret_cast<const u32x4_t *>(
+            wl + buf * kMmaWBuf + swz(wave * kMmaRowsW + vt * 16 + lr, s * 4 + lq));
+#pragma unroll
+      for (int n = 0; n < NH; ++n)
+        bx[n] = *reinterpret_cast<const u32x4_t *>(
+            xl + buf * S::kXBuf + swz(n * 16 + lr, s * 4 + lq));
+#pragma unroll
+      for (int vt = 0; vt < kMmaVT; ++vt)
+#pragma unroll
+        for (int n = 0; n < NH; ++n) acc[vt][n] = M::run(a[vt], bx[n], acc[vt][n]);
+    }
+  };
+
+  Chunk ring;
+  fetch(ring, 0);
+  stage(ring, 0);
+  fetch(ring, 1);
+  // Scheduling barriers keep each phase where it is written, so the wait before a stage is
+  // for the chunk that stage writes and the next chunk's loads stay in flight.
+  for (int c = 0; c < nch; ++c) {
+    __syncthreads();          // chunk c is in LDS; every wave is done with chunk c - 1
+    __builtin_amdgcn_sched_barrier(0);
+    compute(c);
+    __builtin_amdgcn_sched_barrier(0);
+    stage(ring, c + 1);
+    fetch(ring, c + 2);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  __syncthreads();   // the chunk buffers are free: they hold the reduction arrays now
+  mfma_epilogue<NH>(acc, smem, wave, lr, lq, vb, vw, r0, temp, logits, probs, so, R, V);
+}
+
 // ------------------------------------------------------------------------- small-R GEMV path
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
-constexpr int kGemvMaxR = 3;         // above this the MFMA contraction streams faster
+// Rows up to which the GEMV serves a call; above it the MFMA contraction streams faster.  Set
+// from kernel times of both measured on MI355X at 1..8 rows over 2560- and 5376-wide tables;
+// a build may override it (SPEC_GEMV_MAX_ROWS) to time one kernel against the other.
+#ifndef SPEC_GEMV_MAX_ROWS
+#define SPEC_GEMV_MAX_ROWS 6
+#endif
+constexpr int kGemvMaxR = SPEC_GEMV_MAX_ROWS;
+constexpr int kGemvMaxInstR = 8;     // GEMV instantiations: 1..8 rows
+static_assert(kGemvMaxR >= 0 && kGemvMaxR <= kGemvMaxInstR, "GEMV rows within its instantiations");
 constexpr int kRowsPerWave = 64;     // one table row per lane in the epilogue
 
 template <typename T> struct Dot;
@@ -419,7 +441,7 @@ __device__ __forceinline__ void gemv_epilogue(const float (&keep)[RT], int v0, i
 // location, and slots past H are zeroed on both operands.  (At three rows one register is
 // spilled around the main loop, not inside it.)
 template <typename T, int RT>
-__global__ __launch_bounds__(kThreads, 4) void lm_head_gemv(
+__global__ __launch_bounds__(kThreads, RT <= 2 ? 4 : RT == 3 ? 3 : 2) void lm_head_gemv(
     const T *__restrict__ X, const T *__restrict__ W, const float *__restrict__ temp,
     float *__restrict__ logits, float *__restrict__ probs, spec::StatsOut so, int H, int V) {
   using Dt = Dot<T>;
@@ -516,7 +538,12 @@ int launch_gemv_r(int R, const void *X, const void *W, const float *temp, float 
   switch (R) {
     case 1: return launch_gemv<T, 1>(X, W, temp, logits, probs, so, H, V, st);
     case 2: return launch_gemv<T, 2>(X, W, temp, logits, probs, so, H, V, st);
-    default: return launch_gemv<T, 3>(X, W, temp, logits, probs, so, H, V, st);
+    case 3: return launch_gemv<T, 3>(X, W, temp, logits, probs, so, H, V, st);
+    case 4: return launch_gemv<T, 4>(X, W, temp, logits, probs, so, H, V, st);
+    case 5: return launch_gemv<T, 5>(X, W, temp, logits, probs, so, H, V, st);
+    case 6: return launch_gemv<T, 6>(X, W, temp, logits, probs, so, H, V, st);
+    case 7: return launch_gemv<T, 7>(X, W, temp, logits, probs, so, H, V, st);
+    default: return launch_gemv<T, 8>(X, W, temp, logits, probs, so, H, V, st);
   }
 }
 

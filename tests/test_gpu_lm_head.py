@@ -55,7 +55,13 @@ def test_tiny_fp32_workload():
                                           (1, 2560, 3001, "bf16"), (3, 2560, 4097, "bf16"),
                                           (3, 5376, 2500, "bf16"), (1, 5376, 777, "bf16"),
                                           (2, 8, 100, "bf16"), (3, 24, 65, "f32"),
-                                          (1, 8, 1, "bf16")])
+                                          (1, 8, 1, "bf16"),
+                                          # bf16 MFMA with table fragments from HBM: hidden
+                                          # widths below one 128-byte chunk, a 256-byte
+                                          # super-chunk (5-6 hidden tiles) with a tail
+                                          (5, 8, 300, "bf16"), (20, 24, 1000, "bf16"),
+                                          (70, 328, 2100, "bf16"), (96, 5376, 1100, "bf16"),
+                                          (200, 200, 600, "bf16")])
 def test_ragged_shapes(R, H, V, dtype):
     torch.manual_seed(R * 7 + V)
     td = torch.float32 if dtype == "f32" else torch.bfloat16
@@ -65,11 +71,12 @@ def test_ragged_shapes(R, H, V, dtype):
     run_and_compare(x, W, temps, dtype, label="ragged")
 
 
-@pytest.mark.parametrize("R", [2, 20])        # GEMV and MFMA paths
-def test_greedy_ties_take_first_index(R):
+@pytest.mark.parametrize("R", [2, 6, 20])     # GEMV and MFMA paths
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_greedy_ties_take_first_index(R, dtype):
     d = dev()
-    x = torch.ones(R, 16, dtype=torch.float32)
-    W = torch.zeros(600, 16, dtype=torch.float32)
+    x = torch.ones(R, 16, dtype=dtype)
+    W = torch.zeros(600, 16, dtype=dtype)
     W[[7, 300, 599]] = 1.0                         # three equal maxima across blocks
     t = torch.zeros(R, device=d)
     _, p = sv.lm_head(x.to(d), W.to(d), t)
@@ -77,15 +84,16 @@ def test_greedy_ties_take_first_index(R):
     assert pc[:, 7].tolist() == [1.0] * R and float(pc.sum()) == float(R)
 
 
-@pytest.mark.parametrize("R", [2, 3, 20])     # the GEMV (two and three rows) and the MFMA path
+@pytest.mark.parametrize("R", [2, 3, 5, 20])  # the GEMV (two, three, five rows) and the MFMA path
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 @pytest.mark.parametrize("ties", [[45, 13, 2, 3, 130], [50, 33, 17], [1, 0], [255, 64, 128, 192],
                                   [63, 62, 61, 48, 47, 31, 16, 15]])
-def test_greedy_ties_within_a_wave(R, ties):
+def test_greedy_ties_within_a_wave(R, dtype, ties):
     # equal maxima on lanes of one 64-row wave in different quads, half rows and rows of 16,
     # and across the waves of one block: the lowest index wins every reduction step
     d = dev()
-    x = torch.ones(R, 16, dtype=torch.float32)
-    W = torch.zeros(600, 16, dtype=torch.float32)
+    x = torch.ones(R, 16, dtype=dtype)
+    W = torch.zeros(600, 16, dtype=dtype)
     W[ties] = 1.0
     W[400] = 0.5                                   # a smaller value elsewhere
     t = torch.zeros(R, device=d)
