@@ -64,8 +64,8 @@ METRIC = "verified tokens/sec and verify-step HBM GB/s (% peak), batch 1, k=2, 8
 PROFILED_TRAFFIC = {
     "workload": DEFAULT_WORKLOAD,
     "source": "speculative_decoding_decode_amd/csrc/lm_head.hip",
-    "sha256": "db7fbf8a4acf56e2529fb152b382c16421ab957b095f5183517b9c5e74b06933",
-    "bytes_per_launch": 1348161125,
+    "sha256": "2946f1e1a62c8f1f04890cb763c1d065528ff239d34590f21d0f60069e814bd2",
+    "bytes_per_launch": 1346044717,
 }
 
 
