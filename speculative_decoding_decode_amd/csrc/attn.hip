@@ -56,6 +56,15 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));   // one 16-byte group
 
+// DPP row_ror:8 on every dword: lane i of each 16-lane row takes lane i ^ 8 of the same row.
+__device__ __forceinline__ u32x4_t rows_ror8(u32x4_t v) {
+  return u32x4_t{(uint32_t)spec::dpp_move<0x128>((int)v[0]), (uint32_t)spec::dpp_move<0x128>((int)v[1]),
+                 (uint32_t)spec::dpp_move<0x128>((int)v[2]), (uint32_t)spec::dpp_move<0x128>((int)v[3])};
+}
+__device__ __forceinline__ u32x4_t rows_pick(bool first, u32x4_t a, u32x4_t b) {
+  return u32x4_t{first ? a[0] : b[0], first ? a[1] : b[1], first ? a[2] : b[2], first ? a[3] : b[3]};
+}
+
 template <int D, typename T, int RT>
 struct AttnShape {
   static constexpr int kEPG = 16 / (int)sizeof(T);       // elements per 16-byte group
@@ -82,8 +91,13 @@ struct AttnShape {
     return n < kRegCap ? n : kRegCap;
   }
   static constexpr bool kSplit = D >= 256 && kWGs(kTiles + kSplitBytes) >= kWGs(kTiles);
-  static constexpr size_t kLds = kTiles + (kSplit ? kSplitBytes : 0);
-  static constexpr int kWavesPerEU = kWGs(kLds);
+  // Head dim 512 in bf16: each wave streams its quarter of the head dim straight into MFMA
+  // operand registers (unit_quarter below); LDS holds only the double-buffered score exchange,
+  // and registers limit occupancy.
+  static constexpr bool kQuarter = D == 512 && sizeof(T) == 2;
+  static constexpr size_t kQuarterLds = 2 * (size_t)kWaves * RT * 64 * 16;
+  static constexpr size_t kLds = kQuarter ? kQuarterLds : kTiles + (kSplit ? kSplitBytes : 0);
+  static constexpr int kWavesPerEU = kQuarter ? (RT == 1 ? 3 : 2) : kWGs(kLds);
 };
 
 // MFMA helpers: QK^T per K-step, PV per page.  16x16 accumulator layout: lane l holds rows
@@ -217,6 +231,203 @@ __device__ __forceinline__ long long pages_before(const int32_t *__restrict__ ct
   return uni64(Pb);
 }
 
+// ---------------------------------------------------------------- head dim 512, bf16
+// One (sequence, KV head, row chunk) unit's pages [pg_begin, pg_begin + npg), with wave w owning
+// the head-dim quarter [128 w, 128 w + 128) of the scores and of the output.  Nothing is staged in
+// LDS: each wave loads its quarter of every page's K and V straight into MFMA operand registers,
+// and the only exchange between waves is the sum of the four partial score tiles of a page
+// (double-buffered in LDS, one workgroup barrier per page).
+//  * Scores S^T = K Q^T.  The contraction over the head dim may take its dims in any order that
+//    K and Q share, so K is loaded with 128-byte runs per key row: in instruction h of a 128-byte
+//    segment, lane 16 G + 8 q + r reads 16-byte slot 4 q + G of key 8 h + r; the A fragment of the
+//    segment's first / second 32-dim K-step (lane 16 G + j: slot 4 s + G of key j) is then, per
+//    dword, instruction 0 or 1 kept or rotated by eight lanes within the 16-lane row (DPP).  Q's
+//    B fragments use the plain layout (row j, slot 4 s + G), loaded once per unit.
+//  * Values O^T[d][row] += V^T[d][key] P^T[key][row].  Lane 16 G + c loads V[keys 4 G .. 4 G + 3]
+//    [dims 8 c .. 8 c + 7] of the quarter (four 16-byte loads, 256 contiguous bytes per key row
+//    and instruction).  In value tile t the A-operand row i stands for dim 8 i + t, so lane
+//    16 G + c takes element t of its own four registers: no transpose, no LDS.  P is split into a
+//    bf16 head and tail (the two halves of the 32-wide contraction), as in AttnMma<uint16_t>::pv.
+//    Accumulator lane (j, q) element e of tile t is output dim 32 q + 8 e + t of the quarter.
+template <int RT>
+__device__ __forceinline__ void unit_quarter(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ kpool,
+    const uint16_t *__restrict__ vpool, const int32_t *__restrict__ table, int *pid_sh,
+    f32x4_t *sred, float2 *__restrict__ part_ml, float *__restrict__ part_acc, int b, int K1,
+    int Hq, int Hkv, int num_pages, int max_pages, int window, float qscale, int g, int G,
+    int rr0, int nr, int pg_begin, int npg, long long piece, int rstride, int ctx) {
+  constexpr int D = 512, DQ = 128, kPage = 16;
+  typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+  const int tid = threadIdx.x, lane = tid & (spec::kWave - 1), wave = tid / spec::kWave;
+  const int lr = lane & 15, lq = lane >> 4;
+  const int r8 = lane & 7, qq = (lane >> 3) & 1;
+
+  // (1) page ids of the piece, then the query fragments of this wave's quarter
+  const int pid_reg = table[(size_t)b * max_pages + pg_begin + min(tid, npg - 1)];
+  u32x4_t qf[RT][4];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int row = rt * 16 + lr;
+    const int rr = rr0 + min(row, nr - 1), i = rr / G, h = g * G + (rr - i * G);
+    const uint16_t *qrow = q + (((size_t)b * K1 + i) * Hq + h) * D + DQ * wave + 8 * lq;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const u32x4_t v = *reinterpret_cast<const u32x4_t *>(qrow + 32 * s);
+      qf[rt][s] = row < nr ? v : u32x4_t{0u, 0u, 0u, 0u};
+    }
+  }
+  if (tid < npg) pid_sh[tid] = (pid_reg >= 0 && pid_reg < num_pages) ? pid_reg : -1;
+  __syncthreads();
+
+  struct PageRegs {
+    u32x4_t k[4];   // segment 2 s + h: keys 8 h .. 8 h + 7, 128-byte run of segment s
+    u32x4_t v[4];   // keys 4 lq + x, dims 8 lr .. 8 lr + 7 of the quarter
+  };
+  // A fetch past the piece reads the pools' first 16 bytes in every lane, so the loads stay
+  // unconditional (exact waits) without a trip to memory.
+  auto fetch = [&](PageRegs &pr, int i) __attribute__((always_inline)) {
+    const bool real = i < npg;
+    const int pid = pid_sh[min(i, npg - 1)];
+    const size_t base = real ? ((size_t)(pid < 0 ? 0 : pid) * Hkv + g) * kPage * D : 0;
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const size_t off = real ? (size_t)(8 * h + r8) * D + DQ * wave + 64 * s + 8 * (4 * qq + lq) : 0;
+        pr.k[2 * s + h] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(kpool + base + off));
+      }
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const size_t off = real ? (size_t)(4 * lq + x) * D + DQ * wave + 8 * lr : 0;
+      pr.v[x] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(vpool + base + off));
+    }
+  };
+
+  int trow[RT];
+  float m_run[RT], l_run[RT];
+  f32x4_t acc[RT][8];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int r = rt * 16 + lr;
+    trow[rt] = r < nr ? ctx - K1 + (rr0 + r) / G : -1;
+    m_run[rt] = -INFINITY;
+    l_run[rt] = 0.f;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) acc[rt][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  const bool two_tiles = nr > 16;   // uniform
+  int par = 0;                      // score-exchange buffer of the next page that is computed
+
+  auto page = [&](const PageRegs &pr, int i) __attribute__((always_inline)) {
+    if (pid_sh[i] < 0) return;       // uniform: an invalid page id hides its keys
+    const int pg = pg_begin + i;
+    f32x4_t part[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) part[rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const u32x4_t k0 = pr.k[2 * s], k1 = pr.k[2 * s + 1];
+      const u32x4_t f0 = rows_pick(lr < 8, k0, rows_ror8(k1));
+      const u32x4_t f1 = rows_pick(lr < 8, rows_ror8(k0), k1);
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        if (rt == 1 && !two_tiles) break;
+        part[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, f0),
+                                                           __builtin_bit_cast(bf16x8, qf[rt][2 * s]), part[rt], 0, 0, 0);
+        part[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, f1),
+                                                           __builtin_bit_cast(bf16x8, qf[rt][2 * s + 1]), part[rt], 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) sred[((par * kWaves + wave) * RT + rt) * 64 + lane] = part[rt];
+    __syncthreads();
+    f32x4_t scs[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      f32x4_t t = sred[((par * kWaves) * RT + rt) * 64 + lane];
+#pragma unroll
+      for (int w2 = 1; w2 < kWaves; ++w2) t += sred[((par * kWaves + w2) * RT + rt) * 64 + lane];
+      scs[rt] = t;
+    }
+    par ^= 1;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      if (rt == 1 && !two_tiles) break;
+      const f32x4_t sc = scs[rt];
+      float sv[4];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int pos = pg * kPage + 4 * lq + e, t = trow[rt];
+        const bool vis = pos <= t && (window == 0 || t - pos < window);
+        sv[e] = vis ? sc[e] * qscale : -INFINITY;
+        mx = fmaxf(mx, sv[e]);
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(m_run[rt], mx);
+      float pr_[4], sum = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        pr_[e] = sv[e] == -INFINITY ? 0.f : exp2f(sv[e] - m_new);
+        sum += pr_[e];
+      }
+      sum += __shfl_xor(sum, 16);
+      sum += __shfl_xor(sum, 32);
+      const float alpha = m_run[rt] == -INFINITY ? 0.f : exp2f(m_run[rt] - m_new);
+      l_run[rt] = l_run[rt] * alpha + sum;
+      m_run[rt] = m_new;
+      bf16x8 bp;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const __bf16 hi = static_cast<__bf16>(pr_[e]);
+        bp[e] = hi;
+        bp[e + 4] = static_cast<__bf16>(pr_[e] - static_cast<float>(hi));
+      }
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        bf16x8 av;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          const uint32_t w32 = pr.v[x][t >> 1];
+          const __bf16 vv = __builtin_bit_cast(__bf16, (uint16_t)((t & 1) ? (w32 >> 16) : (w32 & 0xffffu)));
+          av[x] = vv;
+          av[x + 4] = vv;
+        }
+        acc[rt][t] *= alpha;
+        acc[rt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bp, acc[rt][t], 0, 0, 0);
+      }
+    }
+  };
+
+  PageRegs ra, rb;
+  fetch(ra, 0);
+  fetch(rb, 1);
+  for (int i = 0; i < npg; i += 2) {
+    page(ra, i);
+    fetch(ra, i + 2);
+    if (i + 1 < npg) page(rb, i + 1);
+    fetch(rb, i + 3);
+  }
+  __syncthreads();   // every wave is done with pid_sh and the exchange buffers
+
+  // the piece's partial: lane (j, q) element e of tile t is dim 128 w + 32 q + 8 e + t of row j
+  const size_t base = (size_t)piece * rstride;
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int r = rt * 16 + lr;
+    if (r < nr) {
+      if (wave == 0 && lq == 0) part_ml[base + r] = make_float2(m_run[rt], l_run[rt]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float *dst = part_acc + (base + r) * D + DQ * wave + 32 * lq + 8 * e;
+        *reinterpret_cast<float4 *>(dst) = make_float4(acc[rt][0][e], acc[rt][1][e], acc[rt][2][e], acc[rt][3][e]);
+        *reinterpret_cast<float4 *>(dst + 4) = make_float4(acc[rt][4][e], acc[rt][5][e], acc[rt][6][e], acc[rt][7][e]);
+      }
+    }
+  }
+}
+
 // Grid: nwg workgroups (one per resident slot, or more for very long contexts); a row chunk
 // is 16 * RT query rows.  Per unit: round trips before the first page is in LDS are the
 // piece's page ids, then the queries and the first two pages' K/V together.  Two register
@@ -303,6 +514,13 @@ __global__ __launch_bounds__(kThreads, (AttnShape<D, T, RT>::kWavesPerEU)) void 
     const int nr = min(kRowsWG, GK1 - rr0);
     const long long piece = (long long)w + (long long)b * U + j;
 
+    if constexpr (S::kQuarter) {
+      unit_quarter<RT>(reinterpret_cast<const uint16_t *>(q), reinterpret_cast<const uint16_t *>(kpool),
+                       reinterpret_cast<const uint16_t *>(vpool), table, pid_sh,
+                       reinterpret_cast<f32x4_t *>(smem), part_ml, part_acc, b, K1, Hq, Hkv,
+                       num_pages, max_pages, window, qscale, g, G, rr0, nr, pg_begin, npg, piece,
+                       rstride, sp.ctx);
+    } else {
     // (1) page ids of the piece, then the queries.  Loads are unconditional with clamped
     // indices so the wait counts the compiler inserts stay exact.
     const int pid_reg = table[(size_t)b * max_pages + pg_begin + min(tid, npg - 1)];
@@ -474,6 +692,7 @@ __global__ __launch_bounds__(kThreads, (AttnShape<D, T, RT>::kWavesPerEU)) void 
         }
       }
     }
+    }   // the staged path
 
     p += take;
     if (p >= pend) break;
