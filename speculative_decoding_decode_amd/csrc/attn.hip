@@ -91,13 +91,16 @@ struct AttnShape {
     return n < kRegCap ? n : kRegCap;
   }
   static constexpr bool kSplit = D >= 256 && kWGs(kTiles + kSplitBytes) >= kWGs(kTiles);
-  // Head dim 512 in bf16: each wave streams its quarter of the head dim straight into MFMA
-  // operand registers (unit_quarter below); LDS holds only the double-buffered score exchange,
-  // and registers limit occupancy.
-  static constexpr bool kQuarter = D == 512 && sizeof(T) == 2;
+  // Head dims 256 and 512 in bf16: each wave streams its quarter of the head dim straight into
+  // MFMA operand registers (unit_quarter below); LDS holds only the double-buffered score
+  // exchange, and registers set the resident workgroups per CU: the most that compile without
+  // spills at D = 256 (103 and 148 VGPRs at RT = 1, 2), two at D = 512 (at RT = 1 a third fits,
+  // but the batch-32 workload streamed 3% slower with it on MI355X).
+  static constexpr bool kQuarter = (D == 512 || D == 256) && sizeof(T) == 2;
   static constexpr size_t kQuarterLds = 2 * (size_t)kWaves * RT * 64 * 16;
   static constexpr size_t kLds = kQuarter ? kQuarterLds : kTiles + (kSplit ? kSplitBytes : 0);
-  static constexpr int kWavesPerEU = kQuarter ? (RT == 1 ? 3 : 2) : kWGs(kLds);
+  static constexpr int kQuarterWaves = D == 512 ? 2 : (RT == 1 ? 4 : 3);
+  static constexpr int kWavesPerEU = kQuarter ? kQuarterWaves : kWGs(kLds);
 };
 
 // MFMA helpers: QK^T per K-step, PV per page.  16x16 accumulator layout: lane l holds rows
@@ -231,9 +234,9 @@ __device__ __forceinline__ long long pages_before(const int32_t *__restrict__ ct
   return uni64(Pb);
 }
 
-// ---------------------------------------------------------------- head dim 512, bf16
+// ---------------------------------------------------------------- head dims 256 and 512, bf16
 // One (sequence, KV head, row chunk) unit's pages [pg_begin, pg_begin + npg), with wave w owning
-// the head-dim quarter [128 w, 128 w + 128) of the scores and of the output.  Nothing is staged in
+// the head-dim quarter [DQ w, DQ w + DQ), DQ = D / 4, of the scores and of the output.  Nothing is staged in
 // LDS: each wave loads its quarter of every page's K and V straight into MFMA operand registers,
 // and the only exchange between waves is the sum of the four partial score tiles of a page
 // (double-buffered in LDS, one workgroup barrier per page).
@@ -243,20 +246,26 @@ __device__ __forceinline__ long long pages_before(const int32_t *__restrict__ ct
 //    segment's first / second 32-dim K-step (lane 16 G + j: slot 4 s + G of key j) is then, per
 //    dword, instruction 0 or 1 kept or rotated by eight lanes within the 16-lane row (DPP).  Q's
 //    B fragments use the plain layout (row j, slot 4 s + G), loaded once per unit.
-//  * Values O^T[d][row] += V^T[d][key] P^T[key][row].  Lane 16 G + c loads V[keys 4 G .. 4 G + 3]
-//    [dims 8 c .. 8 c + 7] of the quarter (four 16-byte loads, 256 contiguous bytes per key row
-//    and instruction).  In value tile t the A-operand row i stands for dim 8 i + t, so lane
-//    16 G + c takes element t of its own four registers: no transpose, no LDS.  P is split into a
-//    bf16 head and tail (the two halves of the 32-wide contraction), as in AttnMma<uint16_t>::pv.
-//    Accumulator lane (j, q) element e of tile t is output dim 32 q + 8 e + t of the quarter.
-template <int RT>
+//  * Values O^T[d][row] += V^T[d][key] P^T[key][row].  With E = DQ / 16 dims per lane, lane
+//    16 G + c loads V[keys 4 G .. 4 G + 3][dims E c .. E c + E - 1] of the quarter (four loads of
+//    2 E bytes, 32 E contiguous bytes per key row and instruction).  In value tile t (t < E) the
+//    A-operand row i stands for dim E i + t, so lane 16 G + c takes element t of its own four
+//    registers: no transpose, no LDS.  P is split into a bf16 head and tail (the two halves of
+//    the 32-wide contraction), as in AttnMma<uint16_t>::pv.  Accumulator lane (j, q) element e
+//    of tile t is output dim E (4 q + e) + t of the quarter.
+template <int D, int RT>
 __device__ __forceinline__ void unit_quarter(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ kpool,
     const uint16_t *__restrict__ vpool, const int32_t *__restrict__ table, int *pid_sh,
     f32x4_t *sred, float2 *__restrict__ part_ml, float *__restrict__ part_acc, int b, int K1,
     int Hq, int Hkv, int num_pages, int max_pages, int window, float qscale, int g, int G,
     int rr0, int nr, int pg_begin, int npg, long long piece, int rstride, int ctx) {
-  constexpr int D = 512, DQ = 128, kPage = 16;
+  constexpr int DQ = D / 4, kPage = 16;
+  constexpr int KS = DQ / 32;            // 32-dim K-steps of the quarter
+  constexpr int SEG = DQ / 64;           // 128-byte segments of a key row's quarter
+  constexpr int E = DQ / 16;             // V dims per lane, value tiles per wave
+  typedef uint32_t vreg_t __attribute__((ext_vector_type(E / 2)));
+  static_assert(SEG >= 1 && (E == 4 || E == 8), "quarters of 64 or 128 dims");
   typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
   const int tid = threadIdx.x, lane = tid & (spec::kWave - 1), wave = tid / spec::kWave;
   const int lr = lane & 15, lq = lane >> 4;
@@ -264,14 +273,14 @@ __device__ __forceinline__ void unit_quarter(
 
   // (1) page ids of the piece, then the query fragments of this wave's quarter
   const int pid_reg = table[(size_t)b * max_pages + pg_begin + min(tid, npg - 1)];
-  u32x4_t qf[RT][4];
+  u32x4_t qf[RT][KS];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     const int row = rt * 16 + lr;
     const int rr = rr0 + min(row, nr - 1), i = rr / G, h = g * G + (rr - i * G);
     const uint16_t *qrow = q + (((size_t)b * K1 + i) * Hq + h) * D + DQ * wave + 8 * lq;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
+    for (int s = 0; s < KS; ++s) {
       const u32x4_t v = *reinterpret_cast<const u32x4_t *>(qrow + 32 * s);
       qf[rt][s] = row < nr ? v : u32x4_t{0u, 0u, 0u, 0u};
     }
@@ -280,8 +289,8 @@ __device__ __forceinline__ void unit_quarter(
   __syncthreads();
 
   struct PageRegs {
-    u32x4_t k[4];   // segment 2 s + h: keys 8 h .. 8 h + 7, 128-byte run of segment s
-    u32x4_t v[4];   // keys 4 lq + x, dims 8 lr .. 8 lr + 7 of the quarter
+    u32x4_t k[2 * SEG];   // 2 s + h: keys 8 h .. 8 h + 7, 128-byte run of segment s
+    vreg_t v[4];          // keys 4 lq + x, dims E lr .. E lr + E - 1 of the quarter
   };
   // A fetch past the piece reads the pools' first 16 bytes in every lane, so the loads stay
   // unconditional (exact waits) without a trip to memory.
@@ -290,7 +299,7 @@ __device__ __forceinline__ void unit_quarter(
     const int pid = pid_sh[min(i, npg - 1)];
     const size_t base = real ? ((size_t)(pid < 0 ? 0 : pid) * Hkv + g) * kPage * D : 0;
 #pragma unroll
-    for (int s = 0; s < 2; ++s)
+    for (int s = 0; s < SEG; ++s)
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const size_t off = real ? (size_t)(8 * h + r8) * D + DQ * wave + 64 * s + 8 * (4 * qq + lq) : 0;
@@ -298,14 +307,14 @@ __device__ __forceinline__ void unit_quarter(
       }
 #pragma unroll
     for (int x = 0; x < 4; ++x) {
-      const size_t off = real ? (size_t)(4 * lq + x) * D + DQ * wave + 8 * lr : 0;
-      pr.v[x] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(vpool + base + off));
+      const size_t off = real ? (size_t)(4 * lq + x) * D + DQ * wave + E * lr : 0;
+      pr.v[x] = __builtin_nontemporal_load(reinterpret_cast<const vreg_t *>(vpool + base + off));
     }
   };
 
   int trow[RT];
   float m_run[RT], l_run[RT];
-  f32x4_t acc[RT][8];
+  f32x4_t acc[RT][E];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     const int r = rt * 16 + lr;
@@ -313,7 +322,7 @@ __device__ __forceinline__ void unit_quarter(
     m_run[rt] = -INFINITY;
     l_run[rt] = 0.f;
 #pragma unroll
-    for (int t = 0; t < 8; ++t) acc[rt][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < E; ++t) acc[rt][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
   const bool two_tiles = nr > 16;   // uniform
   int par = 0;                      // score-exchange buffer of the next page that is computed
@@ -325,7 +334,7 @@ __device__ __forceinline__ void unit_quarter(
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) part[rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
+    for (int s = 0; s < SEG; ++s) {
       const u32x4_t k0 = pr.k[2 * s], k1 = pr.k[2 * s + 1];
       const u32x4_t f0 = rows_pick(lr < 8, k0, rows_ror8(k1));
       const u32x4_t f1 = rows_pick(lr < 8, rows_ror8(k0), k1);
@@ -385,7 +394,7 @@ __device__ __forceinline__ void unit_quarter(
         bp[e + 4] = static_cast<__bf16>(pr_[e] - static_cast<float>(hi));
       }
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
+      for (int t = 0; t < E; ++t) {
         bf16x8 av;
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
@@ -411,7 +420,7 @@ __device__ __forceinline__ void unit_quarter(
   }
   __syncthreads();   // every wave is done with pid_sh and the exchange buffers
 
-  // the piece's partial: lane (j, q) element e of tile t is dim 128 w + 32 q + 8 e + t of row j
+  // the piece's partial: lane (j, q) element e of tile t is dim DQ w + E (4 q + e) + t of row j
   const size_t base = (size_t)piece * rstride;
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
@@ -420,9 +429,11 @@ __device__ __forceinline__ void unit_quarter(
       if (wave == 0 && lq == 0) part_ml[base + r] = make_float2(m_run[rt], l_run[rt]);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        float *dst = part_acc + (base + r) * D + DQ * wave + 32 * lq + 8 * e;
-        *reinterpret_cast<float4 *>(dst) = make_float4(acc[rt][0][e], acc[rt][1][e], acc[rt][2][e], acc[rt][3][e]);
-        *reinterpret_cast<float4 *>(dst + 4) = make_float4(acc[rt][4][e], acc[rt][5][e], acc[rt][6][e], acc[rt][7][e]);
+        float *dst = part_acc + (base + r) * D + DQ * wave + E * (4 * lq + e);
+#pragma unroll
+        for (int t0 = 0; t0 < E; t0 += 4)
+          *reinterpret_cast<float4 *>(dst + t0) =
+              make_float4(acc[rt][t0][e], acc[rt][t0 + 1][e], acc[rt][t0 + 2][e], acc[rt][t0 + 3][e]);
       }
     }
   }
@@ -515,7 +526,7 @@ __global__ __launch_bounds__(kThreads, (AttnShape<D, T, RT>::kWavesPerEU)) void 
     const long long piece = (long long)w + (long long)b * U + j;
 
     if constexpr (S::kQuarter) {
-      unit_quarter<RT>(reinterpret_cast<const uint16_t *>(q), reinterpret_cast<const uint16_t *>(kpool),
+      unit_quarter<D, RT>(reinterpret_cast<const uint16_t *>(q), reinterpret_cast<const uint16_t *>(kpool),
                        reinterpret_cast<const uint16_t *>(vpool), table, pid_sh,
                        reinterpret_cast<f32x4_t *>(smem), part_ml, part_acc, b, K1, Hq, Hkv,
                        num_pages, max_pages, window, qscale, g, G, rr0, nr, pg_begin, npg, piece,
