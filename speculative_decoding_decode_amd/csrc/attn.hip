@@ -15,10 +15,12 @@
 // device from the context lengths (each workgroup and each merge wave derives the same
 // numbers).  Within a share a workgroup walks the pages of each (sequence, KV head, row chunk)
 // unit it touches: each 16-token page of K and of V is one contiguous 16*D block per head,
-// read with coalesced, nontemporal 16-byte loads (each page is read once per call) two pages
-// ahead and staged through LDS; scores come from MFMAs (keys x rows tile), the online softmax
-// runs in registers with wavefront shuffles, and the value update is a second MFMA per 16
-// columns of the head dim.  For every unit it touches
+// read with nontemporal 16-byte loads (each page is read once per call) two pages ahead.  At
+// head dims 64 and 128, in fp32, and at head dim 256 with two row tiles, pages are staged
+// through LDS; at head dim 512, and 256 with one row tile, in bf16, each wave loads its
+// quarter of the head dim straight into MFMA operand registers (unit_quarter).  Scores come
+// from MFMAs (keys x rows tile), the online softmax runs in registers with wavefront shuffles,
+// and the value update is a second MFMA per 16 columns of the head dim.  For every unit it touches
 // the workgroup writes one partial (max, sum, unnormalised output); a second kernel merges the
 // partials of each output row with log-sum-exp weights, one workgroup per row.  All
 // exponentials are base 2 with log2(e) folded into the query scale.
@@ -91,15 +93,17 @@ struct AttnShape {
     return n < kRegCap ? n : kRegCap;
   }
   static constexpr bool kSplit = D >= 256 && kWGs(kTiles + kSplitBytes) >= kWGs(kTiles);
-  // Head dims 256 and 512 in bf16: each wave streams its quarter of the head dim straight into
-  // MFMA operand registers (unit_quarter below); LDS holds only the double-buffered score
-  // exchange, and registers set the resident workgroups per CU: the most that compile without
-  // spills at D = 256 (103 and 148 VGPRs at RT = 1, 2), two at D = 512 (at RT = 1 a third fits,
-  // but the batch-32 workload streamed 3% slower with it on MI355X).
-  static constexpr bool kQuarter = (D == 512 || D == 256) && sizeof(T) == 2;
+  // Head dim 512, and head dim 256 at one row tile, in bf16: each wave streams its quarter of
+  // the head dim straight into MFMA operand registers (unit_quarter below); LDS holds only the
+  // double-buffered score exchange, and registers set the resident workgroups per CU: four at
+  // D = 256 (103 VGPRs, the most without spills), two at D = 512 (a third fits at one row tile,
+  // but the batch-32 workload streamed 3% slower with it on MI355X).  Head dim 256 at two row
+  // tiles stays with the LDS-staged path, which measured 6% faster there (15.9 against 16.9 us
+  // per sliding layer at batch 8, k = 5).
+  static constexpr bool kQuarter = (D == 512 || (D == 256 && RT == 1)) && sizeof(T) == 2;
   static constexpr size_t kQuarterLds = 2 * (size_t)kWaves * RT * 64 * 16;
   static constexpr size_t kLds = kQuarter ? kQuarterLds : kTiles + (kSplit ? kSplitBytes : 0);
-  static constexpr int kQuarterWaves = D == 512 ? 2 : (RT == 1 ? 4 : 3);
+  static constexpr int kQuarterWaves = D == 512 ? 2 : 4;
   static constexpr int kWavesPerEU = kQuarter ? kQuarterWaves : kWGs(kLds);
 };
 

@@ -9,7 +9,7 @@
 //
 // Design (gfx950).  Two contraction kernels share one softmax finalize; which one runs was
 // set by timing both on MI355X at 1..8 rows:
-//  * R <= 3 rows (batch-1 verification): a bandwidth-bound GEMV.  Each wave owns 64 table rows
+//  * R <= 6 rows (batch-1 verification): a bandwidth-bound GEMV.  Each wave owns 64 table rows
 //    and walks the hidden dimension in 128-byte chunks, eight rows per load instruction, with
 //    nontemporal loads (the table is used once per call); every lane accumulates its slot of
 //    eight rows in fp32 with v_dot2_f32_bf16 (fp32 tables: FMAs) and a three-step DPP
@@ -429,7 +429,7 @@ __device__ __forceinline__ void gemv_epilogue(const float (&keep)[RT], int v0, i
     if (vok && !greedy[r]) probs[(size_t)r * V + v] = ex[r];
 }
 
-// Grid: ceil(V / 256).  The GEMV for R <= 3 rows and any H.  A wave owns 64 table rows and
+// Grid: ceil(V / 256).  The GEMV for R <= kGemvMaxR rows and any H.  A wave owns 64 table rows and
 // walks the hidden dimension in chunks of 128 bytes: one load instruction covers 8 rows x 128
 // contiguous bytes (lane 8 g + s reads 16-byte slot s of row t + 8 g of the wave's 64, for
 // load t = 0..7), so a chunk of the wave's 64 rows is eight nontemporal loads and the same
@@ -438,8 +438,8 @@ __device__ __forceinline__ void gemv_epilogue(const float (&keep)[RT], int v0, i
 // only cross-lane work is one three-step DPP reduction inside each 8-lane group at the end
 // (quad swaps and the half-row mirror), after which lane 8 g + t holds row t + 8 g's logits.
 // Two chunks are in flight per wave; a fetch past the last chunk reads one valid 16-byte
-// location, and slots past H are zeroed on both operands.  (At three rows one register is
-// spilled around the main loop, not inside it.)
+// location, and slots past H are zeroed on both operands.  Registers grow by 16 VGPRs per row
+// (97 at one row, 177 at six), so four, three or two workgroups fit per CU.
 template <typename T, int RT>
 __global__ __launch_bounds__(kThreads, RT <= 2 ? 4 : RT == 3 ? 3 : 2) void lm_head_gemv(
     const T *__restrict__ X, const T *__restrict__ W, const float *__restrict__ temp,
