@@ -64,8 +64,8 @@ METRIC = "verified tokens/sec and verify-step HBM GB/s (% peak), batch 1, k=2, 8
 PROFILED_TRAFFIC = {
     "workload": DEFAULT_WORKLOAD,
     "source": "speculative_decoding_decode_amd/csrc/lm_head.hip",
-    "sha256": "2946f1e1a62c8f1f04890cb763c1d065528ff239d34590f21d0f60069e814bd2",
-    "bytes_per_launch": 1346044717,
+    "sha256": "b837444bb7932bc65f866fd6187ae5fafb344f06ce82718a4dbc85dd7f8b30eb",
+    "bytes_per_launch": 1346056370,
 }
 
 
