@@ -26,11 +26,11 @@
 // counter, measured slower on MI355X at batch 1: the counter's round trip and the device-scope
 // reads of the chunk sums cost more than the second launch.)
 //
-// spec_lm_head_accept runs the lm-head contraction and this kernel back to back, without the
-// softmax finalize pass over p: the accept kernel forms the p values it needs (at the drafts and
-// in its chunk of row n) from the contraction's exp values and statistics, with the operations
-// of the finalize (softmax_stats.hpp), so its results equal spec_lm_head + spec_accept bit for
-// bit.  This is the sampling pipeline run as part of the verify forward, the role the serving
+// spec_lm_head_accept runs the lm-head contraction, the row statistics (lm_row_stats, once per
+// row) and these two kernels back to back, without the softmax finalize pass over p: the accept
+// kernels form the p values they need (at the drafts and in the chunks of row n) from the
+// contraction's exp values and the row statistics, with the operations of the finalize
+// (softmax_stats.hpp), so the results equal spec_lm_head + spec_accept bit for bit.  This is the sampling pipeline run as part of the verify forward, the role the serving
 // guide gives its dedicated sampling backend (butteryoon "Gemma 4 MTP 서빙 가이드 해설",
 // section 7 settings table).
 #include "common.hpp"
