@@ -68,7 +68,10 @@ def small_workload(dtype, hq, hkv, d, window, k, batch=3):
 
 @pytest.mark.parametrize("dtype,hq,hkv,d,window,k", [
     ("bf16", 6, 3, 128, 37, 3), ("f32", 4, 1, 256, 0, 1), ("f32", 8, 2, 512, 100, 5),
-    ("bf16", 12, 1, 64, 0, 4), ("bf16", 4, 4, 256, 1, 2), ("f32", 16, 2, 64, 0, 9)])
+    ("bf16", 12, 1, 64, 0, 4), ("bf16", 4, 4, 256, 1, 2), ("f32", 16, 2, 64, 0, 9),
+    # bf16 head dims 256 and 512 at one and two row tiles (head-dim-quarter and staged paths)
+    ("bf16", 8, 2, 512, 50, 1), ("bf16", 8, 2, 512, 0, 5), ("bf16", 8, 2, 256, 37, 4),
+    ("bf16", 8, 2, 256, 0, 3)])
 def test_ragged_small(dtype, hq, hkv, d, window, k):
     w = small_workload(dtype, hq, hkv, d, window, k)
     ctx = np.array([k + 1, 333, 170], dtype=np.int32)         # minimal, ragged, page-ragged
@@ -116,16 +119,17 @@ def test_deterministic_repeat():
     assert torch.equal(a, b)
 
 
-@pytest.mark.parametrize("dtype,window,k", [("bf16", 0, 2), ("f32", 40, 0)])
-def test_many_sequences(dtype, window, k):
+@pytest.mark.parametrize("dtype,window,k,d", [("bf16", 0, 2, 128), ("f32", 40, 0, 128),
+                                             ("bf16", 0, 2, 512), ("bf16", 30, 1, 256)])
+def test_many_sequences(dtype, window, k, d):
     """More than 64 sequences (the work split scans the context lengths 64 at a time), ragged,
     with empty contexts and contexts holding only the verified positions."""
     B = 150
-    w = small_workload(dtype, 4, 2, 128, window, k, batch=B)
+    w = small_workload(dtype, 4, 2, d, window, k, batch=B)
     rng = np.random.default_rng(21)
     ctx = rng.integers(k + 1, 700, size=B).astype(np.int32)
     ctx[[3, 70, 149]] = 0                                   # nothing cached
     ctx[[5, 100]] = k + 1                                   # only the verified positions
     table, P = gen.page_tables(w, ctx, max_pages=44)
     inp = attn_inputs(w, 0, dev(), ctx=ctx, table=table, num_pages=P)
-    check(inp, dtype, f"{B} ragged sequences {dtype} window {window} k {k}")
+    check(inp, dtype, f"{B} ragged sequences {dtype} hd{d} window {window} k {k}")
