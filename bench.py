@@ -64,8 +64,8 @@ METRIC = "verified tokens/sec and verify-step HBM GB/s (% peak), batch 1, k=2, 8
 PROFILED_TRAFFIC = {
     "workload": DEFAULT_WORKLOAD,
     "source": "speculative_decoding_decode_amd/csrc/lm_head.hip",
-    "sha256": "b837444bb7932bc65f866fd6187ae5fafb344f06ce82718a4dbc85dd7f8b30eb",
-    "bytes_per_launch": 1346056370,
+    "sha256": "8ddec85a4911862f273c2300fbc566c904bd8902109870ea6caa46b93a714ea9",
+    "bytes_per_launch": 1346056602,
 }
 
 
@@ -565,41 +565,48 @@ def measure(w, steps, warmup, device, two_calls=False):
 
 
 def lm_head_rows(device, reps=30):
-    """The lm-head contraction alone at 1..8 rows over 2560- and 5376-wide bf16 tables of 262144
-    rows: the contraction kernel's time per launch (HIP events the library records around it),
-    for the library loaded (SPEC_VERIFY_LIB may name a build whose GEMV serves other row counts,
-    so that both kernels can be timed at every row count)."""
+    """The lm-head contraction at 1..8 rows over 2560- and 5376-wide bf16 tables of 262144 rows,
+    timed inside the call the verify step makes (spec_lm_head_accept for one sequence with k =
+    R - 1 drafts: contraction, row statistics, accept): the contraction kernel's time per launch
+    (HIP events the library records around it), for the library loaded (SPEC_VERIFY_LIB may name
+    a build whose GEMV serves other row counts, so that both kernels can be timed at every row
+    count).  Each shape runs 3 untimed and `reps` timed calls."""
     import torch
     import speculative_decoding_decode_amd as sv
     from speculative_decoding_decode_amd import _lib
     lib = _lib.load()
     V = 262144
-    sptr = torch.cuda.current_stream(device).cuda_stream
-    sptr = ctypes.c_void_p(sptr) if sptr else None
     out = {}
     for H in (2560, 5376):
         g = torch.Generator(device=device).manual_seed(H)
         W = (torch.randn(V, H, generator=g, device=device) / math.sqrt(H)).to(torch.bfloat16)
         for R in range(1, 9):
+            k = R - 1
             x = torch.randn(R, H, generator=g, device=device).to(torch.bfloat16)
             t = torch.ones(R, device=device)
-            probs = torch.empty((R, V), dtype=torch.float32, device=device)
-            ws = torch.empty(sv.lm_head_workspace_bytes(R, H, V), dtype=torch.uint8, device=device)
-            args = (x.data_ptr(), W.data_ptr(), t.data_ptr(), None, probs.data_ptr(), R, H, V,
-                    sv.SPEC_BF16, ws.data_ptr(), ws.numel(), sptr)
+            draft = torch.randint(0, V, (1, k), generator=g, device=device, dtype=torch.int32)
+            q = torch.softmax(torch.randn(1, k, V, generator=g, device=device), dim=-1) if k else None
+            u = torch.rand(1, R, generator=g, device=device)
+            n_acc = torch.empty(1, dtype=torch.int32, device=device)
+            tok = torch.empty(1, R, dtype=torch.int32, device=device)
+            ws = torch.zeros(sv.lm_head_accept_workspace_bytes(1, k, H, V), dtype=torch.uint8,
+                             device=device)
+            call = lambda: sv.lm_head_accept(x, W, t, draft, q, uniforms=u, n_accepted=n_acc,
+                                             tokens=tok, workspace=ws)
             for _ in range(3):
-                _lib.check("spec_lm_head", lib.spec_lm_head(*args))
+                call()
             ev = HipEvents(2 * reps)
             for i in range(reps):
                 lib.spec_profile_lm_head(ev.ev[2 * i], ev.ev[2 * i + 1])
-                _lib.check("spec_lm_head", lib.spec_lm_head(*args))
+                call()
             torch.cuda.synchronize(device)
             us = float(np.mean([ev.ms(2 * i, 2 * i + 1) for i in range(reps)]) * 1e3)
             ev.close()
             out[f"{H}x{R}"] = round(us, 2)
             log(f"[bench] lm-head H={H} R={R}: {us:.1f} us ({V * H * 2 / (us * 1e-6) / 1e9:.0f} GB/s)")
         del W
-    print(json.dumps({"metric": "lm-head contraction time per launch, bf16 table 262144 rows",
+    print(json.dumps({"metric": "lm-head contraction time per launch inside spec_lm_head_accept, "
+                                "bf16 table 262144 rows",
                       "unit": "us", "library": _lib.LIB_PATH, "times": out}), flush=True)
 
 
@@ -608,12 +615,13 @@ def sweep_k(w, kmax, steps, warmup, device):
     time and tokens per step at every k, the verified tokens per second they give, and the k
     the telemetry picks (highest throughput; where the tokens per step plateau)."""
     from speculative_decoding_decode_amd.telemetry import choose_k, mal_from_positions
-    us, mal, pos = {}, {}, {}
+    us, mal, pos, lm = {}, {}, {}, {}
     for k in range(kmax + 1):
         wk = dataclasses.replace(w, k=k)
         log(f"[bench] sweep: k = {k}")
         r = measure(wk, steps, warmup, device)
         us[k] = r["ms_per_step"] * 1e3
+        lm[k] = r["lm_avg_ms"] * 1e3
         mal[k] = r["stats"].mean_accepted_length
         pos[k] = [round(a, 4) for a in r["stats"].per_position]
         del r
@@ -626,6 +634,7 @@ def sweep_k(w, kmax, steps, warmup, device):
         "unit": "verified tokens/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
         "config": {"workload": w.name, "k": list(range(kmax + 1))},
         "us_per_step": [round(us[k], 2) for k in range(kmax + 1)],
+        "lm_head_us_per_launch": [round(lm[k], 2) for k in range(kmax + 1)],
         "tokens_per_step": [round(derived[k], 4) for k in range(kmax + 1)],   # per sequence
         "tokens_per_step_measured_at_k": [round(mal[k], 4) for k in range(kmax + 1)],
         "verified_tokens_per_s": [round(w.batch * c.tokens_per_second[k], 1) for k in range(kmax + 1)],

@@ -8,16 +8,17 @@
 // V x H table: every table element is read once from HBM and used R times.
 //
 // Design (gfx950).  Two contraction kernels share one softmax finalize; which one runs was
-// set by timing both on MI355X at 1..8 rows:
-//  * R <= 6 rows (batch-1 verification): a bandwidth-bound GEMV.  Each wave owns 64 table rows
-//    and walks the hidden dimension in 128-byte chunks, eight rows per load instruction, with
-//    nontemporal loads (the table is used once per call); every lane accumulates its slot of
-//    eight rows in fp32 with v_dot2_f32_bf16 (fp32 tables: FMAs) and a three-step DPP
-//    reduction inside each 8-lane group gives each row's logit.  About 6.5 TB/s in the step.
+// set by timing both on MI355X at 1..8 rows and two table widths:
+//  * up to 4 rows (2 rows above 4096 wide; batch-1 verification): a bandwidth-bound GEMV.
+//    Each wave owns 64 table rows and walks the hidden dimension in 128-byte chunks, eight rows
+//    per load instruction, with nontemporal loads (the table is used once per call); every
+//    lane accumulates its slot of eight rows in fp32 with v_dot2_f32_bf16 (fp32 tables: FMAs)
+//    and a three-step DPP reduction inside each 8-lane group gives each row's logit.  About
+//    6.5 TB/s in the step.
 //  * every other R: MFMA (v_mfma_f32_16x16x32_bf16; fp32 tables: four v_mfma_f32_16x16x4_f32).
 //    One workgroup = 512 vocab rows against up to 96 hidden rows per pass; chunks of 128 bytes
 //    of every row are loaded as 128-byte contiguous runs per row and transposed into MFMA
-//    fragments through bank-conflict-free LDS tiles.
+//    fragments through bank-conflict-free LDS tiles; p leaves with nontemporal stores.
 //  * Every epilogue turns a 256-row vocab block into per-block softmax statistics (max, sum of
 //    exp, first argmax) and writes exp(logit - block max) into p; lm_head_finalize merges the
 //    statistics of all blocks and rescales p in place (or writes the greedy one-hot rows).
@@ -121,9 +122,13 @@ __device__ __forceinline__ int swz(int row, int slot) { return row * 128 + ((slo
 
 // Epilogue of the MFMA contractions: per 256-row statistics block and hidden row, the block
 // max / first argmax and the sum of exp, written to `so`; exp((z - block max) / T) into p (the
-// finalize rescales it); logits stored when asked for.  acc[vt][n]: lane l holds the logits of
-// vocab rows vw + 16 vt + 4 (l / 16) + e for hidden row r0 + 16 n + l % 16.  smem: at least
-// 3 * kMmaWaves * kMaxNH * 16 words of LDS no longer in use.
+// finalize rescales it); logits stored when asked for.  The p and logit stores are nontemporal
+// and issued as soon as each tile (pair) is done, so they drain while the sums are reduced:
+// every workgroup of a round reaches its epilogue at about the same time, and stores that
+// allocate in the cache took about 15 us longer per call at 40-48 rows on MI355X (p is read
+// once, by the finalize or the accept, after the whole table has streamed past the cache).
+// acc[vt][n]: lane l holds the logits of vocab rows vw + 16 vt + 4 (l / 16) + e for hidden row
+// r0 + 16 n + l % 16.  smem: at least 3 * kMmaWaves * kMaxNH * 16 words of LDS no longer in use.
 template <int NH>
 __device__ __forceinline__ void mfma_epilogue(f32x4_t (&acc)[kMmaVT][NH], unsigned char *smem,
                                               int wave, int lr, int lq, int vb, int vw, int r0,
@@ -133,6 +138,7 @@ __device__ __forceinline__ void mfma_epilogue(f32x4_t (&acc)[kMmaVT][NH], unsign
   // block max / first argmax, then sum of exp, per hidden row.  Hidden row
   // slot c = n * 16 + lr of the wave is row r0 + 16 n + lr; the four 64-row slices
   // of a statistics block (waves g0 + q) are merged in slice order.
+  static_assert(kMmaVT % 2 == 0, "p is stored by pairs of vocab tiles");
   const int g0 = wave & ~3;                     // first wave of this wave's block
   typedef float RowF[kMaxNH * 16];
   typedef int RowI[kMaxNH * 16];
@@ -180,11 +186,10 @@ __device__ __forceinline__ void mfma_epilogue(f32x4_t (&acc)[kMmaVT][NH], unsign
       if (live[n] && logits != nullptr) {
         float *dst = logits + (size_t)r * V + v0;
         if (v0 + 3 < V && (V & 3) == 0) {
-          *reinterpret_cast<float4 *>(dst) =
-              make_float4(acc[vt][n][0], acc[vt][n][1], acc[vt][n][2], acc[vt][n][3]);
+          __builtin_nontemporal_store(acc[vt][n], reinterpret_cast<f32x4_t *>(dst));
         } else {
           for (int e = 0; e < 4; ++e)
-            if (v0 + e < V) dst[e] = acc[vt][n][e];
+            if (v0 + e < V) __builtin_nontemporal_store(acc[vt][n][e], dst + e);
         }
       }
 #pragma unroll
@@ -192,6 +197,35 @@ __device__ __forceinline__ void mfma_epilogue(f32x4_t (&acc)[kMmaVT][NH], unsign
         const float ex = (v0 + e < V) ? exp2f((acc[vt][n][e] - m) * cexp[n]) : 0.f;
         acc[vt][n][e] = ex;
         sacc += ex;
+      }
+      if (vt & 1) {
+        // p of tiles vt - 1 and vt (32 entries, one 128-byte line of each of the 16 rows) in two
+        // stores of whole lines: lanes lr and lr ^ 8 swap one tile (DPP row_ror:8), so that
+        // the first store writes rows 0..7 and the second rows 8..15 of the tile pair.  Stores
+        // of the 64-byte halves, one per tile, reached HBM as 1.4x the bytes written.
+        const bool lo = lr < 8;
+        const f32x4_t a = acc[vt - 1][n], b = acc[vt][n];
+        f32x4_t pa, pb;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          pa[e] = spec::dpp_move<0x128>(a[e]);
+          pb[e] = spec::dpp_move<0x128>(b[e]);
+        }
+        const int wo = (live[n] && cexp[n] != 0.f) ? 1 : 0;
+        const int wp = spec::dpp_move<0x128>(wo);
+        const int col = v0 - 16 + (lo ? 0 : 16);
+        auto put = [&](int row, const f32x4_t &x, bool ok) __attribute__((always_inline)) {
+          if (!ok) return;
+          float *dst = probs + (size_t)row * V + col;
+          if (col + 3 < V && (V & 3) == 0) {
+            __builtin_nontemporal_store(x, reinterpret_cast<f32x4_t *>(dst));
+          } else {
+            for (int e = 0; e < 4; ++e)
+              if (col + e < V) __builtin_nontemporal_store(x[e], dst + e);
+          }
+        };
+        put(lo ? r : r - 8, lo ? a : pb, lo ? wo != 0 : wp != 0);
+        put(lo ? r + 8 : r, lo ? pa : b, lo ? wp != 0 : wo != 0);
       }
     }
 #pragma unroll
@@ -216,23 +250,6 @@ __device__ __forceinline__ void mfma_epilogue(f32x4_t (&acc)[kMmaVT][NH], unsign
                         red_s[g0 + 3][c];
       so.stats[(size_t)sb * R + r] = make_float2(m, sum);
       so.amax[(size_t)sb * R + r] = a;
-    }
-  }
-#pragma unroll
-  for (int n = 0; n < NH; ++n) {
-    const int r = r0 + n * 16 + lr;
-    if (!live[n] || cexp[n] == 0.f) continue;
-#pragma unroll
-    for (int vt = 0; vt < kMmaVT; ++vt) {
-      const int v0 = vw + vt * 16 + lq * 4;
-      float *dst = probs + (size_t)r * V + v0;
-      if (v0 + 3 < V && (V & 3) == 0) {
-        *reinterpret_cast<float4 *>(dst) =
-            make_float4(acc[vt][n][0], acc[vt][n][1], acc[vt][n][2], acc[vt][n][3]);
-      } else {
-        for (int e = 0; e < 4; ++e)
-          if (v0 + e < V) dst[e] = acc[vt][n][e];
-      }
     }
   }
 }
@@ -345,15 +362,21 @@ __global__ __launch_bounds__(kMmaThreads, 1) void lm_head_mfma(
 // ------------------------------------------------------------------------- small-R GEMV path
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
-// Rows up to which the GEMV serves a call; above it the MFMA contraction streams faster.  Set
-// from kernel times of both measured on MI355X at 1..8 rows over 2560- and 5376-wide tables;
-// a build may override it (SPEC_GEMV_MAX_ROWS) to time one kernel against the other.
-#ifndef SPEC_GEMV_MAX_ROWS
-#define SPEC_GEMV_MAX_ROWS 6
-#endif
-constexpr int kGemvMaxR = SPEC_GEMV_MAX_ROWS;
+// Rows up to which the GEMV serves a call of hidden width H; above it the MFMA contraction
+// streams faster.  The GEMV's time grows with every row (more dot products per table byte),
+// the MFMA contraction's stays flat up to 16 rows, and the rows where they cross fall with the
+// width: timed on MI355X inside the verify step's call at 1..8 rows, the GEMV wins up to four
+// rows of a 2560-wide table and the MFMA contraction from five, while at 5376 wide the two tie
+// at two rows and the MFMA contraction wins from three.  A build may fix the limit for every
+// width (SPEC_GEMV_MAX_ROWS) to time one kernel against the other.
 constexpr int kGemvMaxInstR = 8;     // GEMV instantiations: 1..8 rows
-static_assert(kGemvMaxR >= 0 && kGemvMaxR <= kGemvMaxInstR, "GEMV rows within its instantiations");
+#ifdef SPEC_GEMV_MAX_ROWS
+static_assert(SPEC_GEMV_MAX_ROWS >= 0 && SPEC_GEMV_MAX_ROWS <= kGemvMaxInstR,
+              "GEMV rows within its instantiations");
+constexpr int gemv_max_rows(int) { return SPEC_GEMV_MAX_ROWS; }
+#else
+constexpr int gemv_max_rows(int H) { return H <= 4096 ? 4 : 2; }
+#endif
 constexpr int kRowsPerWave = 64;     // one table row per lane in the epilogue
 
 template <typename T> struct Dot;
@@ -429,7 +452,7 @@ __device__ __forceinline__ void gemv_epilogue(const float (&keep)[RT], int v0, i
     if (vok && !greedy[r]) probs[(size_t)r * V + v] = ex[r];
 }
 
-// Grid: ceil(V / 256).  The GEMV for R <= kGemvMaxR rows and any H.  A wave owns 64 table rows and
+// Grid: ceil(V / 256).  The GEMV for R <= gemv_max_rows(H) rows.  A wave owns 64 table rows and
 // walks the hidden dimension in chunks of 128 bytes: one load instruction covers 8 rows x 128
 // contiguous bytes (lane 8 g + s reads 16-byte slot s of row t + 8 g of the wave's 64, for
 // load t = 0..7), so a chunk of the wave's 64 rows is eight nontemporal loads and the same
@@ -715,7 +738,7 @@ int lm_head_contract(const void *hidden, const void *weight, const float *temper
   if (ev0 != nullptr && hipEventRecord(ev0, st) != hipSuccess)
     return fail(SPEC_EHIP, "spec_lm_head: hipEventRecord(start) failed");
   int rc;
-  if (R <= kGemvMaxR)
+  if (R <= gemv_max_rows(H))
     rc = dtype == SPEC_BF16
              ? launch_gemv_r<uint16_t>(R, hidden, weight, temperature, logits, probs, so, H, V, st)
              : launch_gemv_r<float>(R, hidden, weight, temperature, logits, probs, so, H, V, st);

@@ -84,7 +84,7 @@ def test_greedy_ties_take_first_index(R, dtype):
     assert pc[:, 7].tolist() == [1.0] * R and float(pc.sum()) == float(R)
 
 
-@pytest.mark.parametrize("R", [2, 3, 5, 20])  # the GEMV (two, three, five rows) and the MFMA path
+@pytest.mark.parametrize("R", [2, 3, 4, 5, 20])  # the GEMV (two to four rows), the MFMA path
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 @pytest.mark.parametrize("ties", [[45, 13, 2, 3, 130], [50, 33, 17], [1, 0], [255, 64, 128, 192],
                                   [63, 62, 61, 48, 47, 31, 16, 15]])
@@ -101,6 +101,18 @@ def test_greedy_ties_within_a_wave(R, dtype, ties):
     pc = p.cpu()
     want = min(ties)
     assert pc[:, want].tolist() == [1.0] * R and float(pc.sum()) == float(R)
+
+
+@pytest.mark.parametrize("greedy_rows", [[20, 49], [], list(range(50)), [0]])
+def test_greedy_rows_in_some_row_tiles(greedy_rows):
+    # greedy and tempered rows mixed over the 16-row tiles of the MFMA path: tiles without a
+    # greedy row, tiles with one, every row greedy, none greedy
+    torch.manual_seed(11)
+    R, H, V = 50, 72, 1300
+    x = torch.randn(R, H).to(torch.bfloat16)
+    W = (torch.randn(V, H) / math.sqrt(H)).to(torch.bfloat16)
+    temps = [0.0 if r in greedy_rows else (0.7, 1.0, 2.0)[r % 3] for r in range(R)]
+    run_and_compare(x, W, temps, "bf16", label="greedy tiles")
 
 
 @pytest.mark.parametrize("name", ["b1_k2_sliding256_8k", "b1_k4_global512_32k"])
