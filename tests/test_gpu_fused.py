@@ -114,6 +114,30 @@ def test_ragged_shapes_equal_two_calls(B, k, H, V, dtype, temps):
     assert np.array_equal(n1, n2) and np.array_equal(t1, t2)
 
 
+def test_max_rows_per_call():
+    # B (k + 1) = 65535 rows, the most one call takes, against the two calls and the oracle chain
+    d = dev()
+    B, k, H, V = 13107, 4, 16, 64
+    K1 = k + 1
+    g = torch.Generator().manual_seed(13107)
+    x = torch.randn(B * K1, H, generator=g).to(torch.bfloat16).to(d)
+    W = (torch.randn(V, H, generator=g) / math.sqrt(H)).to(torch.bfloat16).to(d)
+    rt = np.array([(0.0, 0.8, 1.0)[(r // K1) % 3] for r in range(B * K1)], np.float32)
+    _, p = sv.lm_head(x, W, torch.from_numpy(rt).to(d))
+    rng = np.random.default_rng(7)
+    recipe_q = rng.dirichlet(np.ones(V), size=(B, k)).astype(np.float32)
+    q, draft = drafter(p.view(B, K1, V).cpu().numpy(), k, recipe_q, seed=11)
+    u = rng.random((B, K1), dtype=np.float32)
+    say(f"[fused] max rows: B={B} k={k} V={V}")
+    (n1, t1), (n2, t2), _ = run_both(x, W, rt, draft, q, u)
+    assert np.array_equal(n1, n2) and np.array_equal(t1, t2)
+    z_ref = oracle.logits(x.cpu(), W.cpu())
+    p_ref32 = oracle.probabilities(z_ref, rt).astype(np.float32).reshape(B, K1, V)
+    n_r, t_r = oracle.verify_accept(draft, q, p_ref32, u)
+    why = explain_difference(draft, q, p_ref32, u, n1, t1, n_r, t_r)
+    say(f"    against the oracle chain: {why or 'equal'}")
+
+
 def test_workspace_reused_across_sizes():
     # one workspace, calls of decreasing and increasing size: the completion counters at its
     # start must be back at zero after every call, whatever the layout of the call before

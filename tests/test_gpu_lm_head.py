@@ -115,6 +115,17 @@ def test_greedy_rows_in_some_row_tiles(greedy_rows):
     run_and_compare(x, W, temps, "bf16", label="greedy tiles")
 
 
+def test_max_rows_per_call():
+    # 65535 rows, the most one call takes: 683 passes of the MFMA contraction and the wide
+    # finalize chunks (more than 2048 finalize workgroups)
+    torch.manual_seed(65535)
+    R, H, V = 65535, 16, 300
+    x = torch.randn(R, H).to(torch.bfloat16)
+    W = (torch.randn(V, H) / math.sqrt(H)).to(torch.bfloat16)
+    temps = [0.0 if r % 7 == 0 else (0.7, 1.0, 2.0)[r % 3] for r in range(R)]
+    run_and_compare(x, W, temps, "bf16", label="max rows")
+
+
 @pytest.mark.parametrize("name", ["b1_k2_sliding256_8k", "b1_k4_global512_32k"])
 def test_full_size_batch1(name):
     w = WORKLOADS[name]
