@@ -61,7 +61,11 @@ def test_tiny_fp32_workload():
                                           # super-chunk (5-6 hidden tiles) with a tail
                                           (5, 8, 300, "bf16"), (20, 24, 1000, "bf16"),
                                           (70, 328, 2100, "bf16"), (96, 5376, 1100, "bf16"),
-                                          (200, 200, 600, "bf16")])
+                                          (200, 200, 600, "bf16"),
+                                          # either side of the width where the GEMV's row
+                                          # limit drops from four to two
+                                          (4, 4096, 1000, "bf16"), (3, 4104, 1000, "bf16"),
+                                          (2, 4104, 700, "bf16")])
 def test_ragged_shapes(R, H, V, dtype):
     torch.manual_seed(R * 7 + V)
     td = torch.float32 if dtype == "f32" else torch.bfloat16
