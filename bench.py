@@ -64,8 +64,8 @@ METRIC = "verified tokens/sec and verify-step HBM GB/s (% peak), batch 1, k=2, 8
 PROFILED_TRAFFIC = {
     "workload": DEFAULT_WORKLOAD,
     "source": "speculative_decoding_decode_amd/csrc/lm_head.hip",
-    "sha256": "8ddec85a4911862f273c2300fbc566c904bd8902109870ea6caa46b93a714ea9",
-    "bytes_per_launch": 1346056602,
+    "sha256": "c733217508c1a636f5efd672678a778483ea536fd8647f236af402df2f31ed55",
+    "bytes_per_launch": 1346234524,
 }
 
 

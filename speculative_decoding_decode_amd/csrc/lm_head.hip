@@ -517,10 +517,22 @@ __global__ __launch_bounds__(kThreads, RT <= 2 ? 4 : RT == 3 ? 3 : 2) void lm_he
   };
   // The scheduling barriers keep each phase where it is written, so the wait before a compute
   // is for that chunk only and the other chunk's loads stay in flight.
+  // Wave priority falls as the wave gets through its rows (3 for the first eighth of the
+  // chunks, then 2, 1 from three eighths, 0 from five eighths).  The waves of a CU's three
+  // workgroups otherwise share its issue slots oldest first: on MI355X the first-dispatched
+  // workgroup of a CU finished its rows in 68 us, the second in 115, the third in 157, and the
+  // workgroup started in the first one's place at ~70 us ran on with few neighbours to the end
+  // of the call.  Letting the waves that are behind go first evens their progress out and
+  // took the 3-row call at 2560 wide from 200.8 to 198.9 us.
   Chunk ca, cb;
   fetch(ca, 0);
   fetch(cb, 1);
+  __builtin_amdgcn_s_setprio(3);
+  const int q1 = nch / 8, q2 = 3 * nch / 8, q3 = 5 * nch / 8;
   for (int c = 0; c < nch; c += 2) {
+    if (c == (q1 & ~1)) __builtin_amdgcn_s_setprio(2);
+    if (c == (q2 & ~1)) __builtin_amdgcn_s_setprio(1);
+    if (c == (q3 & ~1)) __builtin_amdgcn_s_setprio(0);
     __builtin_amdgcn_sched_barrier(0);
     compute(ca, c);
     __builtin_amdgcn_sched_barrier(0);
