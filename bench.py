@@ -64,8 +64,8 @@ METRIC = "verified tokens/sec and verify-step HBM GB/s (% peak), batch 1, k=2, 8
 PROFILED_TRAFFIC = {
     "workload": DEFAULT_WORKLOAD,
     "source": "speculative_decoding_decode_amd/csrc/lm_head.hip",
-    "sha256": "c733217508c1a636f5efd672678a778483ea536fd8647f236af402df2f31ed55",
-    "bytes_per_launch": 1346234524,
+    "sha256": "213864716328f4a1315a9553be8119d15dffea5b994e61145c0e2a2b8c805f22",
+    "bytes_per_launch": 1346232972,
 }
 
 

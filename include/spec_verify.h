@@ -122,8 +122,7 @@ int spec_verify_attn(const void *q, const void *k_pool, const void *v_pool,
  *   logits       [R, V] fp32, or NULL when the raw logits are not wanted
  *   probs        [R, V] fp32  p, rows summing to 1
  *   H % 8 == 0 (16-byte rows for bf16); R <= 65535.  Accumulation is fp32 (dot products in
- *   the GEMV, which serves up to four rows of a table at most 4096 wide and up to two rows of a
- *   wider one; MFMA otherwise).
+ *   the GEMV, which serves up to five rows; MFMA otherwise).
  *   Workspace: per 256-row vocabulary block and row the softmax statistics.
  * ---------------------------------------------------------------------------------------- */
 size_t spec_lm_head_workspace(int R, int H, int V);

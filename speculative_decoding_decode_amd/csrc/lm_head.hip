@@ -9,7 +9,7 @@
 //
 // Design (gfx950).  Two contraction kernels share one softmax finalize; which one runs was
 // set by timing both on MI355X at 1..8 rows and two table widths:
-//  * up to 4 rows (2 rows above 4096 wide; batch-1 verification): a bandwidth-bound GEMV.
+//  * up to 5 rows (batch-1 verification): a bandwidth-bound GEMV.
 //    Each wave owns 64 table rows and walks the hidden dimension in 128-byte chunks, eight rows
 //    per load instruction, with nontemporal loads (the table is used once per call); every
 //    lane accumulates its slot of eight rows in fp32 with v_dot2_f32_bf16 (fp32 tables: FMAs)
@@ -363,19 +363,18 @@ __global__ __launch_bounds__(kMmaThreads, 1) void lm_head_mfma(
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 // Rows up to which the GEMV serves a call of hidden width H; above it the MFMA contraction
-// streams faster.  The GEMV's time grows with every row (more dot products per table byte),
-// the MFMA contraction's stays flat up to 16 rows, and the rows where they cross fall with the
-// width: timed on MI355X inside the verify step's call at 1..8 rows, the GEMV wins up to four
-// rows of a 2560-wide table and the MFMA contraction from five, while at 5376 wide the two tie
-// at two rows and the MFMA contraction wins from three.  A build may fix the limit for every
-// width (SPEC_GEMV_MAX_ROWS) to time one kernel against the other.
+// streams faster.  The GEMV's time grows with every row (one more dot product per table
+// element), the MFMA contraction's stays flat up to 16 rows.  Timed on MI355X inside the
+// verify step's call at 1..8 rows and 2560 / 5376 wide, the GEMV is faster up to five rows at
+// both widths (at 5376 wide the two tie at five and six rows) and the MFMA contraction from
+// six.  A build may fix the limit (SPEC_GEMV_MAX_ROWS) to time one kernel against the other.
 constexpr int kGemvMaxInstR = 8;     // GEMV instantiations: 1..8 rows
 #ifdef SPEC_GEMV_MAX_ROWS
 static_assert(SPEC_GEMV_MAX_ROWS >= 0 && SPEC_GEMV_MAX_ROWS <= kGemvMaxInstR,
               "GEMV rows within its instantiations");
 constexpr int gemv_max_rows(int) { return SPEC_GEMV_MAX_ROWS; }
 #else
-constexpr int gemv_max_rows(int H) { return H <= 4096 ? 4 : 2; }
+constexpr int gemv_max_rows(int) { return 5; }
 #endif
 constexpr int kRowsPerWave = 64;     // one table row per lane in the epilogue
 
