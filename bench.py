@@ -64,8 +64,8 @@ METRIC = "verified tokens/sec and verify-step HBM GB/s (% peak), batch 1, k=2, 8
 PROFILED_TRAFFIC = {
     "workload": DEFAULT_WORKLOAD,
     "source": "speculative_decoding_decode_amd/csrc/lm_head.hip",
-    "sha256": "213864716328f4a1315a9553be8119d15dffea5b994e61145c0e2a2b8c805f22",
-    "bytes_per_launch": 1346232972,
+    "sha256": "2b016cf275d87557a856c8370a74d2af7fcf57ca9069e1838d2a93c7cfaee4c4",
+    "bytes_per_launch": 1346231983,
 }
 
 

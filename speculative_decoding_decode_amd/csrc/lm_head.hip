@@ -9,12 +9,12 @@
 //
 // Design (gfx950).  Two contraction kernels share one softmax finalize; which one runs was
 // set by timing both on MI355X at 1..8 rows and two table widths:
-//  * up to 5 rows (batch-1 verification): a bandwidth-bound GEMV.
-//    Each wave owns 64 table rows and walks the hidden dimension in 128-byte chunks, eight rows
-//    per load instruction, with nontemporal loads (the table is used once per call); every
-//    lane accumulates its slot of eight rows in fp32 with v_dot2_f32_bf16 (fp32 tables: FMAs)
-//    and a three-step DPP reduction inside each 8-lane group gives each row's logit.  About
-//    6.5 TB/s in the step.
+//  * up to 5 rows (batch-1 verification): a bandwidth-bound GEMV.  Each wave owns 64 table
+//    rows and walks the hidden dimension in 128-byte chunks, eight rows per load instruction,
+//    with nontemporal loads (the table is used once per call); every lane accumulates its slot
+//    of eight rows in fp32 with v_dot2_f32_bf16 (fp32 tables: FMAs) and a three-step DPP
+//    reduction inside each 8-lane group gives each row's logit; wave priorities that fall with
+//    each wave's progress keep a CU's workgroups level.  About 6.7 TB/s in the step.
 //  * every other R: MFMA (v_mfma_f32_16x16x32_bf16; fp32 tables: four v_mfma_f32_16x16x4_f32).
 //    One workgroup = 512 vocab rows against up to 96 hidden rows per pass; chunks of 128 bytes
 //    of every row are loaded as 128-byte contiguous runs per row and transposed into MFMA
