@@ -2,6 +2,8 @@
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--workload NAME]
     python bench.py --sweep-k KMAX [--workload NAME] [--steps K]
+    python bench.py --lm-head-rows      # the contraction at 1..8 rows, 2560 / 5376 wide
+    python bench.py --calibrate-copy    # one plain copy of known size (HBM counter scaling)
 
 Default workload (the headline line): batch 1, k = 2 drafts (3 verified positions), one
 sliding-window attention layer (8 query / 2 KV heads, head dim 256, window 1024) over a paged
