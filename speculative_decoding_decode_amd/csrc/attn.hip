@@ -11,9 +11,9 @@
 // Design (gfx950): the work is the flat list of (sequence, KV head, row chunk, visible page)
 // items, and the grid is about one workgroup per resident slot of the GPU ("stream-K"): every
 // workgroup takes an equal contiguous share of the list, whatever the lengths of the sequences
-// in a ragged batch, so all slots stay busy until the end.  The share is computed on the
-// device from the context lengths (each workgroup and each merge wave derives the same
-// numbers).  Within a share a workgroup walks the pages of each (sequence, KV head, row chunk)
+// in a ragged batch, so every slot has the same number of pages to read.  The share is
+// computed on the device from the context lengths (each workgroup and each merge wave derives
+// the same numbers).  Within a share a workgroup walks the pages of each (sequence, KV head, row chunk)
 // unit it touches: each 16-token page of K and of V is one contiguous 16*D block per head,
 // read with nontemporal 16-byte loads (each page is read once per call) two pages ahead.  At
 // head dims 64 and 128, in fp32, and at head dim 256 with two row tiles, pages are staged
