@@ -28,6 +28,7 @@ def compare(draft, q, p, u, label):
     ("b8_ragged_k5_hybrid", 8, None),
     ("b32_k2_mixed_16k", 32, None),
     ("b8_ragged_k5_hybrid", 40, 1000),
+    ("b1_k2_sliding256_8k", 96, None),    # 16 chunks of 16384 per row: the widest chunks
 ])
 def test_workload_recipes(name, batch, vocab):
     w = WORKLOADS[name]

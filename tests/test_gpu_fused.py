@@ -93,6 +93,8 @@ def test_workloads_equal_two_calls(name, philox):
     (2, 9, 2568, 777, "bf16", (0.0, 1.0)),
     (5, 3, 72, 70001, "f32", (0.7,)),           # many blocks, a ragged last group
     (1, 1, 8, 1, "bf16", (1.0,)),               # one vocabulary entry
+    (48, 2, 64, 262144, "bf16", (1.0, 0.0, 0.7)),   # 32 chunks of 8192 per row
+    (96, 2, 64, 262144, "bf16", (1.0,)),        # 16 chunks of 16384 per row, 288 rows
 ])
 def test_ragged_shapes_equal_two_calls(B, k, H, V, dtype, temps):
     d = dev()
