@@ -163,8 +163,9 @@ int spec_profile_lm_head(void *start_event, void *stop_event);
  * token itself, leaving the output distribution unchanged (llm-wiki "Gemma 4 MTP ...",
  * section "투기적 디코딩(Speculative Decoding)의 기본 구조"; butteryoon guide, section 4,
  * accept/reject step); when the whole draft is accepted the same forward yields one extra
- * token (news.hada.io 29214, section "MTP가 동작하는 방식"; damoang, section "추측적 해독은
- * 어떻게 작동하는가", which cites Leviathan et al. for the rule).
+ * token (GeekNews "Gemma 4 가속하기 : 다중 토큰 예측 drafter로 더 빠른 추론", section "MTP가
+ * 동작하는 방식"; damoang's text of the MTP announcement, section "추측적 해독은 어떻게
+ * 작동하는가", which cites Leviathan et al. for the rule).
  *
  * For each sequence b and i < k: draft i is accepted iff u[b][i] * q[b][i][d] < p[b][i][d]
  * with d = draft[b][i], evaluated exactly (fp64 product of fp32 values); acceptance stops at
@@ -228,8 +229,8 @@ int spec_accept_philox(const int32_t *draft, const float *q, const float *p, uin
  * Passages: the verify forward compares every drafted position with the target's own
  * distribution and accepts or rejects in the same step (butteryoon guide, section 4 "실행
  * 흐름"); the serving guide runs sampling on a dedicated GPU backend (section 7 settings
- * table); the bonus token comes out of the same forward (news.hada.io 29214, section "MTP가
- * 동작하는 방식").
+ * table); the bonus token comes out of the same forward (GeekNews "Gemma 4 가속하기 : 다중
+ * 토큰 예측 drafter로 더 빠른 추론", section "MTP가 동작하는 방식").
  *
  *   hidden, weight, temperature   as spec_lm_head (R = B * (k + 1) rows, b-major)
  *   draft, q                      as spec_accept

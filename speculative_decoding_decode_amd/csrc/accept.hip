@@ -4,8 +4,9 @@
 // token at that position itself, keeping the output distribution that of the target alone
 // (llm-wiki "Gemma 4 MTP: 드래프터가 초안을 쓰고 타깃이 검증하는 추론 가속 구조", section
 // "투기적 디코딩의 기본 구조"; butteryoon "Gemma 4 MTP 서빙 가이드 해설", section 4 accept/reject
-// step); when every draft is accepted the same forward also yields one extra token (news.hada.io
-// 29214, section "MTP가 동작하는 방식").  The rule is Leviathan et al.'s: accept draft i iff
+// step); when every draft is accepted the same forward also yields one extra token (GeekNews
+// "Gemma 4 가속하기 : 다중 토큰 예측 drafter로 더 빠른 추론", section "MTP가 동작하는 방식").
+// The rule is Leviathan et al.'s: accept draft i iff
 // u_i < min(1, p_i(d_i) / q_i(d_i)); on the first rejection draw from norm(max(0, p - q)); after
 // k acceptances draw the bonus token from p.
 //
