@@ -409,8 +409,7 @@ def measure(w, steps, warmup, device, two_calls=False):
     attn_out = [torch.empty((B, K1, L.hq, L.head_dim), dtype=torch.float32, device=device)
                 for L in w.layers]
     probs = torch.empty((R, V), dtype=torch.float32, device=device)
-    # workspaces zero-filled once (the library's completion counters start at zero and every
-    # call leaves them there)
+    # workspaces allocated once, outside the timed region (the calls need no contents in them)
     ws_attn = torch.zeros(max(sv.verify_attn_workspace_bytes(B, K1, L.hq, L.hkv, L.head_dim,
                                                              inp["max_pages"], L.window)
                               for L in w.layers), dtype=torch.uint8, device=device)
