@@ -5,6 +5,7 @@ import pytest
 import torch
 
 import oracle
+import speculative_decoding_decode_amd as sv
 from workloads import WORKLOADS, gen
 from cases import accept_inputs, gpu_accept, say, dev
 
@@ -34,6 +35,22 @@ def test_workload_recipes(name, batch, vocab):
     w = WORKLOADS[name]
     draft, q, p, u = accept_inputs(w, step=1, batch=batch, vocab=vocab)
     compare(draft, q, p, u, name)
+
+
+def test_workspace_contents_unused():
+    # a workspace full of 0xFF bytes (every chunk sum and count at its maximum) gives the same
+    # n and tokens as a zeroed one
+    w = WORKLOADS["b32_k2_mixed_16k"]
+    draft, q, p, u = accept_inputs(w, step=5, batch=12, vocab=70001)
+    d = dev()
+    args = [torch.from_numpy(a).to(d) for a in (draft, q, p, u)]
+    nbytes = sv.accept_workspace_bytes(12, w.k, 70001)
+    n0, t0 = sv.accept(*args, workspace=torch.zeros(nbytes, dtype=torch.uint8, device=d))
+    n1, t1 = sv.accept(*args, workspace=torch.full((nbytes,), 0xFF, dtype=torch.uint8, device=d))
+    torch.cuda.synchronize()
+    assert torch.equal(n0, n1) and torch.equal(t0, t1)
+    n_ref, tok_ref = oracle.verify_accept(draft, q, p, u)
+    assert np.array_equal(n1.cpu().numpy(), n_ref) and np.array_equal(t1.cpu().numpy(), tok_ref)
 
 
 def test_greedy_tiny():

@@ -110,6 +110,23 @@ def test_context_clamped_to_table():
     assert err <= REG_TOL["bf16"]
 
 
+@pytest.mark.parametrize("d,window,k", [(256, 1024, 2), (512, 0, 4), (256, 37, 5)])
+def test_workspace_contents_unused(d, window, k):
+    # a workspace full of NaN bit patterns gives the same bits as a zeroed one: every partial
+    # the merge reads is written by the same call
+    w = small_workload("bf16", 8, 2, d, window, k, batch=4)
+    ctx = np.array([k + 1, 1500, 700, 2100], dtype=np.int32)
+    table, P = gen.page_tables(w, ctx, max_pages=140)
+    inp = attn_inputs(w, 0, dev(), ctx=ctx, table=table, num_pages=P)
+    nbytes = sv.verify_attn_workspace_bytes(4, k + 1, 8, 2, d, 140, window)
+    zero = torch.zeros(nbytes, dtype=torch.uint8, device=dev())
+    junk = torch.full((nbytes,), 0xFF, dtype=torch.uint8, device=dev())
+    a = sv.verify_attn(**inp, workspace=zero).clone()
+    b = sv.verify_attn(**inp, workspace=junk)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b) and not torch.isnan(b).any()
+
+
 def test_deterministic_repeat():
     w = WORKLOADS["b1_k2_sliding256_8k"]
     inp = attn_inputs(w, 0, dev(), step=4)
