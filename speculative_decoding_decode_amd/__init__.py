@@ -66,11 +66,16 @@ def ctypes_void(x):
     return ctypes.c_void_p(int(x)) if x else None
 
 
+def _nbytes(t) -> int:
+    return t.numel() * t.element_size()
+
+
 def _workspace(kind: str, device, nbytes: int, given=None):
     torch = _torch()
     if given is not None:
-        if given.numel() * given.element_size() < nbytes:
-            raise ValueError(f"workspace of {nbytes} bytes needed")
+        _need(given, "workspace", device=device)
+        if _nbytes(given) < nbytes:
+            raise ValueError(f"workspace of {nbytes} bytes needed, got {_nbytes(given)}")
         return given
     key = (kind, str(device))
     ws = _workspaces.get(key)
@@ -114,7 +119,7 @@ def verify_attn(q, k_pool, v_pool, page_table, ctx_lens, window: int = 0, scale=
     rc = _lib.load().spec_verify_attn(
         q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), page_table.data_ptr(),
         ctx_lens.data_ptr(), out.data_ptr(), B, K1, Hq, Hkv, D, ps, P, max_pages, int(window),
-        float(scale), _dtype_code(q), ws.data_ptr(), ws.numel(), _stream_ptr(dev, stream))
+        float(scale), _dtype_code(q), ws.data_ptr(), _nbytes(ws), _stream_ptr(dev, stream))
     _lib.check("spec_verify_attn", rc)
     return out
 
@@ -152,7 +157,7 @@ def lm_head(hidden, weight, temperature, probs=None, logits=None, want_logits: b
     rc = _lib.load().spec_lm_head(
         hidden.data_ptr(), weight.data_ptr(), temperature.data_ptr(),
         logits.data_ptr() if logits is not None else None, probs.data_ptr(), R, H, V,
-        _dtype_code(hidden), ws.data_ptr(), ws.numel(), _stream_ptr(dev, stream))
+        _dtype_code(hidden), ws.data_ptr(), _nbytes(ws), _stream_ptr(dev, stream))
     _lib.check("spec_lm_head", rc)
     return logits, probs
 
@@ -217,7 +222,7 @@ def accept(draft, q, p, uniforms, n_accepted=None, tokens=None, workspace=None, 
     rc = _lib.load().spec_accept(
         draft.data_ptr() if k > 0 else None, q.data_ptr() if k > 0 else None, p.data_ptr(),
         uniforms.data_ptr(), n_accepted.data_ptr(), tokens.data_ptr(), B, k, V,
-        ws.data_ptr(), ws.numel(), _stream_ptr(dev, stream))
+        ws.data_ptr(), _nbytes(ws), _stream_ptr(dev, stream))
     _lib.check("spec_accept", rc)
     return n_accepted, tokens
 
@@ -249,7 +254,7 @@ def accept_philox(draft, q, p, seed: int, offset: int, return_uniforms: bool = F
     rc = _lib.load().spec_accept_philox(
         draft.data_ptr() if k > 0 else None, q.data_ptr() if k > 0 else None, p.data_ptr(),
         int(seed), int(offset), u.data_ptr() if u is not None else None, n_accepted.data_ptr(),
-        tokens.data_ptr(), B, k, V, ws.data_ptr(), ws.numel(), _stream_ptr(dev, stream))
+        tokens.data_ptr(), B, k, V, ws.data_ptr(), _nbytes(ws), _stream_ptr(dev, stream))
     _lib.check("spec_accept_philox", rc)
     return n_accepted, tokens, u
 
@@ -303,7 +308,7 @@ def lm_head_accept(hidden, weight, temperature, draft, q, uniforms=None, seed: i
         draft.data_ptr() if k > 0 else None, q.data_ptr() if k > 0 else None,
         uniforms.data_ptr() if uniforms is not None else None, int(seed), int(offset),
         u.data_ptr() if u is not None else None, n_accepted.data_ptr(), tokens.data_ptr(),
-        B, k, H, V, _dtype_code(hidden), ws.data_ptr(), ws.numel(), _stream_ptr(dev, stream))
+        B, k, H, V, _dtype_code(hidden), ws.data_ptr(), _nbytes(ws), _stream_ptr(dev, stream))
     _lib.check("spec_lm_head_accept", rc)
     return n_accepted, tokens, u
 
