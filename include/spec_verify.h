@@ -26,8 +26,10 @@
  *     the last error (spec_last_error) and the one-shot profiling bracket armed by
  *     spec_profile_lm_head; every call is otherwise independent of earlier calls and may be
  *     made from any thread.
- *   - `stream` is a hipStream_t (NULL: the null stream).  Calls only enqueue work on it and
- *     return; results are valid once the stream has reached that point.
+ *   - Calls run on the calling thread's current HIP device: `stream` (a hipStream_t, NULL
+ *     for the null stream) and every pointer must belong to it, and spec_verify_attn_workspace
+ *     sizes for its compute units.  Calls only enqueue work on the stream and return; results
+ *     are valid once the stream has reached that point.
  *   - Return value: SPEC_OK (0) or a negative spec_status.  Host-checkable argument errors are
  *     reported before anything is enqueued; spec_last_error() then describes the failure (a
  *     thread-local string, valid until the next call on the same thread).

@@ -66,6 +66,15 @@ def ctypes_void(x):
     return ctypes.c_void_p(int(x)) if x else None
 
 
+def _run(device, name: str, *args) -> None:
+    """Call `name` of the C ABI with `device` current (the library launches on the current
+    device, whose stream `args` carries) and raise on a negative status."""
+    torch = _torch()
+    with torch.cuda.device(device):
+        rc = getattr(_lib.load(), name)(*args)
+    _lib.check(name, rc)
+
+
 def _nbytes(t) -> int:
     return t.numel() * t.element_size()
 
@@ -114,13 +123,13 @@ def verify_attn(q, k_pool, v_pool, page_table, ctx_lens, window: int = 0, scale=
     if out is None:
         out = torch.empty((B, K1, Hq, D), dtype=torch.float32, device=dev)
     _need(out, "out", torch.float32, dev)
-    nbytes = verify_attn_workspace_bytes(B, K1, Hq, Hkv, D, max_pages, window, ps)
+    with torch.cuda.device(dev):   # the split depends on the device's compute units
+        nbytes = verify_attn_workspace_bytes(B, K1, Hq, Hkv, D, max_pages, window, ps)
     ws = _workspace("attn", dev, nbytes, workspace)
-    rc = _lib.load().spec_verify_attn(
+    _run(dev, "spec_verify_attn",
         q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), page_table.data_ptr(),
         ctx_lens.data_ptr(), out.data_ptr(), B, K1, Hq, Hkv, D, ps, P, max_pages, int(window),
         float(scale), _dtype_code(q), ws.data_ptr(), _nbytes(ws), _stream_ptr(dev, stream))
-    _lib.check("spec_verify_attn", rc)
     return out
 
 
@@ -154,11 +163,10 @@ def lm_head(hidden, weight, temperature, probs=None, logits=None, want_logits: b
     if logits is not None:
         _need(logits, "logits", torch.float32, dev)
     ws = _workspace("lm_head", dev, lm_head_workspace_bytes(R, H, V), workspace)
-    rc = _lib.load().spec_lm_head(
+    _run(dev, "spec_lm_head",
         hidden.data_ptr(), weight.data_ptr(), temperature.data_ptr(),
         logits.data_ptr() if logits is not None else None, probs.data_ptr(), R, H, V,
         _dtype_code(hidden), ws.data_ptr(), _nbytes(ws), _stream_ptr(dev, stream))
-    _lib.check("spec_lm_head", rc)
     return logits, probs
 
 
@@ -182,11 +190,10 @@ def lm_head_noalloc(hidden, weight, temperature, probs=None, logits=None,
         logits = torch.empty((R, V), dtype=torch.float32, device=dev)
     if logits is not None:
         _need(logits, "logits", torch.float32, dev)
-    rc = _lib.load().spec_lm_head_noalloc(
+    _run(dev, "spec_lm_head_noalloc",
         hidden.data_ptr(), weight.data_ptr(), temperature.data_ptr(),
         logits.data_ptr() if logits is not None else None, probs.data_ptr(), R, H, V,
         _dtype_code(hidden), _stream_ptr(dev, stream))
-    _lib.check("spec_lm_head_noalloc", rc)
     return logits, probs
 
 
@@ -219,11 +226,10 @@ def accept(draft, q, p, uniforms, n_accepted=None, tokens=None, workspace=None, 
     _need(n_accepted, "n_accepted", torch.int32, dev)
     _need(tokens, "tokens", torch.int32, dev)
     ws = _workspace("accept", dev, accept_workspace_bytes(B, k, V), workspace)
-    rc = _lib.load().spec_accept(
+    _run(dev, "spec_accept",
         draft.data_ptr() if k > 0 else None, q.data_ptr() if k > 0 else None, p.data_ptr(),
         uniforms.data_ptr(), n_accepted.data_ptr(), tokens.data_ptr(), B, k, V,
         ws.data_ptr(), _nbytes(ws), _stream_ptr(dev, stream))
-    _lib.check("spec_accept", rc)
     return n_accepted, tokens
 
 
@@ -251,11 +257,10 @@ def accept_philox(draft, q, p, seed: int, offset: int, return_uniforms: bool = F
     _need(tokens, "tokens", torch.int32, dev)
     u = torch.empty((B, K1), dtype=torch.float32, device=dev) if return_uniforms else None
     ws = _workspace("accept", dev, accept_workspace_bytes(B, k, V), workspace)
-    rc = _lib.load().spec_accept_philox(
+    _run(dev, "spec_accept_philox",
         draft.data_ptr() if k > 0 else None, q.data_ptr() if k > 0 else None, p.data_ptr(),
         int(seed), int(offset), u.data_ptr() if u is not None else None, n_accepted.data_ptr(),
         tokens.data_ptr(), B, k, V, ws.data_ptr(), _nbytes(ws), _stream_ptr(dev, stream))
-    _lib.check("spec_accept_philox", rc)
     return n_accepted, tokens, u
 
 
@@ -303,13 +308,12 @@ def lm_head_accept(hidden, weight, temperature, draft, q, uniforms=None, seed: i
     _need(tokens, "tokens", torch.int32, dev)
     u = torch.empty((B, k + 1), dtype=torch.float32, device=dev) if return_uniforms else None
     ws = _workspace("lm_head_accept", dev, lm_head_accept_workspace_bytes(B, k, H, V), workspace)
-    rc = _lib.load().spec_lm_head_accept(
+    _run(dev, "spec_lm_head_accept",
         hidden.data_ptr(), weight.data_ptr(), temperature.data_ptr(),
         draft.data_ptr() if k > 0 else None, q.data_ptr() if k > 0 else None,
         uniforms.data_ptr() if uniforms is not None else None, int(seed), int(offset),
         u.data_ptr() if u is not None else None, n_accepted.data_ptr(), tokens.data_ptr(),
         B, k, H, V, _dtype_code(hidden), ws.data_ptr(), _nbytes(ws), _stream_ptr(dev, stream))
-    _lib.check("spec_lm_head_accept", rc)
     return n_accepted, tokens, u
 
 
@@ -336,11 +340,10 @@ def kv_append(k_new, v_new, k_pool, v_pool, page_table, ctx_lens, stream=None):
     P, Hkv2, ps, D2 = k_pool.shape
     if (Hkv2, D2) != (Hkv, D) or tuple(v_new.shape) != tuple(k_new.shape):
         raise ValueError("k_new / v_new must be [B, K1, Hkv, D] matching the pools")
-    rc = _lib.load().spec_kv_append(
+    _run(dev, "spec_kv_append",
         k_new.data_ptr(), v_new.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
         page_table.data_ptr(), ctx_lens.data_ptr(), B, K1, Hkv, D, ps, P, page_table.shape[1],
         _dtype_code(k_pool), _stream_ptr(dev, stream))
-    _lib.check("spec_kv_append", rc)
 
 
 def kv_commit(ctx_lens, n_accepted, K1: int, stream=None):
@@ -349,9 +352,8 @@ def kv_commit(ctx_lens, n_accepted, K1: int, stream=None):
     dev = ctx_lens.device
     _need(ctx_lens, "ctx_lens", torch.int32, dev)
     _need(n_accepted, "n_accepted", torch.int32, dev)
-    rc = _lib.load().spec_kv_commit(ctx_lens.data_ptr(), n_accepted.data_ptr(),
-                                    ctx_lens.shape[0], int(K1), _stream_ptr(dev, stream))
-    _lib.check("spec_kv_commit", rc)
+    _run(dev, "spec_kv_commit", ctx_lens.data_ptr(), n_accepted.data_ptr(), ctx_lens.shape[0],
+         int(K1), _stream_ptr(dev, stream))
 
 
 def version() -> int:
