@@ -136,6 +136,18 @@ def test_deterministic_repeat():
     assert torch.equal(a, b)
 
 
+@pytest.mark.parametrize("ctx_len", [2000, 800_000])
+def test_long_page_table(ctx_len):
+    """A 50000-page table (800K tokens): the plan's floor on pages per piece (13 here, which
+    keeps one unit's pieces within what the merge takes) sets the split of a short context,
+    and a full one splits into ~100-page pieces, ~500 per unit."""
+    w = small_workload("bf16", 8, 2, 128, 0, 2, batch=1)
+    ctx = np.array([ctx_len], dtype=np.int32)
+    table, P = gen.page_tables(w, ctx, max_pages=50_000)
+    inp = attn_inputs(w, 0, dev(), ctx=ctx, table=table, num_pages=P)
+    check(inp, "bf16", f"page table of 50000 pages, ctx {ctx_len}")
+
+
 @pytest.mark.parametrize("dtype,window,k,d", [("bf16", 0, 2, 128), ("f32", 40, 0, 128),
                                              ("bf16", 0, 2, 512), ("bf16", 30, 1, 256)])
 def test_many_sequences(dtype, window, k, d):
