@@ -59,3 +59,40 @@ def test_multi_step_chain(dtype, D, window):
         assert np.array_equal(ctx_d.cpu().numpy(), ctx_h)
     np.testing.assert_array_equal(kp_d.cpu().double().numpy(), kp_h)
     np.testing.assert_array_equal(vp_d.cpu().double().numpy(), vp_h)
+
+
+def test_append_and_commit_edge_cases():
+    """Positions before the cache start or past the page table, page ids outside the pool and
+    negative table entries are skipped (nothing else in the pools changes); commit clamps n to
+    [0, K1 - 1]."""
+    d = dev()
+    rng = np.random.default_rng(3)
+    B, K1, Hkv, D, ps, maxp, P = 6, 4, 2, 128, 16, 3, 24
+    table = rng.permutation(P)[:B * maxp].reshape(B, maxp).astype(np.int32)   # no page shared
+    table[1, 2] = -1          # a hole in the table
+    table[2, 0] = P + 5       # a page id outside the pool
+    table[3, 1] = -7
+    # ctx (already counting the K1 new positions): 2 < K1 (two positions before the start),
+    # 49 (the last new position is past the 48-token table), 33..36 over the hole / bad ids
+    ctx = np.array([2, 49, 4, 20, 36, 48], dtype=np.int32)
+    g = torch.Generator().manual_seed(9)
+    kp = torch.randn(P, Hkv, ps, D, generator=g).to(torch.bfloat16)
+    vp = torch.randn(P, Hkv, ps, D, generator=g).to(torch.bfloat16)
+    kn = torch.randn(B, K1, Hkv, D, generator=g).to(torch.bfloat16)
+    vn = torch.randn(B, K1, Hkv, D, generator=g).to(torch.bfloat16)
+    kp_h, vp_h = kp.double().numpy().copy(), vp.double().numpy().copy()
+    okv.append(kp_h, vp_h, table, ctx, kn.double().numpy(), vn.double().numpy())
+    kp_d, vp_d = kp.to(d), vp.to(d)
+    sv.kv_append(kn.to(d), vn.to(d), kp_d, vp_d, torch.from_numpy(table).to(d),
+                 torch.from_numpy(ctx).to(d))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(kp_d.cpu().double().numpy(), kp_h)
+    np.testing.assert_array_equal(vp_d.cpu().double().numpy(), vp_h)
+    # commit: n below 0 and above K1 - 1 are clamped
+    ctx_c = np.array([10, 49, 20, 20, 36, 48], dtype=np.int32)
+    n = np.array([-3, 0, 1, 3, 4, 100], dtype=np.int32)
+    ctx_d = torch.from_numpy(ctx_c.copy()).to(d)
+    sv.kv_commit(ctx_d, torch.from_numpy(n).to(d), K1)
+    torch.cuda.synchronize()
+    assert np.array_equal(ctx_d.cpu().numpy(), okv.commit(ctx_c, n, K1))
+    assert okv.commit(ctx_c, n, K1).tolist() == [7, 46, 18, 20, 36, 48]
