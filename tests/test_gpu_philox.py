@@ -1,5 +1,5 @@
 """spec_accept_philox on the GPU: the uniforms it draws equal the oracle's Philox4x32-10 bit
-for bit (several seeds and offsets, k up to 9, 300 sequences), and its accept counts and
+for bit (several seeds and offsets, k up to 63, 300 sequences), and its accept counts and
 tokens equal spec_accept given those uniforms and, bit for bit, the oracle's accept rule on
 the same fp32 p, q and uniforms."""
 import numpy as np
@@ -16,7 +16,7 @@ pytestmark = pytest.mark.gpu
 
 @pytest.mark.parametrize("seed,offset,B,k", [
     (0, 0, 3, 2), (0x0123456789ABCDEF, 7, 300, 5), (2 ** 64 - 1, 2 ** 40 + 3, 17, 9),
-    (12345, 99, 4, 0)])
+    (12345, 99, 4, 0), (7, 2 ** 32 - 1, 5, 63)])   # k = 63: 64 uniforms, counters 0..15
 def test_uniforms_equal_oracle_generator(seed, offset, B, k):
     d = dev()
     V = 64
