@@ -28,8 +28,10 @@
  *     made from any thread.
  *   - Calls run on the calling thread's current HIP device: `stream` (a hipStream_t, NULL
  *     for the null stream) and every pointer must belong to it, and spec_verify_attn_workspace
- *     sizes for its compute units.  Calls only enqueue work on the stream and return; results
- *     are valid once the stream has reached that point.
+ *     sizes for its compute units.  Calls only enqueue kernels on the stream and return;
+ *     results are valid once the stream has reached that point.  They enqueue no memset, copy
+ *     or synchronisation, so a sequence of calls can be captured in a HIP graph and replayed
+ *     (the inputs read at replay time are whatever the captured buffers then hold).
  *   - Return value: SPEC_OK (0) or a negative spec_status.  Host-checkable argument errors are
  *     reported before anything is enqueued; spec_last_error() then describes the failure (a
  *     thread-local string, valid until the next call on the same thread).
