@@ -95,15 +95,16 @@ struct AttnShape {
   static constexpr bool kSplit = D >= 256 && kWGs(kTiles + kSplitBytes) >= kWGs(kTiles);
   // Head dim 512, and head dim 256 at one row tile, in bf16: each wave streams its quarter of
   // the head dim straight into MFMA operand registers (unit_quarter below); LDS holds only the
-  // double-buffered score exchange (and, after a piece's pages, its partial on the way out: 16,
-  // 32 or 64 KB), and registers set the resident workgroups per CU: four at
+  // double-buffered score exchange (and at two row tiles, after a piece's pages, its partial
+  // on the way out: 66 KB at D = 512), and registers set the resident workgroups per CU: four at
   // D = 256 (103 VGPRs, the most without spills), two at D = 512 (a third fits at one row tile,
   // but the batch-32 workload streamed 3% slower with it on MI355X).  Head dim 256 at two row
   // tiles stays with the LDS-staged path, which measured 6% faster there (15.9 against 16.9 us
   // per sliding layer at batch 8, k = 5).
   static constexpr bool kQuarter = (D == 512 || (D == 256 && RT == 1)) && sizeof(T) == 2;
   static constexpr size_t kQuarterXch = 2 * (size_t)kWaves * RT * 64 * 16;   // score exchange
-  static constexpr size_t kQuarterStg = (size_t)kWaves * 16 * RT * (D / 4 + 4) * 4;   // partial
+  static constexpr size_t kQuarterStg =                                      // partial (RT 2)
+      RT == 2 ? (size_t)kWaves * 16 * RT * (D / 4 + 4) * 4 : 0;
   static constexpr size_t kQuarterLds = kQuarterXch > kQuarterStg ? kQuarterXch : kQuarterStg;
   static constexpr size_t kLds = kQuarter ? kQuarterLds : kTiles + (kSplit ? kSplitBytes : 0);
   static constexpr int kQuarterWaves = D == 512 ? 2 : 4;
@@ -428,34 +429,54 @@ __device__ __forceinline__ void unit_quarter(
   __syncthreads();   // every wave is done with pid_sh and the exchange buffers
 
   // the piece's partial: lane (j, q) element e of tile t is dim DQ w + E (4 q + e) + t of row j.
-  // A lane holds 16-byte pieces of 4 (hd256) or 1 (hd512) lines of a row, so stored as they
-  // lie one instruction would touch 64 lines; instead each wave puts its quarter of the rows in
-  // LDS (the exchange buffers are free now) and writes it back row by row, eight lanes to a
-  // 128-byte line, with nontemporal stores (the merge reads them once, from another CU).  At
-  // the batch-8 global layer this took the call (partial + merge) from 79.6 to 75.8 us on
-  // MI355X; the other layers moved by less than the run-to-run spread.  Nontemporal stores of
-  // the pieces as they lie were much slower (batch-1 / 32K 65 -> 86 us).
   const size_t base = (size_t)piece * rstride;
-  constexpr int SQ = DQ + 4;   // padded LDS row stride (floats)
-  float *stg = reinterpret_cast<float *>(sred) + (size_t)wave * 16 * RT * SQ;
+  if constexpr (RT == 2) {
+    // A lane holds 16-byte pieces of 4 (hd256) or 1 (hd512) lines of a row, so stored as they
+    // lie one instruction would touch 64 lines; instead each wave puts its quarter of the rows
+    // in LDS (the exchange buffers are free now) and writes it back row by row, eight lanes to
+    // a 128-byte line, with nontemporal stores (the merge reads them once, from another CU).
+    // At the batch-8 global layer this took the call (partial + merge) from 79.6 to 75.8 us on
+    // MI355X, the batch-1 / 32K layer moved by less than the spread; at one row tile the
+    // batch-1 sliding layer's merge lost 0.6 us (its partials no longer cache-resident) and
+    // the batch-32 layers did not move, so one row tile keeps cached stores.  Nontemporal
+    // stores of the pieces as they lie were much slower (batch-1 / 32K 65 -> 86 us).
+    constexpr int SQ = DQ + 4;   // padded LDS row stride (floats)
+    float *stg = reinterpret_cast<float *>(sred) + (size_t)wave * 16 * RT * SQ;
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    const int r = rt * 16 + lr;
-    if (r < nr && wave == 0 && lq == 0) part_ml[base + r] = make_float2(m_run[rt], l_run[rt]);
+    for (int rt = 0; rt < RT; ++rt) {
+      const int r = rt * 16 + lr;
+      if (r < nr && wave == 0 && lq == 0) part_ml[base + r] = make_float2(m_run[rt], l_run[rt]);
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
+      for (int e = 0; e < 4; ++e)
 #pragma unroll
-      for (int t0 = 0; t0 < E; t0 += 4)
-        *reinterpret_cast<f32x4_t *>(stg + r * SQ + E * (4 * lq + e) + t0) =
-            f32x4_t{acc[rt][t0][e], acc[rt][t0 + 1][e], acc[rt][t0 + 2][e], acc[rt][t0 + 3][e]};
-  }
-  __syncthreads();
-  constexpr int C4 = DQ / 4;   // 16-byte pieces of a row's quarter
-  for (int idx = lane; idx < nr * C4; idx += spec::kWave) {
-    const int row = idx / C4, c = idx - row * C4;
-    const f32x4_t v = *reinterpret_cast<const f32x4_t *>(stg + row * SQ + 4 * c);
-    __builtin_nontemporal_store(
-        v, reinterpret_cast<f32x4_t *>(part_acc + (base + row) * D + DQ * wave + 4 * c));
+        for (int t0 = 0; t0 < E; t0 += 4)
+          *reinterpret_cast<f32x4_t *>(stg + r * SQ + E * (4 * lq + e) + t0) =
+              f32x4_t{acc[rt][t0][e], acc[rt][t0 + 1][e], acc[rt][t0 + 2][e], acc[rt][t0 + 3][e]};
+    }
+    __syncthreads();
+    constexpr int C4 = DQ / 4;   // 16-byte pieces of a row's quarter
+    for (int idx = lane; idx < nr * C4; idx += spec::kWave) {
+      const int row = idx / C4, c = idx - row * C4;
+      const f32x4_t v = *reinterpret_cast<const f32x4_t *>(stg + row * SQ + 4 * c);
+      __builtin_nontemporal_store(
+          v, reinterpret_cast<f32x4_t *>(part_acc + (base + row) * D + DQ * wave + 4 * c));
+    }
+  } else {
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      const int r = rt * 16 + lr;
+      if (r < nr) {
+        if (wave == 0 && lq == 0) part_ml[base + r] = make_float2(m_run[rt], l_run[rt]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float *dst = part_acc + (base + r) * D + DQ * wave + E * (4 * lq + e);
+#pragma unroll
+          for (int t0 = 0; t0 < E; t0 += 4)
+            *reinterpret_cast<float4 *>(dst + t0) = make_float4(
+                acc[rt][t0][e], acc[rt][t0 + 1][e], acc[rt][t0 + 2][e], acc[rt][t0 + 3][e]);
+        }
+      }
+    }
   }
 }
 
